@@ -1,0 +1,202 @@
+"""libkda: the Kimi Delta Attention recurrence on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI declared in include/kda.h.  It only
+checks dtypes, shapes, contiguity and devices, allocates outputs with torch
+(device memory and streams are all torch provides here) and passes raw
+pointers plus the current HIP stream; every step of the recurrence runs in the
+HIP kernels of libkda.so.  There is no fallback: importing works without a
+GPU, but any call needs the built library and a GPU, and raises otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "KDAError", "lib", "library_path", "kda_version", "kda_status_string",
+    "chunk_fwd", "kcp_scan", "kcp_workspace_size", "decode_step",
+    "KDA_BF16", "KDA_F32",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+KDA_BF16, KDA_F32 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+           3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
+
+# Every symbol include/kda.h declares.
+SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd", "kda_kcp_workspace_size",
+           "kda_kcp_scan", "kda_decode_step")
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {_STATUS.get(status, status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so with argument types set (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libkda.so is not built ({_LIB_PATH}); run "
+                          "python -m gated_delta_rule_75_amd.build")
+    L = ctypes.CDLL(_LIB_PATH)
+    i, i64, f, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    L.kda_version.argtypes = []
+    L.kda_version.restype = i
+    L.kda_status_string.argtypes = [i]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_chunk_fwd.restype = i
+    L.kda_kcp_workspace_size.argtypes = [i, i, i, i]
+    L.kda_kcp_workspace_size.restype = sz
+    L.kda_kcp_scan.argtypes = [i, i, i, i, i, f, i64, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                               sz, vp]
+    L.kda_kcp_scan.restype = i
+    L.kda_decode_step.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_decode_step.restype = i
+    _lib = L
+    return L
+
+
+def kda_version() -> int:
+    return lib().kda_version()
+
+
+def kda_status_string(status: int) -> str:
+    return lib().kda_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KDAError(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v/z must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libkda tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("libkda tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("libkda tensors must share one device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check_inputs(q, k, v, g, beta, z):
+    dt = _dt(q)
+    for name, t in (("k", k), ("v", v), ("z", z)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (T, H, dv):
+        raise ValueError("q, k, g must be [T, H, dk] and v [T, H, dv]")
+    if beta.shape != (T, H) or (z is not None and z.shape != v.shape):
+        raise ValueError("beta must be [T, H] and z like v")
+    return dt, T, H, dk, dv
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=None,
+              initial_state=None, output_final_state: bool = True, chunk: int = 64,
+              scale: float = 1.0, y: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill over packed sequences; returns (y, final_state or None)."""
+    dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1
+    if y is None:
+        y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    for name, s in (("initial_state", initial_state), ("final_state", final_state)):
+        if s is not None and (s.dtype != torch.float32 or s.shape != (N, H, dk, dv)):
+            raise ValueError(f"{name} must be float32 [{N}, {H}, {dk}, {dv}]")
+    st = lib().kda_chunk_fwd(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens), _ptr(q),
+                             _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                             _ptr(initial_state), _ptr(final_state), _ptr(y), _stream(dev))
+    _check("kda_chunk_fwd", st)
+    return y, final_state
+
+
+def kcp_workspace_size(H: int, dk: int, dv: int, num_segments: int) -> int:
+    return int(lib().kda_kcp_workspace_size(H, dk, dv, num_segments))
+
+
+def kcp_scan(q, k, v, g, beta, num_segments: int, z=None, initial_state=None, chunk: int = 64,
+             scale: float = 1.0, workspace: Optional[torch.Tensor] = None,
+             y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None):
+    """One long sequence split into segments composed by a prefix scan; returns (y, final_state)."""
+    dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    dev = _dev(q, k, v, g, beta, z, initial_state, workspace, y, final_state)
+    need = kcp_workspace_size(H, dk, dv, num_segments)
+    if need == 0:
+        raise KDAError("kda_kcp_workspace_size", 2)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
+    if final_state is None:
+        final_state = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    st = lib().kda_kcp_scan(dt, H, dk, dv, chunk, scale, T, num_segments, _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(g), _ptr(beta), _ptr(z), _ptr(initial_state),
+                            _ptr(final_state), _ptr(y), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("kda_kcp_scan", st)
+    return y, final_state
+
+
+def decode_step(q, k, v, g, beta, state, z=None, scale: float = 1.0,
+                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per request; q, k, g: [N, H, dk], v, z: [N, H, dv], beta [N, H],
+    state fp32 [N, H, dk, dv] updated in place.  Returns y [N, H, dv]."""
+    dt, N, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    dev = _dev(q, k, v, g, beta, z, state, y)
+    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
+        raise ValueError("state must be float32 [N, H, dk, dv]")
+    if y is None:
+        y = torch.empty(N, H, dv, dtype=q.dtype, device=dev)
+    st = lib().kda_decode_step(dt, N, H, dk, dv, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(z), _ptr(state), _ptr(y), _stream(dev))
+    _check("kda_decode_step", st)
+    return y

@@ -1,0 +1,106 @@
+// Device helpers shared by the libkda kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element types.  Global tensors q, k, v, z, y are bf16 or fp32.  MFMA operand
+// tiles in LDS use the same element type: bf16 feeds v_mfma_f32_16x16x32_bf16
+// (8 consecutive k per lane), fp32 feeds v_mfma_f32_16x16x4_f32 (1 k per lane).
+// Both produce the 16x16 fp32 tile in the same lane layout: lane l holds rows
+// 4*(l/16)+i, i<4, of column l%16.
+// ---------------------------------------------------------------------------
+struct BF16 {
+    using T = __bf16;
+    using Frag = bf16x8_t;
+    static constexpr int KPL = 8;         // k elements per lane per MFMA
+    static constexpr int KSTEP = 32;      // k depth of one MFMA
+    static __device__ __forceinline__ f32x4_t mma(Frag a, Frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+struct F32 {
+    using T = float;
+    using Frag = float;
+    static constexpr int KPL = 1;
+    static constexpr int KSTEP = 4;
+    static __device__ __forceinline__ f32x4_t mma(Frag a, Frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Fragment element access (k index within the lane's KPL elements).
+template <typename E>
+__device__ __forceinline__ float frag_get(const typename E::Frag& f, int i);
+template <>
+__device__ __forceinline__ float frag_get<BF16>(const bf16x8_t& f, int i) { return (float)f[i]; }
+template <>
+__device__ __forceinline__ float frag_get<F32>(const float& f, int) { return f; }
+
+template <typename E>
+__device__ __forceinline__ void frag_set(typename E::Frag& f, int i, float x);
+template <>
+__device__ __forceinline__ void frag_set<BF16>(bf16x8_t& f, int i, float x) { f[i] = (__bf16)x; }
+template <>
+__device__ __forceinline__ void frag_set<F32>(float& f, int, float x) { f = x; }
+
+// Operand fragment of a 16 x KSTEP tile stored row-major in LDS with pitch ld
+// (elements): rows r0 .. r0+15, k columns k0 .. k0+KSTEP-1.  Used for both A
+// (rows = output rows) and B (rows = output columns, i.e. B stored transposed).
+template <typename E>
+__device__ __forceinline__ typename E::Frag lds_frag(const typename E::T* base, int ld, int r0,
+                                                     int k0, int lane) {
+    const typename E::T* p = base + (r0 + (lane & 15)) * ld + k0 + E::KPL * (lane >> 4);
+    return *reinterpret_cast<const typename E::Frag*>(p);
+}
+
+// Same fragment with every element multiplied by a per-k factor table (fp32,
+// indexed by absolute k).
+template <typename E>
+__device__ __forceinline__ typename E::Frag lds_frag_scaled(const typename E::T* base, int ld,
+                                                            int r0, int k0, int lane,
+                                                            const float* kscale) {
+    typename E::Frag f = lds_frag<E>(base, ld, r0, k0, lane);
+    const int kb = k0 + E::KPL * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < E::KPL; ++i) frag_set<E>(f, i, frag_get<E>(f, i) * kscale[kb + i]);
+    return f;
+}
+
+// Global element loads/stores of bf16 / fp32 tensors.
+__device__ __forceinline__ float gload(const __bf16* p) { return (float)*p; }
+__device__ __forceinline__ float gload(const float* p) { return *p; }
+__device__ __forceinline__ void gstore(__bf16* p, float x) { *p = (__bf16)x; }
+__device__ __forceinline__ void gstore(float* p, float x) { *p = x; }
+
+// Two consecutive elements (4-byte aligned for bf16, 8-byte for fp32).
+__device__ __forceinline__ f32x2_t gload2(const __bf16* p) {
+    bf16x2_t v = *reinterpret_cast<const bf16x2_t*>(p);
+    return f32x2_t{(float)v[0], (float)v[1]};
+}
+__device__ __forceinline__ f32x2_t gload2(const float* p) {
+    return *reinterpret_cast<const f32x2_t*>(p);
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace kda

@@ -1,0 +1,121 @@
+// Decode step of the KDA recurrence: one token per request against the
+// resident fp32 state, updated in place (page "Exercices", Niveau 1 Q4 and Q6:
+// decode is bandwidth-limited and the state has a fixed size).
+//
+// Per (request n, head h) one workgroup makes ONE pass over S (dk x dv fp32):
+//   S^ = Diag(alpha) S                  alpha = exp(g)       (forget)
+//   u  = S^^T k,  w = S^^T q            two reductions over the key channels
+//   delta = beta (v - u)                                     (erase)
+//   S  <- S^ + k delta^T                written back in place (write)
+//   o  = scale (w + (k.q) delta)        = scale S_t^T q
+//   y  = o * sigmoid(z)                 (gated)
+// The identity o = S_t^T q = S^^T q + (k^T q) delta lets the output be formed
+// without a second read of the state.  Each thread owns float4 column groups
+// of several rows, so every wave reads whole 512-byte rows (coalesced 16-byte
+// accesses) and the state crosses HBM exactly once each way.
+#include "common.h"
+#include "launch.h"
+
+namespace kda {
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T* __restrict__ q,
+                                                     const T* __restrict__ k,
+                                                     const T* __restrict__ v,
+                                                     const float* __restrict__ g,
+                                                     const float* __restrict__ beta,
+                                                     const T* __restrict__ z,
+                                                     float* __restrict__ state, T* __restrict__ y) {
+    constexpr int CG = DV / 4;      // float4 column groups per row
+    constexpr int RG = 256 / CG;    // row groups
+    constexpr int RPT = DK / RG;    // rows per thread
+    static_assert(RG * CG == 256 && RPT * RG == DK, "decode tiling");
+
+    __shared__ float s_k[DK], s_q[DK], s_a[DK];
+    __shared__ float s_u[RG][DV + 4], s_w[RG][DV + 4];
+    __shared__ float s_delta[DV];
+    __shared__ float s_kq;
+
+    const int nh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const int64_t kb = (int64_t)nh * DK, vb = (int64_t)nh * DV;
+    float* st = state + (int64_t)nh * DK * DV;
+
+    // issue the state loads first: they are the whole cost of the step
+    f32x4_t S[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = r * RG + rg;
+        S[r] = *reinterpret_cast<const f32x4_t*>(st + (int64_t)row * DV + 4 * cg);
+    }
+    for (int c = tid; c < DK; c += 256) {
+        s_k[c] = gload(k + kb + c);
+        s_q[c] = gload(q + kb + c);
+        s_a[c] = fast_exp(g[kb + c]);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        float p = 0.f;
+        for (int c = tid; c < DK; c += kWave) p += s_k[c] * s_q[c];
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        if (tid == 0) s_kq = p;
+    }
+    f32x4_t u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = r * RG + rg;
+        S[r] *= s_a[row];
+        u += s_k[row] * S[r];
+        w += s_q[row] * S[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s_u[rg][4 * cg + i] = u[i];
+        s_w[rg][4 * cg + i] = w[i];
+    }
+    __syncthreads();
+    if (tid < DV) {
+        const int j = tid;
+        float U = 0.f, W = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            U += s_u[r][j];
+            W += s_w[r][j];
+        }
+        const float d = beta[nh] * (gload(v + vb + j) - U);
+        s_delta[j] = d;
+        float o = scale * (W + s_kq * d);
+        if (z) o *= sigmoid(gload(z + vb + j));
+        gstore(y + vb + j, o);
+    }
+    __syncthreads();
+    const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&s_delta[4 * cg]);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = r * RG + rg;
+        const f32x4_t val = S[r] + s_k[row] * d4;
+        *reinterpret_cast<f32x4_t*>(st + (int64_t)row * DV + 4 * cg) = val;
+    }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+    if (a.N == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
+                       (hipStream_t)a.stream, a.scale, a.H, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, a.g, a.beta, (const T*)a.z, a.state, (T*)a.y);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+    if (a.dtype == 0) {
+        if (a.dk == 128) return launch_decode_t<__bf16, 128, 128>(a);
+        return launch_decode_t<__bf16, 64, 64>(a);
+    }
+    if (a.dk == 128) return launch_decode_t<float, 128, 128>(a);
+    return launch_decode_t<float, 64, 64>(a);
+}
+
+}  // namespace kda

@@ -1,0 +1,156 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) recurrence on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per sequence and head; page "Exercices", Niveau 2 Q7 names
+ * its three operations forget / erase / write; page "Ce qui est public et ce
+ * qui ne l'est pas", table "Entièrement publié et vérifiable", lists the
+ * recurrence, its parametrisation (q, k, v, beta, z), the bounded decay and
+ * the output gate):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *     y_t = o_t * sigmoid(z_t)        (gated; y_t = o_t when z == NULL)
+ *
+ * S is dk x dv per head.  Every entry point takes caller-owned device memory,
+ * enqueues its kernels on `stream` (a hipStream_t; NULL = the null stream)
+ * and returns without synchronising.  Problems the host can see (a NULL
+ * required pointer, unsupported sizes, misalignment, a short workspace) are
+ * reported by the return code BEFORE anything is launched; a failed launch
+ * returns KDA_ERR_HIP; faults inside a kernel surface at the caller's next
+ * synchronisation.  No call allocates device or host memory, keeps state
+ * between calls, or throws across the ABI.  Calls on different streams may
+ * run concurrently; results are deterministic (no atomics in reductions).
+ *
+ * Layouts (row-major, last index fastest; T_total = packed token count):
+ *   q, k        [T_total, H, dk]       dtype dt
+ *   v, z, y     [T_total, H, dv]       dtype dt
+ *   g           [T_total, H, dk]       fp32, natural log of the decay alpha
+ *   beta        [T_total, H]           fp32
+ *   states      [N, H, dk, dv]         fp32 (N = sequences or requests)
+ * Pointers to bf16 data must be 4-byte aligned, fp32 data 8-byte aligned,
+ * states 16-byte aligned.
+ *
+ * Preconditions (documented, not checked on the hot path):
+ *   - q and k are L2-normalised per (token, head): page "Exercices",
+ *     Niveau 2 Q9 -- with unit keys I - beta k k^T does not expand the state;
+ *   - g lies in [g_min, 0] with g_min = -5 (page "Exercices", Niveau 2 Q8:
+ *     the cumulative log-decay of a 16-token tile is then >= -80, and e^80
+ *     fits the bf16 range); the kernels stay finite for g >= -5.4;
+ *   - beta lies in [0, 1];
+ *   - cu_seqlens is non-decreasing, cu_seqlens[0] = 0,
+ *     cu_seqlens[num_seqs] = T_total.
+ *
+ * Supported sizes: (dk, dv) in {(64, 64), (128, 128)}; chunk in {16, 64},
+ * except fp32 inputs with dk = 128, which support chunk = 16 only.
+ * Anything else returns KDA_ERR_UNSUPPORTED.
+ */
+#ifndef LIBKDA_KDA_H
+#define LIBKDA_KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, negative size, misalignment */
+    KDA_ERR_UNSUPPORTED = 2,        /* dk/dv/chunk/dtype combination not built */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} kda_status;
+
+typedef enum {
+    KDA_BF16 = 0,   /* q, k, v, z, y stored as bfloat16 */
+    KDA_F32 = 1     /* q, k, v, z, y stored as float32 */
+} kda_dtype;
+
+/* Version of the library as 10000 * major + 100 * minor + patch. */
+int kda_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(kda_status status);
+
+/*
+ * kda_chunk_fwd -- prefill: run the recurrence over every token of a batch of
+ * packed sequences (page "Exercices", Niveau 1 Q4: prefill processes the
+ * whole input in parallel and is compute-limited).
+ *
+ *   dt, H, dk, dv   dtype and head shape.
+ *   chunk           tokens per chunk of the blocked algorithm (16 or 64); it
+ *                   changes rounding only, never the result's definition.
+ *   scale           factor on the output o_t (1.0 for the plain recurrence).
+ *   num_seqs        number of packed sequences (>= 1).
+ *   T_total         total tokens (>= 0; 0 is a no-op apart from copying the
+ *                   initial state to the final state).
+ *   cu_seqlens      device int32 [num_seqs + 1] offsets, or NULL when
+ *                   num_seqs == 1 (one sequence of T_total tokens).
+ *   q, k, v, g, beta  inputs (layouts above); all required.
+ *   z               gate input [T_total, H, dv], or NULL for no gate.
+ *   initial_state   fp32 [num_seqs, H, dk, dv] or NULL (zeros).
+ *   final_state     fp32 [num_seqs, H, dk, dv] or NULL (not written).  May
+ *                   alias initial_state (each state is read before written).
+ *   y               output [T_total, H, dv] in dtype dt; must not alias inputs.
+ */
+kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                         int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                         const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const void* z, const float* initial_state,
+                         float* final_state, void* y, void* stream);
+
+/*
+ * kda_kcp_workspace_size -- bytes of device workspace kda_kcp_scan needs for
+ * H heads split into num_segments segments: the segment pairs
+ * (M [dk x dk], Sloc [dk x dv]) and the entering states [dk x dv], all fp32.
+ * Returns 0 for invalid or unsupported sizes.
+ */
+size_t kda_kcp_workspace_size(int H, int dk, int dv, int num_segments);
+
+/*
+ * kda_kcp_scan -- one long sequence of T tokens split into num_segments equal
+ * contiguous segments (the last one may be shorter) processed side by side.
+ * Each segment's effect on the state entering it is the pair (cumulative
+ * transition M, local state Sloc): S_end = M S_start + Sloc; pairs compose as
+ * (M2, S2) o (M1, S1) = (M2 M1, M2 S1 + S2) (page "Exercices", Niveau 3
+ * Q21-Q22; page "Reproduire Kimi K3", "Le script de vérification").  Three
+ * phases on `stream`: pairs of all segments in parallel, a scan of the pairs
+ * giving every segment its entering state, then every segment's outputs.  The
+ * result equals kda_chunk_fwd on the same sequence up to rounding.
+ *
+ *   T, num_segments  T >= num_segments >= 1.
+ *   q..z, initial_state, final_state, y: as kda_chunk_fwd with one sequence.
+ *   workspace        device buffer of at least kda_kcp_workspace_size bytes,
+ *                    256-byte aligned; overwritten.
+ */
+kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float scale, int64_t T,
+                        int num_segments, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const void* z,
+                        const float* initial_state, float* final_state, void* y,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_decode_step -- decode: one token for each of N requests against states
+ * resident in device memory (page "Exercices", Niveau 1 Q4: decode is limited
+ * by memory bandwidth; Q6: the KDA state has a fixed size whatever the
+ * length).  One pass over each state: decay, the two reductions S^T k and
+ * S^T q, the in-place rank-1 update and the gated output.
+ *
+ *   N                requests (>= 0).
+ *   q, k, v, z       [N, H, d] in dtype dt (z may be NULL).
+ *   g, beta          [N, H, dk] and [N, H] fp32.
+ *   state            fp32 [N, H, dk, dv], read and updated in place.
+ *   y                [N, H, dv] output in dtype dt.
+ */
+kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float scale,
+                           const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const void* z, float* state, void* y,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_KDA_H */

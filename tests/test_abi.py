@@ -1,0 +1,110 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_75_amd as kda
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kda.h")
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+BF16, F32 = kda.KDA_BF16, kda.KDA_F32
+P = ctypes.c_void_p(1 << 20)          # a fake, aligned, never dereferenced address
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return kda.lib()
+
+
+def test_header_declares_what_the_binding_knows():
+    assert declared_symbols() == sorted(kda.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert L.kda_version() == 10000
+    assert kda.kda_status_string(0) == "KDA_OK"
+    assert kda.kda_status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
+    assert kda.kda_status_string(99) == "KDA_ERR_UNKNOWN"
+
+
+def _fwd(L, dt=BF16, H=2, dk=128, dv=128, chunk=64, N=1, T=64, cu=None, q=P, k=P, v=P, g=P,
+         beta=P, z=None, s0=None, sf=None, y=P):
+    return L.kda_chunk_fwd(dt, H, dk, dv, chunk, 1.0, N, T, cu, q, k, v, g, beta, z, s0, sf, y,
+                           None)
+
+
+def test_chunk_fwd_rejects_bad_arguments(L):
+    assert _fwd(L, dt=7) == INVALID
+    assert _fwd(L, H=0) == INVALID
+    assert _fwd(L, N=0) == INVALID
+    assert _fwd(L, T=-1) == INVALID
+    assert _fwd(L, N=2, cu=None) == INVALID                      # several sequences need offsets
+    assert _fwd(L, q=None) == INVALID
+    assert _fwd(L, y=None) == INVALID
+    assert _fwd(L, beta=None) == INVALID
+    assert _fwd(L, q=ctypes.c_void_p((1 << 20) + 2)) == INVALID  # bf16 pairs need 4-byte alignment
+    assert _fwd(L, g=ctypes.c_void_p((1 << 20) + 4)) == INVALID  # fp32 pairs need 8-byte alignment
+    assert _fwd(L, s0=ctypes.c_void_p((1 << 20) + 8)) == INVALID # states need 16-byte alignment
+
+
+def test_chunk_fwd_rejects_unsupported_shapes(L):
+    assert _fwd(L, dk=96, dv=96) == UNSUPPORTED
+    assert _fwd(L, dk=128, dv=64) == UNSUPPORTED
+    assert _fwd(L, chunk=32) == UNSUPPORTED
+    assert _fwd(L, dt=F32, dk=128, dv=128, chunk=64) == UNSUPPORTED
+
+
+def test_kcp_workspace_size(L):
+    H, dk, dv, S = 4, 128, 128, 256
+    pairs = S * H * dk * (dk + dv) * 4
+    starts = S * H * dk * dv * 4
+    assert L.kda_kcp_workspace_size(H, dk, dv, S) == pairs + starts
+    assert L.kda_kcp_workspace_size(H, 96, 96, S) == 0
+    assert L.kda_kcp_workspace_size(0, dk, dv, S) == 0
+    assert L.kda_kcp_workspace_size(H, dk, dv, 0) == 0
+
+
+def _kcp(L, T=4096, S=4, ws=P, wsb=1 << 40, dk=128, chunk=64, dt=BF16, y=P):
+    return L.kda_kcp_scan(dt, 2, dk, dk, chunk, 1.0, T, S, P, P, P, P, P, None, None, None, y,
+                          ws, wsb, None)
+
+
+def test_kcp_rejects_bad_arguments(L):
+    assert _kcp(L, S=0) == INVALID
+    assert _kcp(L, T=3, S=4) == INVALID
+    assert _kcp(L, ws=None) == INVALID
+    assert _kcp(L, ws=ctypes.c_void_p((1 << 20) + 128)) == INVALID   # 256-byte alignment
+    assert _kcp(L, y=None) == INVALID
+    assert _kcp(L, dk=96) == UNSUPPORTED
+    assert _kcp(L, chunk=8) == UNSUPPORTED
+    need = L.kda_kcp_workspace_size(2, 128, 128, 4)
+    assert _kcp(L, wsb=need - 1) == WS_SMALL
+
+
+def test_decode_rejects_bad_arguments(L):
+    def dec(dt=BF16, N=4, H=2, dk=128, dv=128, state=P, y=P, q=P):
+        return L.kda_decode_step(dt, N, H, dk, dv, 1.0, q, P, P, P, P, None, state, y, None)
+    assert dec(N=-1) == INVALID
+    assert dec(H=0) == INVALID
+    assert dec(dt=5) == INVALID
+    assert dec(state=None) == INVALID
+    assert dec(q=None) == INVALID
+    assert dec(state=ctypes.c_void_p((1 << 20) + 4)) == INVALID
+    assert dec(dk=128, dv=64) == UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(4, 1, 64)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(q, q, q, q, torch.zeros(4, 1))

@@ -1,0 +1,256 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: relative L2 error (over the whole flattened tensor, oracle as the
+reference) <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs, on outputs y
+and on final states.  Sizes span several chunks and a ragged tail; the
+long-memory stress draws make the carried state matter across chunks and
+segments.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import oracle
+from oracle import rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def kda():
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    import gated_delta_rule_75_amd as m
+    m.lib()
+    return m
+
+
+def _dev(t):
+    return None if t is None else t.cuda()
+
+
+def run_prefill(kda, inp, chunk, scale=1.0, S0=None):
+    cu = inp.cu_seqlens.cuda() if inp.num_seqs > 1 else None
+    s0 = inp.S0 if S0 is None else S0
+    y, fs = kda.chunk_fwd(_dev(inp.q), _dev(inp.k), _dev(inp.v), _dev(inp.g), _dev(inp.beta),
+                          cu_seqlens=cu, z=_dev(inp.z), initial_state=_dev(s0), chunk=chunk,
+                          scale=scale)
+    torch.cuda.synchronize()
+    return y.cpu(), fs.cpu()
+
+
+def oracle_prefill(inp, scale=1.0):
+    return oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, z=inp.z,
+                             S_init=inp.S0, scale=scale)
+
+
+def assert_parity(name, inp, y, fs, yo, so, tol):
+    ey = rel_l2(y.double().numpy(), yo)
+    es = rel_l2(fs.double().numpy().reshape(so.shape), so)
+    log(f"[parity] {name}: rel_l2 y={ey:.3e} state={es:.3e} (tol {tol:g})")
+    assert np.isfinite(y.double().numpy()).all() and np.isfinite(fs.double().numpy()).all()
+    assert ey <= tol, f"{name}: y rel-L2 {ey:.3e} > {tol:g}"
+    assert es <= tol, f"{name}: state rel-L2 {es:.3e} > {tol:g}"
+    return ey, es
+
+
+# ---------------------------------------------------------------- decode
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("f32", 128), ("bf16", 64)])
+def test_decode_matches_oracle(kda, dtype, d):
+    dec = kda_inputs.make_decode(N=5, H=3, dk=d, dv=d, dtype=dtype, gated=True, s0_std=0.02,
+                                 pool=3, seed=31)
+    state = dec.S0.clone().cuda()
+    steps = 6
+    for s in range(steps):
+        p = s % 3
+        y = kda.decode_step(dec.q[p].cuda(), dec.k[p].cuda(), dec.v[p].cuda(), dec.g[p].cuda(),
+                            dec.beta[p].cuda(), state, z=dec.z[p].cuda())
+    torch.cuda.synchronize()
+    yo, _, so = oracle.decode_steps(dec, steps)
+    ey = rel_l2(y.cpu().double().numpy(), yo)
+    es = rel_l2(state.cpu().double().numpy().reshape(so.shape), so)
+    log(f"[parity] decode {dtype} d={d}: y={ey:.3e} state={es:.3e}")
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_decode_ungated_and_scaled(kda):
+    dec = kda_inputs.make_decode(N=2, H=2, dk=128, dv=128, dtype="f32", gated=False,
+                                 s0_std=0.5, pool=1, seed=8)
+    state = dec.S0.clone().cuda()
+    y = kda.decode_step(dec.q[0].cuda(), dec.k[0].cuda(), dec.v[0].cuda(), dec.g[0].cuda(),
+                        dec.beta[0].cuda(), state, scale=0.25)
+    torch.cuda.synchronize()
+    yo, _, so = oracle.decode_steps(dec, 1, scale=0.25)
+    assert rel_l2(y.cpu().double().numpy(), yo) <= 1e-5
+    assert rel_l2(state.cpu().double().numpy().reshape(so.shape), so) <= 1e-5
+
+
+# ---------------------------------------------------------------- prefill
+def test_prefill_tiny_fp32_workload(kda):
+    """B=1, H=2, T=256, dk=dv=64, chunk 16, fp32, ungated, S0 = 0."""
+    inp = kda_inputs.make_workload(0)
+    y, fs = run_prefill(kda, inp, chunk=16)
+    yo, so = oracle_prefill(inp)
+    assert_parity("tiny fp32 c16", inp, y, fs, yo, so, TOL["f32"])
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+@pytest.mark.parametrize("stress", [None, "chunk"])
+def test_prefill_fp32_d64(kda, chunk, stress):
+    inp = kda_inputs.make_workload(0, stress, lens=[333], H=3, gated=True, s0_std=0.1)
+    y, fs = run_prefill(kda, inp, chunk=chunk, scale=0.5)
+    yo, so = oracle_prefill(inp, scale=0.5)
+    assert_parity(f"fp32 d64 c{chunk} {stress}", inp, y, fs, yo, so, TOL["f32"])
+
+
+@pytest.mark.parametrize("stress", [None, "chunk"])
+def test_prefill_fp32_d128_chunk16(kda, stress):
+    inp = kda_inputs.make_workload(1, stress, lens=[197], H=2, dtype="f32", s0_std=0.05)
+    y, fs = run_prefill(kda, inp, chunk=16)
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"fp32 d128 c16 {stress}", inp, y, fs, yo, so, TOL["f32"])
+
+
+@pytest.mark.parametrize("chunk", [64, 16])
+@pytest.mark.parametrize("stress", [None, "chunk"])
+def test_prefill_bf16_d128(kda, chunk, stress):
+    inp = kda_inputs.make_workload(1, stress, lens=[1000], H=4, s0_std=0.02)
+    y, fs = run_prefill(kda, inp, chunk=chunk)
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"bf16 d128 c{chunk} {stress}", inp, y, fs, yo, so, TOL["bf16"])
+
+
+@pytest.mark.parametrize("chunk", [64, 16])
+def test_prefill_bf16_d64(kda, chunk):
+    inp = kda_inputs.make_workload(1, "chunk", lens=[517], H=3, dk=64, dv=64, s0_std=0.05)
+    y, fs = run_prefill(kda, inp, chunk=chunk)
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"bf16 d64 c{chunk}", inp, y, fs, yo, so, TOL["bf16"])
+
+
+def test_prefill_varlen_with_ragged_and_empty_sequences(kda):
+    lens = [1, 17, 64, 65, 0, 200, 127, 3]
+    inp = kda_inputs.make_prefill(lens, 5, 128, 128, "bf16", True, 0.02, 77, 8.0, 4.0)
+    y, fs = run_prefill(kda, inp, chunk=64)
+    yo, so = oracle_prefill(inp)
+    assert_parity("varlen ragged", inp, y, fs, yo, so, TOL["bf16"])
+    # the empty sequence passes its initial state through unchanged
+    np.testing.assert_array_equal(fs[4].numpy(), inp.S0[4].numpy())
+
+
+def test_prefill_varlen_workload_shape_reduced(kda):
+    """Varlen workload recipe (16 sequences, lengths uniform) at reduced lengths and heads."""
+    inp = kda_inputs.make_workload(2, H=6, lmin=20, lmax=700)
+    y, fs = run_prefill(kda, inp, chunk=64)
+    yo, so = oracle_prefill(inp)
+    assert_parity("varlen workload reduced", inp, y, fs, yo, so, TOL["bf16"])
+
+
+def test_prefill_beta_zero_is_pure_decay(kda):
+    """beta = 0 and S0 != 0: y_t = scale (e^{G_t} * S0)^T q_t exactly (GPU invariant run)."""
+    inp = kda_inputs.make_workload(0, "chunk", lens=[300], H=2, s0_std=1.0)
+    inp.beta.zero_()
+    y, fs = run_prefill(kda, inp, chunk=64)
+    yo, so = oracle_prefill(inp)
+    assert_parity("beta=0", inp, y, fs, yo, so, TOL["f32"])
+
+
+def test_prefill_exact_retrieval_orthonormal_keys(kda):
+    """alpha = 1, beta = 1, orthonormal keys, S0 = 0: query k_j returns v_j."""
+    T, d = 100, 128
+    rng = np.random.default_rng(5)
+    Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    keys = torch.tensor(Qm[:, :T].T.copy(), dtype=torch.float32)
+    v = torch.tensor(rng.standard_normal((T, d)), dtype=torch.float32)
+    pick = torch.tensor([int(rng.integers(0, t + 1)) for t in range(T)])
+    inp = kda_inputs.KDAInputs(q=keys[pick][:, None].contiguous(), k=keys[:, None].contiguous(),
+                               v=v[:, None].contiguous(), z=None,
+                               g=torch.zeros(T, 1, d), beta=torch.ones(T, 1),
+                               cu_seqlens=torch.tensor([0, T], dtype=torch.int32), S0=None,
+                               H=1, dk=d, dv=d, dtype="f32")
+    y, fs = run_prefill(kda, inp, chunk=16)
+    err = (y[:, 0].double() - v[pick].double()).abs().max().item()
+    log(f"[parity] exact retrieval max abs err {err:.3e}")
+    assert err <= 1e-4
+
+
+def test_prefill_chunk16_equals_chunk64(kda):
+    inp = kda_inputs.make_workload(1, "chunk", lens=[700], H=2, s0_std=0.02)
+    y16, s16 = run_prefill(kda, inp, chunk=16)
+    y64, s64 = run_prefill(kda, inp, chunk=64)
+    assert rel_l2(y16.double().numpy(), y64.double().numpy()) <= TOL["bf16"]
+    assert rel_l2(s16.double().numpy(), s64.double().numpy()) <= TOL["bf16"]
+
+
+def test_prefill_resume_equals_single_call(kda):
+    inp = kda_inputs.make_workload(1, "chunk", lens=[600], H=2, s0_std=0.02)
+    y, fs = run_prefill(kda, inp, chunk=64)
+    a = kda_inputs.KDAInputs(inp.q[:250], inp.k[:250], inp.v[:250], inp.z[:250], inp.g[:250],
+                             inp.beta[:250], torch.tensor([0, 250], dtype=torch.int32), inp.S0,
+                             inp.H, inp.dk, inp.dv, inp.dtype)
+    b = kda_inputs.KDAInputs(inp.q[250:], inp.k[250:], inp.v[250:], inp.z[250:], inp.g[250:],
+                             inp.beta[250:], torch.tensor([0, 350], dtype=torch.int32), None,
+                             inp.H, inp.dk, inp.dv, inp.dtype)
+    ya, sa = run_prefill(kda, a, chunk=64)
+    yb, sb = run_prefill(kda, b, chunk=64, S0=sa)
+    assert rel_l2(torch.cat([ya, yb]).double().numpy(), y.double().numpy()) <= 1e-2
+    assert rel_l2(sb.double().numpy(), fs.double().numpy()) <= 1e-2
+
+
+def test_prefill_is_deterministic(kda):
+    inp = kda_inputs.make_workload(2, H=4, lmin=50, lmax=300)
+    y1, s1 = run_prefill(kda, inp, chunk=64)
+    y2, s2 = run_prefill(kda, inp, chunk=64)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+def test_prefill_final_state_may_alias_initial_state(kda):
+    inp = kda_inputs.make_workload(1, "chunk", lens=[300], H=2, s0_std=0.02)
+    st = inp.S0.clone().cuda()
+    y, _ = kda.chunk_fwd(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(),
+                         inp.beta.cuda(), z=inp.z.cuda(), initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    yo, so = oracle_prefill(inp)
+    assert_parity("aliased state", inp, y.cpu(), st.cpu(), yo, so, TOL["bf16"])
+
+
+# ---------------------------------------------------------------- KCP
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 64, 16), ("bf16", 64, 64)])
+def test_kcp_scan_matches_sequential_oracle(kda, dtype, d, chunk):
+    inp = kda_inputs.make_workload(3, "segment", lens=[4096], H=2, dk=d, dv=d, dtype=dtype,
+                                   s0_std=0.05, gated=True)
+    nseg = 8
+    y, fs = kda.kcp_scan(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(),
+                         inp.beta.cuda(), nseg, z=inp.z.cuda(), initial_state=inp.S0.cuda(),
+                         chunk=chunk)
+    torch.cuda.synchronize()
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"kcp {dtype} d{d} c{chunk}", inp, y.cpu(), fs.cpu(), yo, so, TOL[dtype])
+
+
+def test_kcp_ragged_segments(kda):
+    """T not a multiple of the segment count (trailing segments shorter or empty)."""
+    inp = kda_inputs.make_workload(3, "segment", lens=[1001], H=2, s0_std=0.05)
+    y, fs = kda.kcp_scan(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(),
+                         inp.beta.cuda(), 7, initial_state=inp.S0.cuda())
+    torch.cuda.synchronize()
+    yo, so = oracle_prefill(inp)
+    assert_parity("kcp ragged", inp, y.cpu(), fs.cpu(), yo, so, TOL["bf16"])
+
+
+def test_kcp_equals_chunk_fwd(kda):
+    inp = kda_inputs.make_workload(3, "segment", lens=[2048], H=2)
+    yk, sk = kda.kcp_scan(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(),
+                          inp.beta.cuda(), 16)
+    yc, sc = run_prefill(kda, inp, chunk=64)
+    torch.cuda.synchronize()
+    assert rel_l2(yk.cpu().double().numpy(), yc.double().numpy()) <= 1e-2
+    assert rel_l2(sk.cpu().double().numpy(), sc.double().numpy()) <= 1e-2
