@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of libkda on one MI355X.
+
+The headline line times the KDA prefill at the K3 layer shape (B=1, H=96,
+T=8192, dk=dv=128, bf16 q/k/v/z, fp32 g/beta, fp32 state, chunk 64, output
+gate, final state emitted): `value` is tokens/s with the inputs resident in
+HBM.  The other workloads of the method (varlen prefill, the KCP scan of a
+1M-token sequence, the decode step) are timed in the same run and reported
+under "workloads".  The fp64 CPU oracle is timed on a sample of the headline
+workload on the host's cores ("cpu_baseline") and its outputs double as a
+parity spot check ("parity_sample").
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b]
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
+ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ work model
+def prefill_bytes(tokens: int, H: int, dk: int, dv: int, elt: int, gated: bool,
+                  nseq: int, reads_s0: bool, writes_sT: bool) -> int:
+    """Algorithmic HBM bytes: every input read once, every output written once."""
+    per_th = 2 * dk * elt + dv * elt + (dv * elt if gated else 0) + dv * elt + dk * 4 + 4
+    states = nseq * H * dk * dv * 4 * (int(reads_s0) + int(writes_sT))
+    return tokens * H * per_th + states
+
+
+def prefill_flops(tokens: int, H: int, dk: int, dv: int, C: int) -> float:
+    """Triangle-aware flops of the chunked form per token-head:
+    2 [3 dk dv + C (3 dk + 2 dv) / 2] (state products + intra-chunk products)."""
+    return float(tokens) * H * 2 * (3 * dk * dv + C * (3 * dk + 2 * dv) / 2)
+
+
+def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int, gated: bool) -> int:
+    state = 2 * N * H * dk * dv * 4
+    inputs = N * H * (2 * dk * elt + dv * elt + (dv * elt if gated else 0) + dk * 4 + 4)
+    return state + inputs + N * H * dv * elt
+
+
+# ------------------------------------------------------------------ helpers
+def time_steps(fn, steps: int, warmup: int, torch):
+    """Average ms per call of fn over `steps` calls, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def gpu_inputs(torch, lens, H, dk, dv, gated, s0_std, seed, dev):
+    """The synthetic recipe drawn directly on the GPU (same distributions as
+    kda_inputs; used for workloads too large to draw on the host quickly)."""
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    T = int(sum(lens))
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    q = unit(torch.randn(T, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
+    k = unit(torch.randn(T, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
+    v = torch.randn(T, H, dv, generator=gen, device=dev).to(torch.bfloat16)
+    z = torch.randn(T, H, dv, generator=gen, device=dev).to(torch.bfloat16) if gated else None
+    beta = torch.sigmoid(torch.randn(T, H, generator=gen, device=dev))
+    g = -5.0 * torch.sigmoid(torch.randn(T, H, dk, generator=gen, device=dev))
+    s0 = None
+    if s0_std > 0:
+        s0 = torch.randn(len(lens), H, dk, dv, generator=gen, device=dev) * s0_std
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    return dict(q=q, k=k, v=v, z=z, beta=beta, g=g, s0=s0, cu=cu.to(dev))
+
+
+# ------------------------------------------------------------------ workloads
+def bench_headline(args, torch, kda, kda_inputs, dev):
+    w = kda_inputs.WORKLOADS[1]
+    H, dk, dv, T, C = w["H"], w["dk"], w["dv"], w["lens"][0], w["chunk"]
+    log(f"headline k3_layer_prefill: drawing inputs H={H} T={T} d={dk}")
+    inp = kda_inputs.make_workload(1)
+    d = {n: getattr(inp, n).to(dev) for n in ("q", "k", "v", "z", "g", "beta")}
+    y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+
+    def step():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C, y=y,
+                      final_state=fs)
+
+    ms, wall = time_steps(step, args.steps, args.warmup, torch)
+    log(f"headline: {ms:.4f} ms per step ({args.steps} steps, wall {wall:.3f} s)")
+    nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True)
+    flops = prefill_flops(T, H, dk, dv, C)
+    res = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), bytes=nbytes, flops=flops,
+               gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12)
+    return inp, res, (y, fs)
+
+
+def bench_cpu_baseline(args, inp, gpu_out, torch):
+    import numpy as np
+    import oracle
+    H, T = inp.H, inp.T
+    nh = max(1, min(H, args.cpu_sample_heads))
+    heads = list(range(0, H, max(1, H // nh)))[:nh]
+    threads = oracle.default_threads()
+    log(f"cpu baseline: fp64 oracle on {len(heads)} of {H} heads, T={T}, {threads} threads")
+    t0 = time.perf_counter()
+    yo, so = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, z=inp.z,
+                               chains=[(0, h) for h in heads], nthreads=threads)
+    wall = time.perf_counter() - t0
+    log(f"cpu baseline: {wall:.2f} s")
+    y, fs = gpu_out
+    yg = y.cpu().double().numpy()[:, heads]
+    sg = fs.cpu().double().numpy()[0, heads]
+    ey = oracle.rel_l2(yg, yo[:, heads])
+    es = oracle.rel_l2(sg, so)
+    cpu = {"value": T / (wall * H / len(heads)), "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": (f"{len(heads)} of {H} heads of k3_layer_prefill (T={T}, full chains), fp64 "
+                      f"sequential recurrence in C, {wall:.2f} s wall; value scaled to all {H} heads")}
+    parity = {"heads": len(heads), "rel_l2_y": ey, "rel_l2_state": es, "tolerance": 2e-2}
+    return cpu, parity
+
+
+def bench_varlen(args, torch, kda, kda_inputs, dev):
+    w = kda_inputs.WORKLOADS[2]
+    gen = torch.Generator().manual_seed(kda_inputs.workload_seed(2))
+    lens = torch.randint(w["lmin"], w["lmax"] + 1, (w["nseq"],), generator=gen).tolist()
+    H, dk, dv = w["H"], w["dk"], w["dv"]
+    log(f"varlen_prefill: {len(lens)} sequences, {sum(lens)} tokens")
+    d = gpu_inputs(torch, lens, H, dk, dv, True, w["s0_std"], kda_inputs.workload_seed(2), dev)
+    T = sum(lens)
+    y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(len(lens), H, dk, dv, dtype=torch.float32, device=dev)
+
+    def step():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], z=d["z"],
+                      initial_state=d["s0"], chunk=w["chunk"], y=y, final_state=fs)
+
+    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch)
+    nbytes = prefill_bytes(T, H, dk, dv, 2, True, len(lens), True, True)
+    out = dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3),
+               gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               tflops=prefill_flops(T, H, dk, dv, w["chunk"]) / (ms * 1e-3) / 1e12)
+    del d, y, fs
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_kcp(args, torch, kda, kda_inputs, dev):
+    w = kda_inputs.WORKLOADS[3]
+    H, dk, dv, T, S = w["H"], w["dk"], w["dv"], w["lens"][0], w["segments"]
+    log(f"kcp_long_sequence: T={T} H={H} segments={S}")
+    d = gpu_inputs(torch, [T], H, dk, dv, False, 0.0, kda_inputs.workload_seed(3), dev)
+    ws = torch.empty(kda.kcp_workspace_size(H, dk, dv, S), dtype=torch.uint8, device=dev)
+    y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+
+    def step():
+        kda.kcp_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], S, chunk=w["chunk"],
+                     workspace=ws, y=y, final_state=fs)
+
+    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch)
+    nbytes = prefill_bytes(T, H, dk, dv, 2, False, 1, False, True)
+    out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), segments=S,
+               gbs_single_pass=nbytes / (ms * 1e-3) / 1e9,
+               hbm_frac_single_pass=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del d, ws, y, fs
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(args, torch, kda, kda_inputs, dev):
+    w = kda_inputs.WORKLOADS[4]
+    N, H, dk, dv, P, steps = w["N"], w["H"], w["dk"], w["dv"], w["pool"], w["steps"]
+    log(f"decode: N={N} H={H} pool={P} steps={steps}")
+    gen = torch.Generator(device=dev).manual_seed(kda_inputs.workload_seed(4))
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    state = torch.randn(N, H, dk, dv, generator=gen, device=dev) * w["s0_std"]
+    pool = []
+    for _ in range(P):
+        pool.append(dict(
+            q=unit(torch.randn(N, H, dk, generator=gen, device=dev)).to(torch.bfloat16),
+            k=unit(torch.randn(N, H, dk, generator=gen, device=dev)).to(torch.bfloat16),
+            v=torch.randn(N, H, dv, generator=gen, device=dev).to(torch.bfloat16),
+            z=torch.randn(N, H, dv, generator=gen, device=dev).to(torch.bfloat16),
+            beta=torch.sigmoid(torch.randn(N, H, generator=gen, device=dev)),
+            g=-5.0 * torch.sigmoid(torch.randn(N, H, dk, generator=gen, device=dev))))
+    y = torch.empty(N, H, dv, dtype=torch.bfloat16, device=dev)
+
+    def run_all():
+        for s in range(steps):
+            p = pool[s % P]
+            kda.decode_step(p["q"], p["k"], p["v"], p["g"], p["beta"], state, z=p["z"], y=y)
+
+    ms_all, _ = time_steps(run_all, 1, 1, torch)
+    ms = ms_all / steps
+    nbytes = decode_bytes(N, H, dk, dv, 2, True)
+    out = dict(ms_per_step=ms, steps=steps, tokens_per_s=N / (ms * 1e-3),
+               bytes_per_step=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del state, pool, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="all",
+                    help="comma list of extra workloads (%s), 'all' or 'none'" % ",".join(ALL_WORKLOADS))
+    ap.add_argument("--cpu-sample-heads", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the KDA path here has no multi-GPU leg "
+              "(heads and requests shard with no exchange; see the design notes).",
+              file=sys.stderr)
+        return 2
+    import torch
+    import gated_delta_rule_75_amd as kda
+    import kda_inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    kda.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    inp, head, gpu_out = bench_headline(args, torch, kda, kda_inputs, dev)
+    extras = ALL_WORKLOADS if args.workloads == "all" else tuple(
+        x for x in args.workloads.split(",") if x and x != "none")
+    workloads = {}
+    for name in extras:
+        fn = {"varlen_prefill": bench_varlen, "kcp_long_sequence": bench_kcp,
+              "decode": bench_decode}[name]
+        workloads[name] = fn(args, torch, kda, kda_inputs, dev)
+        log(f"{name}: {json.dumps(workloads[name])}")
+    cpu, parity = (None, None)
+    if not args.no_cpu_baseline:
+        cpu, parity = bench_cpu_baseline(args, inp, gpu_out, torch)
+
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "k3_layer_prefill", "B": 1, "H": 96, "T": 8192, "dk": 128,
+                   "dv": 128, "chunk": 64, "gated": True, "state": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "prefill_kernel (kModeSeq, bf16, dk=dv=128, chunk 64)",
+                     "bytes_per_launch": head["bytes"]},
+        "mfma": {"achieved": head["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": head["tflops"] / BF16_MFMA_PEAK_TFLOPS,
+                 "flops_per_launch": head["flops"]},
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -81,7 +81,7 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
     a.final_state = final_state;
     a.final_seq_lo = 0;
     a.y = y;
-    a.aug = 0;
+    a.mode = cu_seqlens ? 1 : 0;
     a.vs = 0;
     a.stream = stream;
     return from_hip(kda::launch_prefill(a));
@@ -138,7 +138,7 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.vs = 0;
     // phase 1: (M, Sloc) of every segment, as the state that the augmented value
     // block [0 | v] builds from the augmented start [I | 0]
-    a.aug = 1;
+    a.mode = 2;
     a.initial_state = nullptr;
     a.final_state = pairs;
     a.final_seq_lo = 0;
@@ -151,7 +151,7 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     if (e != hipSuccess) return KDA_ERR_HIP;
     // phase 3: outputs of every segment from its entering state; the last
     // segment's final state is the sequence's final state
-    a.aug = 0;
+    a.mode = 3;
     a.initial_state = starts;
     a.final_state = final_state;
     a.final_seq_lo = num_segments - 1;

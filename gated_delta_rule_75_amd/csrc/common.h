@@ -72,6 +72,21 @@ __device__ __forceinline__ typename E::Frag lds_frag(const typename E::T* base, 
     return *reinterpret_cast<const typename E::Frag*>(p);
 }
 
+// Fragment of a reduction shorter than one MFMA (klim < KSTEP, klim a
+// multiple of KPL): lanes whose k range starts at or past klim supply zeros.
+template <typename E>
+__device__ __forceinline__ typename E::Frag lds_frag_lim(const typename E::T* base, int ld, int r0,
+                                                         int k0, int lane, int klim) {
+    typename E::Frag f;
+    if (k0 + E::KPL * (lane >> 4) < klim) {
+        f = lds_frag<E>(base, ld, r0, k0, lane);
+    } else {
+#pragma unroll
+        for (int i = 0; i < E::KPL; ++i) frag_set<E>(f, i, 0.f);
+    }
+    return f;
+}
+
 // Same fragment with every element multiplied by a per-k factor table (fp32,
 // indexed by absolute k).
 template <typename E>
@@ -101,6 +116,6 @@ __device__ __forceinline__ f32x2_t gload2(const float* p) {
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace kda

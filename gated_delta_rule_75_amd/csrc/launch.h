@@ -31,11 +31,13 @@ struct PrefillArgs {
     const float *g, *beta;
     const void* z;
     const float* initial_state;  // [num_seqs, H, dk, dv] or NULL
-    float* final_state;          // see final_seq_lo / aug
+    float* final_state;          // see final_seq_lo and mode 2
     int final_seq_lo;            // only sequences n >= final_seq_lo write final_state[n - lo]
-    void* y;                     // NULL only in aug mode
-    int aug;                     // KCP pair mode: value width dk + dv, identity start on the
-                                 // first dk columns, final_state gets [num_seqs, H, dk, dk + dv]
+    void* y;                     // NULL only in mode 2
+    int mode;                    // 0 one sequence / equal segments, 1 varlen (cu_seqlens),
+                                 // 2 KCP pairs: value width dk + dv, identity start on the first
+                                 //   dk columns, final_state gets [num_seqs, H, dk, dk + dv],
+                                 // 3 KCP segment outputs
     int vs;                      // value-slice width per workgroup (0 = library choice)
     void* stream;
 };

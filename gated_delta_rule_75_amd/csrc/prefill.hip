@@ -51,29 +51,42 @@ struct PrefillParams {
     void* y;
 };
 
-template <typename E_, int DK_, int VS_, int CH_, bool AUG_>
+// Launch modes.  They share one kernel body; distinct instantiations keep the
+// per-kernel profiler statistics of the different call sites apart.
+enum PfMode : int {
+    kModeSeq = 0,     // one sequence, or equal segments (no offsets array)
+    kModeVarlen = 1,  // packed sequences given by cu_seqlens
+    kModePairs = 2,   // KCP segment pairs: augmented state [I | 0], values [0 | v], no outputs
+    kModeFinish = 3,  // KCP outputs of every segment from its entering state
+};
+
+template <typename E_, int DK_, int VS_, int CH_, int MODE_>
 struct PfCfg {
     using E = E_;
     using T = typename E::T;
-    static constexpr int DK = DK_, VS = VS_, CH = CH_;
-    static constexpr bool AUG = AUG_;
+    static constexpr int DK = DK_, VS = VS_, CH = CH_, MODE = MODE_;
+    static constexpr bool AUG = MODE_ == kModePairs;
     static constexpr int NT = CH / 16, NCT = DK / 16, NVT = VS / 16;
     static constexpr int PADE = 16 / (int)sizeof(T);
     static constexpr int LDK = DK + PADE;  // pitch of [.][DK] operand arrays
     static constexpr int LCH = CH + PADE;  // pitch of [.][CH] operand arrays
     static constexpr int LN = CH + 4;      // pitch of the fp32 N array
-    static constexpr int NW = 4, NTHR = 256;
+    static constexpr int NW = 8, NTHR = 64 * NW;
+    // Waves 0-3 own the state and the R tiles; waves 4-7 own the output tiles
+    // and the diagonal inverses.
     static constexpr int NG = NTHR / (DK / 2);  // token groups of the decay phase
     static constexpr int L = CH / NG;           // tokens per thread in that phase
     static constexpr int GPT = 16 / L;          // token groups per 16-token tile
-    static constexpr int NOT = NT * NVT;        // output (t, v) tiles
-    static constexpr int OPW = (NOT + NW - 1) / NW;
-    static constexpr int NST = NCT * NVT;       // state (c, v) tiles
-    static constexpr int SPW = NST / NW;
+    static constexpr int NOT = NT * NVT;        // (t, v) tiles of R, Delta and O
+    static constexpr int OPW = (NOT + 3) / 4;   // R / O tiles per wave of a 4-wave group
+    static constexpr int DPW = (NOT + NW - 1) / NW;  // Delta tiles per wave
+    static constexpr int NST = NCT * NVT;       // (c, v) state tiles
+    static constexpr int SPW = NST / 4;         // state tiles per wave of waves 0-3
     static constexpr int NPAIR = NT * (NT + 1) / 2;
     static constexpr int NTASK = AUG ? NPAIR : 2 * NPAIR;
+    static_assert(NT == 1 || NT == 4, "chunk of 16 or 64 tokens");
     static_assert(L >= 1 && 16 % L == 0, "decay-phase token groups must tile 16");
-    static_assert(NST % NW == 0, "state tiles per wave");
+    static_assert(NST % 4 == 0, "state tiles per wave");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t SZ_OP = (size_t)CH * LDK * sizeof(T);
@@ -84,25 +97,25 @@ struct PfCfg {
     static constexpr size_t O_ST = O_KT + al((size_t)DK * LCH * sizeof(T));
     static constexpr size_t O_N = O_ST + al((size_t)VS * LDK * sizeof(T));
     static constexpr size_t SZ_N0 = (size_t)CH * LN * 4, SZ_N1 = (size_t)VS * LCH * sizeof(T);
-    static constexpr size_t O_T = O_N + al(SZ_N0 > SZ_N1 ? SZ_N0 : SZ_N1);
+    static constexpr size_t O_NT = O_N + al(SZ_N0 > SZ_N1 ? SZ_N0 : SZ_N1);
+    static constexpr size_t O_T = O_NT + (size_t)NT * 16 * 16 * 4;
     static constexpr size_t O_P = O_T + al((size_t)CH * LCH * sizeof(T));
     static constexpr size_t O_RT = O_P + al((size_t)CH * LCH * sizeof(T));
     static constexpr size_t O_GS = O_RT + al((size_t)VS * LCH * sizeof(T));
     static constexpr size_t O_ES = O_GS + (size_t)NG * DK * 4;
-    static constexpr size_t O_TAU = O_ES + (size_t)NT * DK * 4;
-    static constexpr size_t O_F = O_TAU + (size_t)NT * DK * 4;
-    static constexpr size_t O_EGC = O_F + (size_t)NT * NT * DK * 4;
+    static constexpr size_t O_D = O_ES + (size_t)NT * DK * 4;
+    static constexpr size_t O_EGC = O_D + (size_t)NT * NT * DK * 4;
     static constexpr size_t O_BETA = O_EGC + (size_t)DK * 4;
     static constexpr size_t O_MISC = O_BETA + (size_t)CH * 4;
     static constexpr size_t BYTES = O_MISC + 16;
     // aliases of regions that are dead while they are used
-    static constexpr size_t O_TT = O_KR;   // L^{-1} transposed, during the inverse only
-    static constexpr size_t O_YT = O_QR;   // per-wave 16x16 scratch of the inverse
+    static constexpr size_t O_TT = O_KC;   // L^{-1} transposed, during the inverse only
+    static constexpr size_t O_YT = O_GS;   // per-wave 16x16 scratch of the inverse
     static constexpr size_t O_DT = O_N;    // Delta^T, after the inverse
-    static constexpr size_t O_SORT = O_KR; // sequence lengths / ranks, before the first chunk
-    static_assert((size_t)CH * LCH * sizeof(T) <= SZ_OP, "L^-1 transpose fits the Kr region");
-    static_assert(NT == 1 || (size_t)NW * 16 * (16 + PADE) * sizeof(T) <= SZ_OP, "inverse scratch fits");
-    static_assert(BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+    static constexpr size_t O_SORT = O_KR; // sequence lengths, before the first chunk
+    static constexpr bool FITS = BYTES <= 160 * 1024 &&
+        (size_t)CH * LCH * sizeof(T) <= SZ_OP &&
+        (NT == 1 || (size_t)3 * 16 * (16 + PADE) * sizeof(T) <= (size_t)NG * DK * 4);
 };
 
 // Pairs of consecutive channels of q / k as loaded from global memory.
@@ -110,42 +123,113 @@ template <typename T> struct Pair2;
 template <> struct Pair2<__bf16> { using type = bf16x2_t; };
 template <> struct Pair2<float> { using type = f32x2_t; };
 
-template <typename T>
-__device__ __forceinline__ f32x2_t pair_f32(const typename Pair2<T>::type& p) {
-    return f32x2_t{to_f32(p[0]), to_f32(p[1])};
+__device__ __forceinline__ void st_pair(__bf16* p, float a, float b) {
+    *reinterpret_cast<bf16x2_t*>(p) = bf16x2_t{(__bf16)a, (__bf16)b};
+}
+__device__ __forceinline__ void st_pair(float* p, float a, float b) {
+    *reinterpret_cast<f32x2_t*>(p) = f32x2_t{a, b};
 }
 
-// 16x16x16 product acc += A[16 x 16] B[16 x 16]^T-stored, operands in LDS:
-// A rows r (k contiguous, fp32 or element type), B stored as rows = output
-// columns with k contiguous (element type).
+// n consecutive elements (n*sizeof(T) a multiple of 4, 4-byte aligned).
+template <int n>
+__device__ __forceinline__ void st_row(__bf16* p, const float* v) {
+    if constexpr (n % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < n; i += 8) {
+            bf16x8_t w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (__bf16)v[i + e];
+            *reinterpret_cast<bf16x8_t*>(p + i) = w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < n; ++i) p[i] = (__bf16)v[i];
+    }
+}
+template <int n>
+__device__ __forceinline__ void st_row(float* p, const float* v) {
+#pragma unroll
+    for (int i = 0; i < n; ++i) p[i] = v[i];
+}
+
+// 16x16x16 product acc += A B^T over a 16-deep reduction, operands in LDS:
+// A rows r (k contiguous; fp32 or the element type), B stored as rows =
+// output columns (k contiguous, element type).  bf16: one 16x16x32 MFMA whose
+// upper k half is zero; fp32: four 16x16x4 MFMAs.
 template <typename E, typename TA>
 __device__ __forceinline__ f32x4_t mma16(f32x4_t acc, const TA* A, int lda,
-                                         const typename E::T* B, int ldb, int lane) {
+                                         const typename E::T* B, int ldb, int lane);
+
+template <>
+__device__ __forceinline__ f32x4_t mma16<BF16, float>(f32x4_t acc, const float* A, int lda,
+                                                      const __bf16* B, int ldb, int lane) {
+    const int r = lane & 15, gq = lane >> 4;
+    bf16x8_t fa, fb;
+    if (gq < 2) {
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(A + r * lda + 8 * gq);
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(A + r * lda + 8 * gq + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            fa[e] = (__bf16)a0[e];
+            fa[e + 4] = (__bf16)a1[e];
+        }
+        fb = *reinterpret_cast<const bf16x8_t*>(B + r * ldb + 8 * gq);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fa[e] = fb[e] = (__bf16)0.f;
+    }
+    return BF16::mma(fa, fb, acc);
+}
+
+template <>
+__device__ __forceinline__ f32x4_t mma16<BF16, __bf16>(f32x4_t acc, const __bf16* A, int lda,
+                                                       const __bf16* B, int ldb, int lane) {
+    const int r = lane & 15, gq = lane >> 4;
+    bf16x8_t fa, fb;
+    if (gq < 2) {
+        fa = *reinterpret_cast<const bf16x8_t*>(A + r * lda + 8 * gq);
+        fb = *reinterpret_cast<const bf16x8_t*>(B + r * ldb + 8 * gq);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fa[e] = fb[e] = (__bf16)0.f;
+    }
+    return BF16::mma(fa, fb, acc);
+}
+
+template <>
+__device__ __forceinline__ f32x4_t mma16<F32, float>(f32x4_t acc, const float* A, int lda,
+                                                     const float* B, int ldb, int lane) {
     const int r = lane & 15, gq = lane >> 4;
 #pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += E::KSTEP) {
-        typename E::Frag fa, fb;
-#pragma unroll
-        for (int e = 0; e < E::KPL; ++e) {
-            const int kk = k0 + E::KPL * gq + e;
-            const bool in = kk < 16;
-            frag_set<E>(fa, e, in ? to_f32(A[r * lda + (in ? kk : 0)]) : 0.f);
-            frag_set<E>(fb, e, in ? to_f32(B[r * ldb + (in ? kk : 0)]) : 0.f);
-        }
-        acc = E::mma(fa, fb, acc);
-    }
+    for (int k0 = 0; k0 < 16; k0 += 4) acc = F32::mma(A[r * lda + k0 + gq], B[r * ldb + k0 + gq], acc);
     return acc;
 }
 
+// (ta, vt) of the m-th R / O tile of wave gw (0..3) of a 4-wave group.  With
+// 4 sub-tiles per chunk each wave owns one row tile, so the scaled row
+// operand of a k step is built once and shared by its NVT tiles.
 template <class C>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__device__ __forceinline__ void ro_tile(int gw, int m, int& ta, int& vt) {
+    if constexpr (C::NT == 4) {
+        ta = gw;
+        vt = m;
+    } else {
+        const int ti = gw + 4 * m;
+        ta = 0;
+        vt = ti;
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
     using E = typename C::E;
     using T = typename C::T;
     using T2 = typename Pair2<T>::type;
     constexpr int DK = C::DK, VS = C::VS, CH = C::CH, NT = C::NT, NVT = C::NVT;
     constexpr int LDK = C::LDK, LCH = C::LCH, LN = C::LN, L = C::L, GPT = C::GPT, NG = C::NG;
-    constexpr int KS = E::KSTEP;
+    constexpr int KS = E::KSTEP, NTHR = C::NTHR;
     constexpr bool AUG = C::AUG;
+    static_assert(C::FITS, "LDS budget of a gfx950 workgroup (160 KiB)");
 
     __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
     T* sKr = reinterpret_cast<T*>(smem + C::O_KR);
@@ -154,6 +238,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     T* sKt = reinterpret_cast<T*>(smem + C::O_KT);
     T* sSt = reinterpret_cast<T*>(smem + C::O_ST);
     float* sN = reinterpret_cast<float*>(smem + C::O_N);
+    float* sNt = reinterpret_cast<float*>(smem + C::O_NT);
     T* sDt = reinterpret_cast<T*>(smem + C::O_DT);
     T* sT = reinterpret_cast<T*>(smem + C::O_T);
     T* sTt = reinterpret_cast<T*>(smem + C::O_TT);
@@ -162,14 +247,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     T* sRt = reinterpret_cast<T*>(smem + C::O_RT);
     float* sGs = reinterpret_cast<float*>(smem + C::O_GS);
     float* sES = reinterpret_cast<float*>(smem + C::O_ES);
-    float* sTau = reinterpret_cast<float*>(smem + C::O_TAU);
-    float* sF = reinterpret_cast<float*>(smem + C::O_F);
+    float* sD = reinterpret_cast<float*>(smem + C::O_D);
     float* sEGC = reinterpret_cast<float*>(smem + C::O_EGC);
     float* sBeta = reinterpret_cast<float*>(smem + C::O_BETA);
     int* sMisc = reinterpret_cast<int*>(smem + C::O_MISC);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g4 = lane >> 4;
+    const int gw = wave & 3;            // wave index within its group of four
+    const bool lowg = wave < 4;         // waves 0-3: state, R; waves 4-7: outputs, inverse
 
     // ---- which (sequence, head, slice) this workgroup owns ------------------
     const int b = blockIdx.x;
@@ -183,9 +269,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     if (p.cu_seqlens && p.num_seqs > 1 && p.num_seqs <= 256) {
         // longest sequences first: find the sequence of rank `seqrank`
         int* sLen = reinterpret_cast<int*>(smem + C::O_SORT);
-        for (int i = tid; i < p.num_seqs; i += C::NTHR) sLen[i] = p.cu_seqlens[i + 1] - p.cu_seqlens[i];
+        for (int i = tid; i < p.num_seqs; i += NTHR) sLen[i] = p.cu_seqlens[i + 1] - p.cu_seqlens[i];
         __syncthreads();
-        for (int i = tid; i < p.num_seqs; i += C::NTHR) {
+        for (int i = tid; i < p.num_seqs; i += NTHR) {
             const int li = sLen[i];
             int rank = 0;
             for (int j = 0; j < p.num_seqs; ++j) {
@@ -209,7 +295,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const int64_t len = t1 > t0 ? t1 - t0 : 0;
     const int cb = slice * VS;                 // first state column of the slice
     const bool ident = AUG && cb < DK;         // KCP transition columns: V = 0, S0 = I
-    const int vcol0 = AUG ? (cb - DK) : cb;    // column of v feeding this slice
+    const int vcol0 = ident ? 0 : (AUG ? cb - DK : cb);  // column of v feeding this slice
     const int DV = AUG ? p.dvt - DK : p.dvt;   // row width of v / z / y
 
     const T* gq = static_cast<const T*>(p.q);
@@ -217,34 +303,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const T* gv = static_cast<const T*>(p.v);
     const T* gz = static_cast<const T*>(p.z);
     T* gy = static_cast<T*>(p.y);
+    const bool gated = !AUG && gz != nullptr;
 
-    // ---- state tiles owned by this wave: (ct, vt) = si / NVT, si % NVT -----
+    // ---- state tiles (waves 0-3): (ct, vt) = si / NVT, si % NVT, si = gw + 4m --
     f32x4_t S[C::SPW];
     {
         const int64_t sbase = ((int64_t)n * H + h) * DK * (int64_t)p.dvt;
 #pragma unroll
         for (int m = 0; m < C::SPW; ++m) {
-            const int si = wave + C::NW * m, ct = si / NVT, vt = si % NVT;
+            const int si = gw + 4 * m, ct = si / NVT, vt = si % NVT;
             const int col = cb + 16 * vt + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = 16 * ct + 4 * g4 + i;
                 float s = 0.f;
                 if (AUG) s = (col == c) ? 1.f : 0.f;
-                else if (p.s0) s = p.s0[sbase + (int64_t)c * p.dvt + col];
+                else if (p.s0 && lowg) s = p.s0[sbase + (int64_t)c * p.dvt + col];
                 S[m][i] = s;
+            }
+            if (lowg) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sSt[(16 * vt + r16) * LDK + 16 * ct + 4 * g4 + i] = from_f32<T>(S[m][i]);
             }
         }
     }
     // zero the upper-triangular blocks of P and L^{-1} (never written later)
-    for (int idx = tid; idx < CH * CH; idx += C::NTHR) {
+    for (int idx = tid; idx < CH * CH; idx += NTHR) {
         const int t = idx / CH, j = idx % CH;
         if ((j >> 4) > (t >> 4)) {
             sT[t * LCH + j] = from_f32<T>(0.f);
             sP[t * LCH + j] = from_f32<T>(0.f);
         }
     }
-    __syncthreads();  // also orders the sort scratch before its region is reused
 
     // ---- decay-phase thread mapping: channel pair cp, token group tg --------
     const int cp = tid % (DK / 2), tg = tid / (DK / 2);
@@ -254,150 +345,147 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     T2 rq[L], rk[L];
     f32x2_t rgv[L];
     float rbeta = 0.f;
-    auto load_chunk = [&](int64_t cs) {
+    // v (waves 0-3, R tiles) or z (waves 4-7, output tiles) in MMA-output layout
+    float vz[C::OPW][4];
+    const int64_t tclamp = len > 0 ? len - 1 : 0;
+    const int HDK = H * DK, HDV = H * DV;   // token strides (elements)
+    // Global addresses: a 64-bit row base per chunk plus 32-bit in-chunk offsets.
+    // Loads are unconditional from clamped rows; invalid tokens are masked at use.
+    auto load_qkg = [&](int64_t cs) {
+        const int64_t row = (t0 + cs) * H + h;
+        const int last = (int)(tclamp - cs);   // >= 0 while cs < len
+        const T* kb = gk + row * DK + c0;
+        const T* qb = gq + row * DK + c0;
+        const float* gb = p.g + row * DK + c0;
 #pragma unroll
         for (int l = 0; l < L; ++l) {
-            const int64_t tt = cs + tg * L + l;
-            const bool valid = tt < len;
-            const int64_t base = ((t0 + (valid ? tt : 0)) * H + h) * DK + c0;
-            if (valid) {
-                rk[l] = *reinterpret_cast<const T2*>(gk + base);
-                if (!AUG) rq[l] = *reinterpret_cast<const T2*>(gq + base);
-                rgv[l] = *reinterpret_cast<const f32x2_t*>(p.g + base);
-            } else {
-                rk[l] = T2{from_f32<T>(0.f), from_f32<T>(0.f)};
-                rq[l] = rk[l];
-                rgv[l] = f32x2_t{0.f, 0.f};
-            }
+            const int tr = tg * L + l < last ? tg * L + l : last;
+            rk[l] = *reinterpret_cast<const T2*>(kb + tr * HDK);
+            if (!AUG) rq[l] = *reinterpret_cast<const T2*>(qb + tr * HDK);
+            rgv[l] = *reinterpret_cast<const f32x2_t*>(gb + tr * HDK);
         }
         if (tid < CH) {
-            const int64_t tt = cs + tid;
-            rbeta = tt < len ? p.beta[(t0 + tt) * H + h] : 0.f;
+            const int tr = tid < last ? tid : last;
+            rbeta = p.beta[row + (int64_t)tr * H];
+        }
+    };
+    auto load_vz = [&](int64_t cs) {
+        if (lowg || gated) {
+            const int64_t row = (t0 + cs) * H + h;
+            const int last = (int)(tclamp - cs);
+            const T* src = (lowg ? gv : gz) + row * DV + vcol0 + r16;
+#pragma unroll
+            for (int m = 0; m < C::OPW; ++m) {
+                int ta, vt;
+                ro_tile<C>(gw, m, ta, vt);
+                const int vtc = vt < NVT ? vt : 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * ta + 4 * g4 + i;
+                    const int tr = t < last ? t : last;
+                    vz[m][i] = gload(src + tr * HDV + 16 * vtc);
+                }
+            }
         }
     };
 
     const int64_t nchunks = (len + CH - 1) / CH;
-    if (nchunks > 0) load_chunk(0);
-
-    // initial S^T (element type) for the first chunk's state products
-#pragma unroll
-    for (int m = 0; m < C::SPW; ++m) {
-        const int si = wave + C::NW * m, ct = si / NVT, vt = si % NVT;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sSt[(16 * vt + r16) * LDK + 16 * ct + 4 * g4 + i] = from_f32<T>(S[m][i]);
+    if (nchunks > 0) {
+        load_qkg(0);
+        load_vz(0);
     }
-
-    f32x4_t O[C::OPW];
-    float vreg[C::OPW][4], zreg[C::OPW][4];
+    __syncthreads();  // initial S^T and zeroed blocks visible; sort scratch consumed
 
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t cs = ch * CH;
-        // v and z of the output tiles this wave owns, in MMA-output layout
-#pragma unroll
-        for (int m = 0; m < C::OPW; ++m) {
-            const int ti = wave + C::NW * m;
-            const int ta = ti / NVT, vt = ti % NVT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t tt = cs + 16 * ta + 4 * g4 + i;
-                const bool valid = ti < C::NOT && tt < len;
-                const int64_t off = ((t0 + (valid ? tt : 0)) * H + h) * (int64_t)DV + vcol0 + 16 * vt + r16;
-                vreg[m][i] = (valid && !ident) ? gload(gv + off) : 0.f;
-                zreg[m][i] = (valid && !AUG && gz) ? gload(gz + off) : 0.f;
-            }
-        }
-
+        const int nvalid = len - cs < CH ? (int)(len - cs) : CH;
         // ================= phase 1: decay prefix and scaled operands ==========
-        float al0[L], al1[L], cp0[L], cp1[L], sf0[L], sf1[L];
-        float gs0 = 0.f, gs1 = 0.f;
-        {
-            float pr0 = 1.f, pr1 = 1.f;
+        // Thread (tg, cp) holds tokens tg*L .. tg*L+L-1 of channels c0, c0+1.
+        float cpv[2][L], sfv[2][L];
+        float gsum2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float al[L], pr = 1.f, gs = 0.f;
 #pragma unroll
             for (int l = 0; l < L; ++l) {
-                al0[l] = fast_exp(rgv[l][0]);
-                al1[l] = fast_exp(rgv[l][1]);
-                pr0 *= al0[l];
-                pr1 *= al1[l];
-                cp0[l] = pr0;
-                cp1[l] = pr1;
-                gs0 += rgv[l][0];
-                gs1 += rgv[l][1];
+                const bool valid = tg * L + l < nvalid;
+                const float gv_ = valid ? rgv[l][e] : 0.f;
+                al[l] = fast_exp(gv_);
+                pr *= al[l];
+                cpv[e][l] = pr;          // e^{G_t - G_first + g_first}
+                gs += gv_;
             }
-            sf0[L - 1] = 1.f;
-            sf1[L - 1] = 1.f;
+            sfv[e][L - 1] = 1.f;
 #pragma unroll
-            for (int l = L - 2; l >= 0; --l) {
-                sf0[l] = sf0[l + 1] * al0[l + 1];
-                sf1[l] = sf1[l + 1] * al1[l + 1];
-            }
+            for (int l = L - 2; l >= 0; --l) sfv[e][l] = sfv[e][l + 1] * al[l + 1];
+            gsum2[e] = gs;
         }
-        sGs[tg * DK + c0] = gs0;
-        sGs[tg * DK + c0 + 1] = gs1;
-        if (tid < CH) sBeta[tid] = rbeta;
+        st_pair(sGs + tg * DK + c0, gsum2[0], gsum2[1]);
+        if (tid < CH) sBeta[tid] = tid < nvalid ? rbeta : 0.f;
         __syncthreads();
         {
-            float gsum[2][NG];
-#pragma unroll
-            for (int q2 = 0; q2 < NG; ++q2) {
-                gsum[0][q2] = sGs[q2 * DK + c0];
-                gsum[1][q2] = sGs[q2 * DK + c0 + 1];
-            }
+            float E1[2], E2[2], E3[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int c = c0 + e;
-                float tileTot[NT], Sref[NT + 1];
+                float gsum[NG];
+#pragma unroll
+                for (int q2 = 0; q2 < NG; ++q2) gsum[q2] = sGs[q2 * DK + c];
+                float Sref[NT + 1];
+                Sref[0] = 0.f;
 #pragma unroll
                 for (int a = 0; a < NT; ++a) {
                     float s = 0.f;
 #pragma unroll
-                    for (int q2 = 0; q2 < GPT; ++q2) s += gsum[e][a * GPT + q2];
-                    tileTot[a] = s;
+                    for (int q2 = 0; q2 < GPT; ++q2) s += gsum[a * GPT + q2];
+                    Sref[a + 1] = Sref[a] + s;
                 }
-                Sref[0] = 0.f;
-#pragma unroll
-                for (int a = 0; a < NT; ++a) Sref[a + 1] = Sref[a] + tileTot[a];
                 float off = 0.f;
 #pragma unroll
                 for (int q2 = 0; q2 < NG; ++q2)
-                    if (q2 >= tile * GPT && q2 < tg) off += gsum[e][q2];
+                    if (q2 >= tile * GPT && q2 < tg) off += gsum[q2];
                 const float Sa = Sref[tile], GC = Sref[NT];
-                const float gs = e ? gs1 : gs0;
-                const float E1 = fast_exp(off);                   // e^{G_first - R_a} / alpha_first
-                const float E2 = fast_exp(-off - gs);             // e^{R_a - G_last}
-                const float E3 = fast_exp(GC - Sa - off - gs);    // e^{G_C - G_last}
-                const float* cpv = e ? cp1 : cp0;
-                const float* sfv = e ? sf1 : sf0;
-                T ktv[L];
+                E1[e] = fast_exp(off);                        // times cpv: e^{G_t - R_a}  (<= 1)
+                E2[e] = fast_exp(-off - gsum2[e]);            // times sfv: e^{R_a - G_t}  (<= e^80)
+                E3[e] = fast_exp(GC - Sa - off - gsum2[e]);   // times sfv: e^{G_C - G_t}  (<= 1)
+                if (tg == 0) {
+                    // per-channel tables: e^{R_a}, e^{R_a - R_b} (b < a), e^{G_C}
 #pragma unroll
-                for (int l = 0; l < L; ++l) {
-                    const int t = tg * L + l;
-                    const float kv = to_f32(rk[l][e]);
-                    const float f1 = E1 * cpv[l];   // e^{G_t - R_a}  (<= 1)
-                    const float f2 = E2 * sfv[l];   // e^{R_a - G_t}  (<= e^80)
-                    const float f3 = E3 * sfv[l];   // e^{G_C - G_t}  (<= 1)
-                    sKr[t * LDK + c] = from_f32<T>(kv * f1);
-                    if (!AUG) sQr[t * LDK + c] = from_f32<T>(to_f32(rq[l][e]) * f1);
-                    sKc[t * LDK + c] = from_f32<T>(kv * f2);
-                    ktv[l] = from_f32<T>(kv * f3);
-                }
+                    for (int a = 0; a < NT; ++a) {
+                        sES[a * DK + c] = fast_exp(Sref[a]);
 #pragma unroll
-                for (int l = 0; l < L; ++l) sKt[c * LCH + tg * L + l] = ktv[l];
-                if (gi == 0) {
-                    sES[tile * DK + c] = fast_exp(Sa);
-                    sTau[tile * DK + c] = fast_exp(tileTot[tile]);
-#pragma unroll
-                    for (int bb = 0; bb + 1 < tile; ++bb)
-                        sF[(tile * NT + bb) * DK + c] = fast_exp(Sa - Sref[bb + 1]);
-                    if (tile == 0) sEGC[c] = fast_exp(GC);
+                        for (int bb = 0; bb < a; ++bb)
+                            sD[(a * NT + bb) * DK + c] = fast_exp(Sref[a] - Sref[bb]);
+                    }
+                    sEGC[c] = fast_exp(GC);
                 }
             }
+            float kt0[L], kt1[L];
+#pragma unroll
+            for (int l = 0; l < L; ++l) {
+                const int t = tg * L + l;
+                const bool valid = t < nvalid;
+                const float k0 = valid ? to_f32(rk[l][0]) : 0.f, k1 = valid ? to_f32(rk[l][1]) : 0.f;
+                const float f10 = E1[0] * cpv[0][l], f11 = E1[1] * cpv[1][l];
+                st_pair(sKr + t * LDK + c0, k0 * f10, k1 * f11);
+                if (!AUG) {
+                    const float q0 = valid ? to_f32(rq[l][0]) : 0.f, q1 = valid ? to_f32(rq[l][1]) : 0.f;
+                    st_pair(sQr + t * LDK + c0, q0 * f10, q1 * f11);
+                }
+                st_pair(sKc + t * LDK + c0, k0 * (E2[0] * sfv[0][l]), k1 * (E2[1] * sfv[1][l]));
+                kt0[l] = k0 * (E3[0] * sfv[0][l]);
+                kt1[l] = k1 * (E3[1] * sfv[1][l]);
+            }
+            st_row<L>(sKt + c0 * LCH + tg * L, kt0);
+            st_row<L>(sKt + (c0 + 1) * LCH + tg * L, kt1);
         }
         // prefetch the next chunk's q, k, g, beta while this one computes
-        if (ch + 1 < nchunks) load_chunk(cs + CH);
+        if (ch + 1 < nchunks) load_qkg(cs + CH);
         __syncthreads();
 
-        // ================= phase 2: gated Gram blocks A (and P) ==============
+        // ================= phase 2: gated Gram blocks A and P ===================
+        // Block (a, b): rows use e^{G_t - R_a} (<= 1); columns use e^{R_a - G_j},
+        // i.e. the diagonal-reference column operand times e^{R_a - R_b} for b < a.
         for (int task = wave; task < C::NTASK; task += C::NW) {
             const int mat = task / C::NPAIR;  // 0: A (keys), 1: P (queries)
             const int pi = task % C::NPAIR;
@@ -406,79 +494,113 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
             const int bb = pi - a * (a + 1) / 2;
             const T* X = mat ? sQr : sKr;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 2
             for (int kk = 0; kk < DK; kk += KS) {
-                typename E::Frag fa = (bb + 1 < a)
-                    ? lds_frag_scaled<E>(X, LDK, 16 * a, kk, lane, sF + (a * NT + bb) * DK)
-                    : lds_frag<E>(X, LDK, 16 * a, kk, lane);
-                typename E::Frag fb = (bb < a)
-                    ? lds_frag_scaled<E>(sKc, LDK, 16 * bb, kk, lane, sTau + bb * DK)
+                const typename E::Frag fa = lds_frag<E>(X, LDK, 16 * a, kk, lane);
+                const typename E::Frag fb = (bb < a)
+                    ? lds_frag_scaled<E>(sKc, LDK, 16 * bb, kk, lane, sD + (a * NT + bb) * DK)
                     : lds_frag<E>(sKc, LDK, 16 * bb, kk, lane);
                 acc = E::mma(fa, fb, acc);
             }
             const int j = 16 * bb + r16;
+            if (mat == 0) {
+                if (bb == a) {
+                    // diagonal block of N = diag(beta) A, stored transposed for the inverse
+                    f32x4_t nv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * a + 4 * g4 + i;
-                if (mat == 0) {
-                    const bool keep = bb < a || j < t;
-                    sN[t * LN + j] = keep ? sBeta[t] * acc[i] : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * a + 4 * g4 + i;
+                        nv[i] = (j < t) ? sBeta[t] * acc[i] : 0.f;
+                    }
+                    *reinterpret_cast<f32x4_t*>(sNt + (a * 16 + r16) * 16 + 4 * g4) = nv;
                 } else {
-                    const bool keep = bb < a || j <= t;
-                    sP[t * LCH + j] = from_f32<T>(keep ? acc[i] : 0.f);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ================= phase 3: R = beta (V - (K e^G) S), O = (Q e^G) S ===
 #pragma unroll
-        for (int m = 0; m < C::OPW; ++m) {
-            const int ti = wave + C::NW * m;
-            if (ti < C::NOT) {
-                const int ta = ti / NVT, vt = ti % NVT;
-                f32x4_t ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < DK; kk += KS) {
-                    const typename E::Frag fb = lds_frag<E>(sSt, LDK, 16 * vt, kk, lane);
-                    ak = E::mma(lds_frag_scaled<E>(sKr, LDK, 16 * ta, kk, lane, sES + ta * DK), fb, ak);
-                    if (!AUG)
-                        aq = E::mma(lds_frag_scaled<E>(sQr, LDK, 16 * ta, kk, lane, sES + ta * DK), fb, aq);
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * a + 4 * g4 + i;
+                        sN[t * LN + j] = sBeta[t] * acc[i];
+                    }
                 }
-                O[m] = aq;
-                T rv[4];
+            } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * ta + 4 * g4 + i;
-                    rv[i] = from_f32<T>(sBeta[t] * (vreg[m][i] - ak[i]));
+                    const int t = 16 * a + 4 * g4 + i;
+                    sP[t * LCH + j] = from_f32<T>((bb < a || j <= t) ? acc[i] : 0.f);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sRt[(16 * vt + r16) * LCH + 16 * ta + 4 * g4 + i] = rv[i];
             }
         }
         __syncthreads();
 
-        // ================= phase 4: L^{-1}, L = I + N (N = diag(beta) A) ======
-        if (wave == 0 && lane < 16 * NT) {
-            // diagonal 16x16 blocks by forward substitution, one column per lane
-            const int a = lane >> 4, jj = lane & 15;
-            const float* Nb = sN + (16 * a) * LN + 16 * a;
-            float x[16];
+        // ================= phase 3: R = beta (V - (K e^G) S)  |  diagonal inverses
+        if (lowg) {
+            f32x4_t ak[C::OPW];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = 0.f;
+            for (int m = 0; m < C::OPW; ++m) ak[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            int ta0, vt0;
+            ro_tile<C>(gw, 0, ta0, vt0);
+#pragma unroll 2
+            for (int kk = 0; kk < DK; kk += KS) {
+                const typename E::Frag fa = lds_frag_scaled<E>(sKr, LDK, 16 * ta0, kk, lane, sES + ta0 * DK);
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc += Nb[i * LN + m] * x[m];
-                x[i] = (i > jj) ? -acc : (i == jj ? 1.f : 0.f);
+                for (int m = 0; m < C::OPW; ++m) {
+                    int ta, vt;
+                    ro_tile<C>(gw, m, ta, vt);
+                    if (vt < NVT) ak[m] = E::mma(fa, lds_frag<E>(sSt, LDK, 16 * vt, kk, lane), ak[m]);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const T xv = from_f32<T>(x[i]);
-                sT[(16 * a + i) * LCH + 16 * a + jj] = xv;
-                if (NT > 1) sTt[(16 * a + jj) * LCH + 16 * a + i] = xv;
+            for (int m = 0; m < C::OPW; ++m) {
+                int ta, vt;
+                ro_tile<C>(gw, m, ta, vt);
+                if (vt < NVT) {
+                    T rv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * ta + 4 * g4 + i;
+                        const float vv = ident ? 0.f : vz[m][i];
+                        rv[i] = from_f32<T>(sBeta[t] * (vv - ak[m][i]));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sRt[(16 * vt + r16) * LCH + 16 * ta + 4 * g4 + i] = rv[i];
+                }
+            }
+            if (ch + 1 < nchunks) load_vz(cs + CH);   // v of the next chunk
+        } else if (wave == 4 && lane < 16 * NT) {
+            // L_aa^{-1} of the 16x16 unit lower-triangular diagonal blocks, one
+            // column per lane, right-looking forward substitution
+            const int a = lane >> 4, jj = lane & 15;
+            const float* Nt = sNt + a * 256;  // Nt[m * 16 + i] = N[i][m]
+            float x[16], acc[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                x[m] = (m < jj) ? 0.f : (m == jj ? 1.f : -acc[m]);
+                if (m + 1 < 16) {
+                    float col[16];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(Nt + m * 16 + 4 * q4);
+                        col[4 * q4] = w[0];
+                        col[4 * q4 + 1] = w[1];
+                        col[4 * q4 + 2] = w[2];
+                        col[4 * q4 + 3] = w[3];
+                    }
+#pragma unroll
+                    for (int i = m + 1; i < 16; ++i) acc[i] += col[i] * x[m];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sT[(16 * a + i) * LCH + 16 * a + jj] = from_f32<T>(x[i]);
+            if (NT > 1) {
+                float xr[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xr[i] = x[i];
+                st_row<16>(sTt + (16 * a + jj) * LCH + 16 * a, xr);
             }
         }
         __syncthreads();
+
+        // ================= phase 4: off-diagonal blocks of L^{-1} ==============
 #pragma unroll
         for (int d = 1; d < NT; ++d) {
             if (wave < NT - d) {
@@ -507,7 +629,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 
         // ================= phase 5: Delta = L^{-1} R ==========================
 #pragma unroll
-        for (int m = 0; m < C::OPW; ++m) {
+        for (int m = 0; m < C::DPW; ++m) {
             const int ti = wave + C::NW * m;
             if (ti < C::NOT) {
                 const int ta = ti / NVT, vt = ti % NVT;
@@ -516,8 +638,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int kk = 0; kk < CH; kk += KS)
                     if (kk < kend)
-                        acc = E::mma(lds_frag<E>(sT, LCH, 16 * ta, kk, lane),
-                                     lds_frag<E>(sRt, LCH, 16 * vt, kk, lane), acc);
+                        acc = E::mma(lds_frag_lim<E>(sT, LCH, 16 * ta, kk, lane, CH),
+                                     lds_frag_lim<E>(sRt, LCH, 16 * vt, kk, lane, CH), acc);
                 T dv4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dv4[i] = from_f32<T>(acc[i]);
@@ -527,56 +649,91 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         }
         __syncthreads();
 
-        // ================= phase 6: outputs and state update ==================
-        if (!AUG) {
+        // ================= phase 6: state update  |  outputs ===================
+        if (lowg) {
+#pragma unroll
+            for (int m = 0; m < C::SPW; ++m) {
+                const int si = gw + 4 * m, ct = si / NVT;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[m][i] *= sEGC[16 * ct + 4 * g4 + i];
+            }
+#pragma unroll
+            for (int kk = 0; kk < CH; kk += KS) {
+#pragma unroll
+                for (int m = 0; m < C::SPW; ++m) {
+                    const int si = gw + 4 * m, ct = si / NVT, vt = si % NVT;
+                    S[m] = E::mma(lds_frag_lim<E>(sKt, LCH, 16 * ct, kk, lane, CH),
+                                  lds_frag_lim<E>(sDt, LCH, 16 * vt, kk, lane, CH), S[m]);
+                }
+            }
+        } else if (!AUG) {
+            // O = (Q e^G) S_old + P Delta, y = scale O sigmoid(z)
+            f32x4_t ao[C::OPW];
+#pragma unroll
+            for (int m = 0; m < C::OPW; ++m) ao[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            int ta0, vt0;
+            ro_tile<C>(gw, 0, ta0, vt0);
+#pragma unroll 2
+            for (int kk = 0; kk < DK; kk += KS) {
+                const typename E::Frag fa = lds_frag_scaled<E>(sQr, LDK, 16 * ta0, kk, lane, sES + ta0 * DK);
+#pragma unroll
+                for (int m = 0; m < C::OPW; ++m) {
+                    int ta, vt;
+                    ro_tile<C>(gw, m, ta, vt);
+                    if (vt < NVT) ao[m] = E::mma(fa, lds_frag<E>(sSt, LDK, 16 * vt, kk, lane), ao[m]);
+                }
+            }
+            T* ychunk = gy + ((t0 + cs) * H + h) * DV + vcol0 + r16;
+            const int kend = 16 * (ta0 + 1);
+#pragma unroll
+            for (int kk = 0; kk < CH; kk += KS) {
+                if (kk < kend) {
+                    const typename E::Frag fa = lds_frag_lim<E>(sP, LCH, 16 * ta0, kk, lane, CH);
+#pragma unroll
+                    for (int m = 0; m < C::OPW; ++m) {
+                        int ta, vt;
+                        ro_tile<C>(gw, m, ta, vt);
+                        if (vt < NVT) ao[m] = E::mma(fa, lds_frag_lim<E>(sDt, LCH, 16 * vt, kk, lane, CH), ao[m]);
+                    }
+                }
+            }
 #pragma unroll
             for (int m = 0; m < C::OPW; ++m) {
-                const int ti = wave + C::NW * m;
-                if (ti < C::NOT) {
-                    const int ta = ti / NVT, vt = ti % NVT;
-                    f32x4_t acc = O[m];
-                    const int kend = 16 * (ta + 1);
-#pragma unroll
-                    for (int kk = 0; kk < CH; kk += KS)
-                        if (kk < kend)
-                            acc = E::mma(lds_frag<E>(sP, LCH, 16 * ta, kk, lane),
-                                         lds_frag<E>(sDt, LCH, 16 * vt, kk, lane), acc);
+                int ta, vt;
+                ro_tile<C>(gw, m, ta, vt);
+                if (vt < NVT) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int64_t tt = cs + 16 * ta + 4 * g4 + i;
-                        if (tt < len) {
-                            float o = p.scale * acc[i];
-                            if (gz) o *= sigmoid(zreg[m][i]);
-                            gstore(gy + ((t0 + tt) * H + h) * (int64_t)DV + vcol0 + 16 * vt + r16, o);
+                        const int t = 16 * ta + 4 * g4 + i;
+                        if (t < nvalid) {
+                            float o = p.scale * ao[m][i];
+                            if (gated) o *= sigmoid(vz[m][i]);
+                            gstore(ychunk + t * HDV + 16 * vt, o);
                         }
                     }
                 }
             }
+            if (gated && ch + 1 < nchunks) load_vz(cs + CH);   // z of the next chunk
         }
+        __syncthreads();  // every read of the old S^T is done
+        if (lowg) {
 #pragma unroll
-        for (int m = 0; m < C::SPW; ++m) {
-            const int si = wave + C::NW * m, ct = si / NVT, vt = si % NVT;
-            f32x4_t acc;
+            for (int m = 0; m < C::SPW; ++m) {
+                const int si = gw + 4 * m, ct = si / NVT, vt = si % NVT;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = sEGC[16 * ct + 4 * g4 + i] * S[m][i];
-#pragma unroll
-            for (int kk = 0; kk < CH; kk += KS)
-                acc = E::mma(lds_frag<E>(sKt, LCH, 16 * ct, kk, lane),
-                             lds_frag<E>(sDt, LCH, 16 * vt, kk, lane), acc);
-            S[m] = acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sSt[(16 * vt + r16) * LDK + 16 * ct + 4 * g4 + i] = from_f32<T>(acc[i]);
+                for (int i = 0; i < 4; ++i)
+                    sSt[(16 * vt + r16) * LDK + 16 * ct + 4 * g4 + i] = from_f32<T>(S[m][i]);
+            }
         }
         __syncthreads();
     }
 
     // ---- final state ---------------------------------------------------------
-    if (p.sfin && n >= p.final_seq_lo) {
+    if (lowg && p.sfin && n >= p.final_seq_lo) {
         const int64_t sbase = ((int64_t)(n - p.final_seq_lo) * H + h) * DK * (int64_t)p.dvt;
 #pragma unroll
         for (int m = 0; m < C::SPW; ++m) {
-            const int si = wave + C::NW * m, ct = si / NVT, vt = si % NVT;
+            const int si = gw + 4 * m, ct = si / NVT, vt = si % NVT;
             const int col = cb + 16 * vt + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -594,7 +751,7 @@ static hipError_t launch_cfg(const PrefillArgs& a) {
     p.H = a.H;
     p.num_seqs = a.num_seqs;
     p.nchains = a.num_seqs * a.H;
-    p.dvt = a.aug ? a.dk + a.dv : a.dv;
+    p.dvt = C::AUG ? a.dk + a.dv : a.dv;
     p.nslices = p.dvt / C::VS;
     p.final_seq_lo = a.final_seq_lo;
     p.scale = a.scale;
@@ -617,23 +774,22 @@ static hipError_t launch_cfg(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
-// LDS bytes of a configuration, to keep only the slice widths that fit.
-template <class E, int DK, int VS, int CH>
-constexpr size_t pf_lds_bytes() {
-    using T = typename E::T;
-    constexpr size_t pe = 16 / sizeof(T), ldk = DK + pe, lch = CH + pe, nt = CH / 16;
-    constexpr size_t ng = 256 / (DK / 2);
-    constexpr size_t n0 = (size_t)CH * (CH + 4) * 4, n1 = (size_t)VS * lch * sizeof(T);
-    return (3 * CH * ldk + DK * lch + VS * ldk + 2 * CH * lch + VS * lch) * sizeof(T) +
-           (n0 > n1 ? n0 : n1) + (ng * DK + 2 * nt * DK + nt * nt * DK + DK + CH) * 4 + 16;
+template <class E, int DK, int CH, int MODE>
+static hipError_t launch_vs(const PrefillArgs& a, int vs) {
+    if constexpr (PfCfg<E, DK, 64, CH, MODE>::FITS) {
+        if (vs != 32) return launch_cfg<PfCfg<E, DK, 64, CH, MODE>>(a);
+    }
+    return launch_cfg<PfCfg<E, DK, 32, CH, MODE>>(a);
 }
 
-template <class E, int DK, int CH, bool AUG>
-static hipError_t launch_vs(const PrefillArgs& a, int vs) {
-    if constexpr (pf_lds_bytes<E, DK, 64, CH>() <= 160 * 1024) {
-        if (vs != 32) return launch_cfg<PfCfg<E, DK, 64, CH, AUG>>(a);
+template <class E, int DK, int CH>
+static hipError_t launch_mode(const PrefillArgs& a, int vs) {
+    switch (a.mode) {
+        case kModeSeq: return launch_vs<E, DK, CH, kModeSeq>(a, vs);
+        case kModeVarlen: return launch_vs<E, DK, CH, kModeVarlen>(a, vs);
+        case kModePairs: return launch_vs<E, DK, CH, kModePairs>(a, vs);
+        default: return launch_vs<E, DK, CH, kModeFinish>(a, vs);
     }
-    return launch_cfg<PfCfg<E, DK, 32, CH, AUG>>(a);
 }
 
 bool prefill_supported(int dtype, int dk, int dv, int chunk) {
@@ -646,25 +802,19 @@ bool prefill_supported(int dtype, int dk, int dv, int chunk) {
 hipError_t launch_prefill(const PrefillArgs& a) {
     int vs = a.vs;
     if (vs != 32 && vs != 64) {
-        // enough workgroups to cover the CUs, preferring wide slices
+        // wide slices (fewer repeats of the key-side work) unless that leaves
+        // most compute units without a workgroup
         const long chains = (long)a.num_seqs * a.H;
-        vs = (chains * (a.dv / 64) >= 256 || a.dv == 32) ? 64 : 32;
+        const long wide = chains * ((a.mode == 2 ? a.dk + a.dv : a.dv) / 64);
+        vs = wide >= 128 ? 64 : 32;
     }
     if (a.dtype == 0) {
-        if (a.dk == 128) {
-            if (a.chunk == 64)
-                return a.aug ? launch_vs<BF16, 128, 64, true>(a, vs) : launch_vs<BF16, 128, 64, false>(a, vs);
-            return a.aug ? launch_vs<BF16, 128, 16, true>(a, vs) : launch_vs<BF16, 128, 16, false>(a, vs);
-        }
-        if (a.chunk == 64)
-            return a.aug ? launch_vs<BF16, 64, 64, true>(a, vs) : launch_vs<BF16, 64, 64, false>(a, vs);
-        return a.aug ? launch_vs<BF16, 64, 16, true>(a, vs) : launch_vs<BF16, 64, 16, false>(a, vs);
+        if (a.dk == 128)
+            return a.chunk == 64 ? launch_mode<BF16, 128, 64>(a, vs) : launch_mode<BF16, 128, 16>(a, vs);
+        return a.chunk == 64 ? launch_mode<BF16, 64, 64>(a, vs) : launch_mode<BF16, 64, 16>(a, vs);
     }
-    if (a.dk == 128)
-        return a.aug ? launch_vs<F32, 128, 16, true>(a, vs) : launch_vs<F32, 128, 16, false>(a, vs);
-    if (a.chunk == 64)
-        return a.aug ? launch_vs<F32, 64, 64, true>(a, vs) : launch_vs<F32, 64, 64, false>(a, vs);
-    return a.aug ? launch_vs<F32, 64, 16, true>(a, vs) : launch_vs<F32, 64, 16, false>(a, vs);
+    if (a.dk == 128) return launch_mode<F32, 128, 16>(a, vs);
+    return a.chunk == 64 ? launch_mode<F32, 64, 64>(a, vs) : launch_mode<F32, 64, 16>(a, vs);
 }
 
 }  // namespace kda
