@@ -55,6 +55,24 @@ def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int, gated: bool) -> int
 
 
 # ------------------------------------------------------------------ helpers
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (calibrated against a plain copy), or None when the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if h.hexdigest() == rec["src_sha256"] else None
+
+
 def time_steps(fn, steps: int, warmup: int, torch):
     """Average ms per call of fn over `steps` calls, HIP events on the current stream."""
     for _ in range(warmup):
@@ -194,7 +212,8 @@ def bench_kcp(args, torch, kda, kda_inputs, dev):
 
 def bench_decode(args, torch, kda, kda_inputs, dev):
     w = kda_inputs.WORKLOADS[4]
-    N, H, dk, dv, P, steps = w["N"], w["H"], w["dk"], w["dv"], w["pool"], w["steps"]
+    N, H, dk, dv, P = w["N"], w["H"], w["dk"], w["dv"], w["pool"]
+    steps = args.decode_steps
     log(f"decode: N={N} H={H} pool={P} steps={steps}")
     gen = torch.Generator(device=dev).manual_seed(kda_inputs.workload_seed(4))
 
@@ -223,7 +242,8 @@ def bench_decode(args, torch, kda, kda_inputs, dev):
     nbytes = decode_bytes(N, H, dk, dv, 2, True)
     out = dict(ms_per_step=ms, steps=steps, tokens_per_s=N / (ms * 1e-3),
                bytes_per_step=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               traffic_per_step=counter_traffic("decode"))
     del state, pool, y
     torch.cuda.empty_cache()
     return out
@@ -238,6 +258,10 @@ def main() -> int:
                     help="comma list of extra workloads (%s), 'all' or 'none'" % ",".join(ALL_WORKLOADS))
     ap.add_argument("--cpu-sample-heads", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1000,
+                    help="decode steps timed as one loop (the workload runs 1000)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the KDA path here has no multi-GPU leg "
@@ -253,6 +277,13 @@ def main() -> int:
     kda.lib()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms, _ = time_steps(lambda: dst.copy_(src), 5, 1, torch)
+        print(json.dumps({"calibrate_copy_bytes": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}))
+        return 0
 
     inp, head, gpu_out = bench_headline(args, torch, kda, kda_inputs, dev)
     extras = ALL_WORKLOADS if args.workloads == "all" else tuple(
@@ -283,7 +314,8 @@ def main() -> int:
         "config": {"workload": "k3_layer_prefill", "B": 1, "H": 96, "T": 8192, "dk": 128,
                    "dv": 128, "chunk": 64, "gated": True, "state": "fp32"},
         "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS,
+                     "traffic": counter_traffic("prefill"),
                      "kernel": "prefill_kernel (kModeSeq, bf16, dk=dv=128, chunk 64)",
                      "bytes_per_launch": head["bytes"]},
         "mfma": {"achieved": head["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
