@@ -91,26 +91,11 @@ def time_steps(fn, steps: int, warmup: int, torch):
 
 
 def gpu_inputs(torch, lens, H, dk, dv, gated, s0_std, seed, dev):
-    """The synthetic recipe drawn directly on the GPU (same distributions as
-    kda_inputs; used for workloads too large to draw on the host quickly)."""
-    gen = torch.Generator(device=dev).manual_seed(seed)
-    T = int(sum(lens))
-
-    def unit(x):
-        return x / x.norm(dim=-1, keepdim=True)
-
-    q = unit(torch.randn(T, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
-    k = unit(torch.randn(T, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
-    v = torch.randn(T, H, dv, generator=gen, device=dev).to(torch.bfloat16)
-    z = torch.randn(T, H, dv, generator=gen, device=dev).to(torch.bfloat16) if gated else None
-    beta = torch.sigmoid(torch.randn(T, H, generator=gen, device=dev))
-    g = -5.0 * torch.sigmoid(torch.randn(T, H, dk, generator=gen, device=dev))
-    s0 = None
-    if s0_std > 0:
-        s0 = torch.randn(len(lens), H, dk, dv, generator=gen, device=dev) * s0_std
-    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
-    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
-    return dict(q=q, k=k, v=v, z=z, beta=beta, g=g, s0=s0, cu=cu.to(dev))
+    """The synthetic recipe drawn on the GPU (kda_inputs.draw_on_device)."""
+    import kda_inputs
+    inp = kda_inputs.draw_on_device(lens, H, dk, dv, gated, s0_std, seed, dev)
+    return dict(q=inp.q, k=inp.k, v=inp.v, z=inp.z, beta=inp.beta, g=inp.g, s0=inp.S0,
+                cu=inp.cu_seqlens.to(dev))
 
 
 # ------------------------------------------------------------------ workloads
@@ -164,8 +149,7 @@ def bench_cpu_baseline(args, inp, gpu_out, torch):
 
 def bench_varlen(args, torch, kda, kda_inputs, dev):
     w = kda_inputs.WORKLOADS[2]
-    gen = torch.Generator().manual_seed(kda_inputs.workload_seed(2))
-    lens = torch.randint(w["lmin"], w["lmax"] + 1, (w["nseq"],), generator=gen).tolist()
+    lens = kda_inputs.varlen_lengths()
     H, dk, dv = w["H"], w["dk"], w["dv"]
     log(f"varlen_prefill: {len(lens)} sequences, {sum(lens)} tokens")
     d = gpu_inputs(torch, lens, H, dk, dv, True, w["s0_std"], kda_inputs.workload_seed(2), dev)

@@ -185,3 +185,38 @@ def make_decode_workload(stress: Optional[str] = None, **override) -> DecodeInpu
     seed = override.get("seed", workload_seed(4, stress))
     return make_decode(w["N"], w["H"], w["dk"], w["dv"], w["dtype"], w["gated"], w["s0_std"],
                        w["pool"], seed, g_shift, beta_shift)
+
+
+def draw_on_device(lens: List[int], H: int, dk: int, dv: int, gated: bool, s0_std: float,
+                   seed: int, device, g_shift: float = 0.0, beta_shift: float = 0.0) -> KDAInputs:
+    """The same recipe (distributions, draw order) drawn by a torch generator on
+    `device`, for workloads too large to draw on the host quickly.  bf16 storage.
+    Not bit-identical to make_prefill (different generator); tests copy the
+    sampled chains back to the host for the oracle."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    T = int(sum(lens))
+    dt = torch.bfloat16
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    q = unit(torch.randn(T, H, dk, generator=gen, device=device)).to(dt)
+    k = unit(torch.randn(T, H, dk, generator=gen, device=device)).to(dt)
+    v = torch.randn(T, H, dv, generator=gen, device=device).to(dt)
+    z = torch.randn(T, H, dv, generator=gen, device=device).to(dt) if gated else None
+    beta = torch.sigmoid(torch.randn(T, H, generator=gen, device=device) - beta_shift)
+    g = G_MIN * torch.sigmoid(torch.randn(T, H, dk, generator=gen, device=device) - g_shift)
+    S0 = None
+    if s0_std > 0:
+        S0 = torch.randn(len(lens), H, dk, dv, generator=gen, device=device) * s0_std
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    if lens:
+        cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    return KDAInputs(q, k, v, z, g, beta, cu, S0, H, dk, dv, "bf16")
+
+
+def varlen_lengths(seed: Optional[int] = None) -> List[int]:
+    """The varlen workload's sequence lengths (first draw of its generator)."""
+    w = WORKLOADS[2]
+    gen = torch.Generator().manual_seed(workload_seed(2) if seed is None else seed)
+    return torch.randint(w["lmin"], w["lmax"] + 1, (w["nseq"],), generator=gen).tolist()
