@@ -8,6 +8,7 @@ namespace kda {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -74,11 +75,12 @@ __device__ __forceinline__ typename E::Frag lds_frag(const typename E::T* base, 
 
 // Fragment of a reduction shorter than one MFMA (klim < KSTEP, klim a
 // multiple of KPL): lanes whose k range starts at or past klim supply zeros.
-template <typename E>
+template <typename E, int KLIM>
 __device__ __forceinline__ typename E::Frag lds_frag_lim(const typename E::T* base, int ld, int r0,
-                                                         int k0, int lane, int klim) {
+                                                         int k0, int lane) {
+    if constexpr (KLIM % E::KSTEP == 0) return lds_frag<E>(base, ld, r0, k0, lane);
     typename E::Frag f;
-    if (k0 + E::KPL * (lane >> 4) < klim) {
+    if (k0 + E::KPL * (lane >> 4) < KLIM) {
         f = lds_frag<E>(base, ld, r0, k0, lane);
     } else {
 #pragma unroll

@@ -74,9 +74,12 @@ struct PfCfg {
     static constexpr int NW = 8, NTHR = 64 * NW;
     // Waves 0-3 own the state and the R tiles; waves 4-7 own the output tiles
     // and the diagonal inverses.
-    static constexpr int NG = NTHR / (DK / 2);  // token groups of the decay phase
-    static constexpr int L = CH / NG;           // tokens per thread in that phase
-    static constexpr int GPT = 16 / L;          // token groups per 16-token tile
+    // decay phase: each thread holds TPT tokens x CPT channels; a wave holds
+    // GPTW token groups x CGW channel groups of one 16-token tile
+    static constexpr int CPT = (CH == 16 && DK == 64) ? 2 : 4;
+    static constexpr int CGW = DK * NT / (8 * CPT);
+    static constexpr int GPTW = 64 / CGW;
+    static constexpr int TPT = 16 / GPTW;
     static constexpr int NOT = NT * NVT;        // (t, v) tiles of R, Delta and O
     static constexpr int OPW = (NOT + 3) / 4;   // R / O tiles per wave of a 4-wave group
     static constexpr int DPW = (NOT + NW - 1) / NW;  // Delta tiles per wave
@@ -85,8 +88,8 @@ struct PfCfg {
     static constexpr int NPAIR = NT * (NT + 1) / 2;
     static constexpr int NTASK = AUG ? NPAIR : 2 * NPAIR;
     static_assert(NT == 1 || NT == 4, "chunk of 16 or 64 tokens");
-    static_assert(L >= 1 && 16 % L == 0, "decay-phase token groups must tile 16");
-    static_assert(NST % 4 == 0, "state tiles per wave");
+    static_assert(GPTW * CGW == 64 && TPT * GPTW == 16 && TPT >= 1, "decay-phase mapping");
+    static_assert(NST % 4 == 0 && 4 % NVT == 0, "state tiles per wave share one value tile");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t SZ_OP = (size_t)CH * LDK * sizeof(T);
@@ -101,8 +104,8 @@ struct PfCfg {
     static constexpr size_t O_T = O_NT + (size_t)NT * 16 * 16 * 4;
     static constexpr size_t O_P = O_T + al((size_t)CH * LCH * sizeof(T));
     static constexpr size_t O_RT = O_P + al((size_t)CH * LCH * sizeof(T));
-    static constexpr size_t O_GS = O_RT + al((size_t)VS * LCH * sizeof(T));
-    static constexpr size_t O_ES = O_GS + (size_t)NG * DK * 4;
+    static constexpr size_t O_TP = O_RT + al((size_t)VS * LCH * sizeof(T));
+    static constexpr size_t O_ES = O_TP + (size_t)NT * DK * 4;
     static constexpr size_t O_D = O_ES + (size_t)NT * DK * 4;
     static constexpr size_t O_EGC = O_D + (size_t)NT * NT * DK * 4;
     static constexpr size_t O_BETA = O_EGC + (size_t)DK * 4;
@@ -110,18 +113,41 @@ struct PfCfg {
     static constexpr size_t BYTES = O_MISC + 16;
     // aliases of regions that are dead while they are used
     static constexpr size_t O_TT = O_KC;   // L^{-1} transposed, during the inverse only
-    static constexpr size_t O_YT = O_GS;   // per-wave 16x16 scratch of the inverse
+    static constexpr size_t O_YT = O_KR;   // per-wave 16x16 scratch of the inverse
     static constexpr size_t O_DT = O_N;    // Delta^T, after the inverse
     static constexpr size_t O_SORT = O_KR; // sequence lengths, before the first chunk
     static constexpr bool FITS = BYTES <= 160 * 1024 &&
         (size_t)CH * LCH * sizeof(T) <= SZ_OP &&
-        (NT == 1 || (size_t)3 * 16 * (16 + PADE) * sizeof(T) <= (size_t)NG * DK * 4);
+        (NT == 1 || (size_t)3 * 16 * (16 + PADE) * sizeof(T) <= SZ_OP);
 };
 
 // Pairs of consecutive channels of q / k as loaded from global memory.
 template <typename T> struct Pair2;
 template <> struct Pair2<__bf16> { using type = bf16x2_t; };
 template <> struct Pair2<float> { using type = f32x2_t; };
+
+template <typename T, int n> struct VecT;
+template <> struct VecT<__bf16, 2> { using type = bf16x2_t; };
+template <> struct VecT<__bf16, 4> { using type = bf16x4_t; };
+template <> struct VecT<float, 2> { using type = f32x2_t; };
+template <> struct VecT<float, 4> { using type = f32x4_t; };
+template <int n> using f32xn = typename VecT<float, n>::type;
+
+// four consecutive elements as fp32 (8-byte aligned for bf16, 16 for fp32)
+__device__ __forceinline__ f32x4_t gload4(const __bf16* p) {
+    const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
+    return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4_t gload4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+__device__ __forceinline__ void gstore4(__bf16* p, f32x4_t v) {
+    *reinterpret_cast<bf16x4_t*>(p) = bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+__device__ __forceinline__ void gstore4(float* p, f32x4_t v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+
+__device__ __forceinline__ void st_vec4(bf16x4_t& d, const float* v) {
+    d = bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+__device__ __forceinline__ void st_vec4(f32x4_t& d, const float* v) { d = f32x4_t{v[0], v[1], v[2], v[3]}; }
 
 __device__ __forceinline__ void st_pair(__bf16* p, float a, float b) {
     *reinterpret_cast<bf16x2_t*>(p) = bf16x2_t{(__bf16)a, (__bf16)b};
@@ -133,7 +159,11 @@ __device__ __forceinline__ void st_pair(float* p, float a, float b) {
 // n consecutive elements (n*sizeof(T) a multiple of 4, 4-byte aligned).
 template <int n>
 __device__ __forceinline__ void st_row(__bf16* p, const float* v) {
-    if constexpr (n % 8 == 0) {
+    if constexpr (n == 4) {
+        *reinterpret_cast<bf16x4_t*>(p) = bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    } else if constexpr (n == 2) {
+        *reinterpret_cast<bf16x2_t*>(p) = bf16x2_t{(__bf16)v[0], (__bf16)v[1]};
+    } else if constexpr (n % 8 == 0) {
 #pragma unroll
         for (int i = 0; i < n; i += 8) {
             bf16x8_t w;
@@ -148,8 +178,14 @@ __device__ __forceinline__ void st_row(__bf16* p, const float* v) {
 }
 template <int n>
 __device__ __forceinline__ void st_row(float* p, const float* v) {
+    if constexpr (n % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < n; ++i) p[i] = v[i];
+        for (int i = 0; i < n; i += 4)
+            *reinterpret_cast<f32x4_t*>(p + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < n; ++i) p[i] = v[i];
+    }
 }
 
 // 16x16x16 product acc += A B^T over a 16-deep reduction, operands in LDS:
@@ -221,12 +257,12 @@ __device__ __forceinline__ void ro_tile(int gw, int m, int& ta, int& vt) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
     using E = typename C::E;
     using T = typename C::T;
     using T2 = typename Pair2<T>::type;
     constexpr int DK = C::DK, VS = C::VS, CH = C::CH, NT = C::NT, NVT = C::NVT;
-    constexpr int LDK = C::LDK, LCH = C::LCH, LN = C::LN, L = C::L, GPT = C::GPT, NG = C::NG;
+    constexpr int LDK = C::LDK, LCH = C::LCH, LN = C::LN;
     constexpr int KS = E::KSTEP, NTHR = C::NTHR;
     constexpr bool AUG = C::AUG;
     static_assert(C::FITS, "LDS budget of a gfx950 workgroup (160 KiB)");
@@ -245,7 +281,7 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
     T* sYt = reinterpret_cast<T*>(smem + C::O_YT);
     T* sP = reinterpret_cast<T*>(smem + C::O_P);
     T* sRt = reinterpret_cast<T*>(smem + C::O_RT);
-    float* sGs = reinterpret_cast<float*>(smem + C::O_GS);
+    float* sTP = reinterpret_cast<float*>(smem + C::O_TP);
     float* sES = reinterpret_cast<float*>(smem + C::O_ES);
     float* sD = reinterpret_cast<float*>(smem + C::O_D);
     float* sEGC = reinterpret_cast<float*>(smem + C::O_EGC);
@@ -337,18 +373,45 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
         }
     }
 
-    // ---- decay-phase thread mapping: channel pair cp, token group tg --------
-    const int cp = tid % (DK / 2), tg = tid / (DK / 2);
-    const int c0 = 2 * cp;
-    const int tile = tg / GPT, gi = tg % GPT;
+    // ---- decay-phase thread mapping ------------------------------------------
+    // Wave w covers 16-token tile dtile = w / (8 / NT) and a block of CPW
+    // channels; lane = (token group tgrp, channel group cg) holds TPT
+    // consecutive tokens x CPT consecutive channels, so q, k and g arrive in
+    // CPT-wide vector loads and a tile's token groups sit in one wave.
+    constexpr int CPT = C::CPT, TPT = C::TPT, CGW = C::CGW, GPTW = C::GPTW;
+    const int dtile = wave / (8 / NT);
+    const int tgrp = lane / CGW, cg = lane % CGW;
+    const int c0 = (wave % (8 / NT)) * (DK * NT / 8) + CPT * cg;   // first channel
+    const int tl0 = 16 * dtile + TPT * tgrp;                        // first token (in chunk)
 
-    T2 rq[L], rk[L];
-    f32x2_t rgv[L];
+    using TV = typename VecT<T, CPT>::type;
+    TV rq[TPT], rk[TPT];
+    f32xn<CPT> rgv[TPT];
     float rbeta = 0.f;
-    // v (waves 0-3, R tiles) or z (waves 4-7, output tiles) in MMA-output layout
-    float vz[C::OPW][4];
-    const int64_t tclamp = len > 0 ? len - 1 : 0;
+    // v (waves 0-3, R tiles) or z (waves 4-7, output tiles): 4 consecutive
+    // value columns of one token per tile, the transposed MMA-output layout
     const int HDK = H * DK, HDV = H * DV;   // token strides (elements)
+    // Kept as raw storage vectors: converting at load time would make the wave
+    // wait for the prefetch right away.  vz_n is in flight for the next chunk,
+    // vz the current chunk's copy.
+    using TV4 = typename VecT<T, 4>::type;
+    TV4 vz[C::OPW], vz_n[C::OPW];
+    // outputs of the previous chunk, stored in the middle of the next one so
+    // that no wait for prefetched data also waits for these stores
+    TV4 yd[C::OPW];
+    T* yd_base = nullptr;
+    int yd_nvalid = 0;
+    auto store_y = [&]() {
+#pragma unroll
+        for (int m = 0; m < C::OPW; ++m) {
+            int ta, vt;
+            ro_tile<C>(gw, m, ta, vt);
+            const int t = 16 * ta + r16;
+            if (vt < NVT && t < yd_nvalid)
+                *reinterpret_cast<TV4*>(yd_base + t * HDV + 16 * vt) = yd[m];
+        }
+    };
+    const int64_t tclamp = len > 0 ? len - 1 : 0;
     // Global addresses: a 64-bit row base per chunk plus 32-bit in-chunk offsets.
     // Loads are unconditional from clamped rows; invalid tokens are masked at use.
     auto load_qkg = [&](int64_t cs) {
@@ -358,11 +421,11 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
         const T* qb = gq + row * DK + c0;
         const float* gb = p.g + row * DK + c0;
 #pragma unroll
-        for (int l = 0; l < L; ++l) {
-            const int tr = tg * L + l < last ? tg * L + l : last;
-            rk[l] = *reinterpret_cast<const T2*>(kb + tr * HDK);
-            if (!AUG) rq[l] = *reinterpret_cast<const T2*>(qb + tr * HDK);
-            rgv[l] = *reinterpret_cast<const f32x2_t*>(gb + tr * HDK);
+        for (int l = 0; l < TPT; ++l) {
+            const int tr = tl0 + l < last ? tl0 + l : last;
+            rk[l] = *reinterpret_cast<const TV*>(kb + tr * HDK);
+            if (!AUG) rq[l] = *reinterpret_cast<const TV*>(qb + tr * HDK);
+            rgv[l] = *reinterpret_cast<const f32xn<CPT>*>(gb + tr * HDK);
         }
         if (tid < CH) {
             const int tr = tid < last ? tid : last;
@@ -373,18 +436,15 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
         if (lowg || gated) {
             const int64_t row = (t0 + cs) * H + h;
             const int last = (int)(tclamp - cs);
-            const T* src = (lowg ? gv : gz) + row * DV + vcol0 + r16;
+            const T* src = (lowg ? gv : gz) + row * DV + vcol0 + 4 * g4;
 #pragma unroll
             for (int m = 0; m < C::OPW; ++m) {
                 int ta, vt;
                 ro_tile<C>(gw, m, ta, vt);
                 const int vtc = vt < NVT ? vt : 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * ta + 4 * g4 + i;
-                    const int tr = t < last ? t : last;
-                    vz[m][i] = gload(src + tr * HDV + 16 * vtc);
-                }
+                const int t = 16 * ta + r16;
+                const int tr = t < last ? t : last;
+                vz_n[m] = *reinterpret_cast<const TV4*>(src + tr * HDV + 16 * vtc);
             }
         }
     };
@@ -399,88 +459,111 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t cs = ch * CH;
         const int nvalid = len - cs < CH ? (int)(len - cs) : CH;
+        // everything prefetched for this chunk is waited for here, once
+#pragma unroll
+        for (int m = 0; m < C::OPW; ++m) vz[m] = vz_n[m];
         // ================= phase 1: decay prefix and scaled operands ==========
-        // Thread (tg, cp) holds tokens tg*L .. tg*L+L-1 of channels c0, c0+1.
-        float cpv[2][L], sfv[2][L];
-        float gsum2[2];
+        // Running products of alpha = e^g inside the thread's tokens, then a
+        // multiplicative scan over the tile's token groups (lanes CGW apart);
+        // tile products go through LDS for the chunk-level references.
+        float cpv[CPT][TPT], sfv[CPT][TPT], ex[CPT], gp[CPT];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            float al[L], pr = 1.f, gs = 0.f;
+        for (int e = 0; e < CPT; ++e) {
+            float al[TPT], pr = 1.f;
 #pragma unroll
-            for (int l = 0; l < L; ++l) {
-                const bool valid = tg * L + l < nvalid;
-                const float gv_ = valid ? rgv[l][e] : 0.f;
-                al[l] = fast_exp(gv_);
+            for (int l = 0; l < TPT; ++l) {
+                al[l] = tl0 + l < nvalid ? fast_exp(rgv[l][e]) : 1.f;
                 pr *= al[l];
-                cpv[e][l] = pr;          // e^{G_t - G_first + g_first}
-                gs += gv_;
+                cpv[e][l] = pr;           // e^{G_t - G_before_group}
             }
-            sfv[e][L - 1] = 1.f;
+            sfv[e][TPT - 1] = 1.f;
 #pragma unroll
-            for (int l = L - 2; l >= 0; --l) sfv[e][l] = sfv[e][l + 1] * al[l + 1];
-            gsum2[e] = gs;
+            for (int l = TPT - 2; l >= 0; --l) sfv[e][l] = sfv[e][l + 1] * al[l + 1];
+            gp[e] = pr;                   // group product
+            float inc = pr;               // inclusive product scan over token groups
+#pragma unroll
+            for (int st = 1; st < GPTW; st *= 2) {
+                const float o = __shfl_up(inc, st * CGW);
+                if (tgrp >= st) inc *= o;
+            }
+            ex[e] = inc * __builtin_amdgcn_rcpf(pr);   // exclusive: e^{G_before_group - R_a} (>= e^-80)
+            if (tgrp == GPTW - 1) sTP[dtile * DK + c0 + e] = inc;   // tile product
         }
-        st_pair(sGs + tg * DK + c0, gsum2[0], gsum2[1]);
         if (tid < CH) sBeta[tid] = tid < nvalid ? rbeta : 0.f;
         __syncthreads();
         {
-            float E1[2], E2[2], E3[2];
+            float eGCmR[CPT];   // e^{G_C - R_a}
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int c = c0 + e;
-                float gsum[NG];
+            for (int e = 0; e < CPT; ++e) {
+                float tp[NT];
 #pragma unroll
-                for (int q2 = 0; q2 < NG; ++q2) gsum[q2] = sGs[q2 * DK + c];
-                float Sref[NT + 1];
-                Sref[0] = 0.f;
+                for (int a = 0; a < NT; ++a) tp[a] = sTP[a * DK + c0 + e];
+                float suf = 1.f;
 #pragma unroll
-                for (int a = 0; a < NT; ++a) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int q2 = 0; q2 < GPT; ++q2) s += gsum[a * GPT + q2];
-                    Sref[a + 1] = Sref[a] + s;
+                for (int a = NT - 1; a >= 0; --a) {
+                    suf *= tp[a];
+                    if (a == dtile) eGCmR[e] = suf;
                 }
-                float off = 0.f;
-#pragma unroll
-                for (int q2 = 0; q2 < NG; ++q2)
-                    if (q2 >= tile * GPT && q2 < tg) off += gsum[q2];
-                const float Sa = Sref[tile], GC = Sref[NT];
-                E1[e] = fast_exp(off);                        // times cpv: e^{G_t - R_a}  (<= 1)
-                E2[e] = fast_exp(-off - gsum2[e]);            // times sfv: e^{R_a - G_t}  (<= e^80)
-                E3[e] = fast_exp(GC - Sa - off - gsum2[e]);   // times sfv: e^{G_C - G_t}  (<= 1)
-                if (tg == 0) {
+                if (tgrp == 0) {
                     // per-channel tables: e^{R_a}, e^{R_a - R_b} (b < a), e^{G_C}
+                    float pre = 1.f;
 #pragma unroll
                     for (int a = 0; a < NT; ++a) {
-                        sES[a * DK + c] = fast_exp(Sref[a]);
+                        if (a == dtile) {
+                            sES[a * DK + c0 + e] = pre;
+                            float dab = 1.f;
 #pragma unroll
-                        for (int bb = 0; bb < a; ++bb)
-                            sD[(a * NT + bb) * DK + c] = fast_exp(Sref[a] - Sref[bb]);
+                            for (int bb = a - 1; bb >= 0; --bb) {
+                                dab *= tp[bb];
+                                sD[(a * NT + bb) * DK + c0 + e] = dab;
+                            }
+                        }
+                        pre *= tp[a];
                     }
-                    sEGC[c] = fast_exp(GC);
+                    if (dtile == 0) sEGC[c0 + e] = pre;
                 }
             }
-            float kt0[L], kt1[L];
+            float kt[CPT][TPT], inv[CPT], g3[CPT];
 #pragma unroll
-            for (int l = 0; l < L; ++l) {
-                const int t = tg * L + l;
-                const bool valid = t < nvalid;
-                const float k0 = valid ? to_f32(rk[l][0]) : 0.f, k1 = valid ? to_f32(rk[l][1]) : 0.f;
-                const float f10 = E1[0] * cpv[0][l], f11 = E1[1] * cpv[1][l];
-                st_pair(sKr + t * LDK + c0, k0 * f10, k1 * f11);
-                if (!AUG) {
-                    const float q0 = valid ? to_f32(rq[l][0]) : 0.f, q1 = valid ? to_f32(rq[l][1]) : 0.f;
-                    st_pair(sQr + t * LDK + c0, q0 * f10, q1 * f11);
-                }
-                st_pair(sKc + t * LDK + c0, k0 * (E2[0] * sfv[0][l]), k1 * (E2[1] * sfv[1][l]));
-                kt0[l] = k0 * (E3[0] * sfv[0][l]);
-                kt1[l] = k1 * (E3[1] * sfv[1][l]);
+            for (int e = 0; e < CPT; ++e) {
+                inv[e] = __builtin_amdgcn_rcpf(ex[e] * gp[e]);   // e^{R_a - G_last}
+                g3[e] = eGCmR[e] * inv[e];                       // e^{G_C - G_last}
             }
-            st_row<L>(sKt + c0 * LCH + tg * L, kt0);
-            st_row<L>(sKt + (c0 + 1) * LCH + tg * L, kt1);
+            const bool full = nvalid == CH;
+#pragma unroll
+            for (int l = 0; l < TPT; ++l) {
+                const int t = tl0 + l;
+                const bool valid = full || t < nvalid;
+                float f1[CPT], f2[CPT], kv[CPT], qv[CPT];
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) {
+                    kv[e] = valid ? to_f32(rk[l][e]) : 0.f;
+                    qv[e] = (valid && !AUG) ? to_f32(rq[l][e]) : 0.f;
+                    f1[e] = ex[e] * cpv[e][l];        // e^{G_t - R_a}  (<= 1)
+                    f2[e] = inv[e] * sfv[e][l];       // e^{R_a - G_t}  (<= e^80)
+                    kt[e][l] = kv[e] * (g3[e] * sfv[e][l]);   // k e^{G_C - G_t}
+                }
+                float o[CPT];
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) o[e] = kv[e] * f1[e];
+                st_row<CPT>(sKr + t * LDK + c0, o);
+                if (!AUG) {
+#pragma unroll
+                    for (int e = 0; e < CPT; ++e) o[e] = qv[e] * f1[e];
+                    st_row<CPT>(sQr + t * LDK + c0, o);
+                }
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) o[e] = kv[e] * f2[e];
+                st_row<CPT>(sKc + t * LDK + c0, o);
+            }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) st_row<TPT>(sKt + (c0 + e) * LCH + tl0, kt[e]);
         }
         // prefetch the next chunk's q, k, g, beta while this one computes
-        if (ch + 1 < nchunks) load_qkg(cs + CH);
+        if (ch + 1 < nchunks) {
+            load_qkg(cs + CH);
+            load_vz(cs + CH);
+        }
         __syncthreads();
 
         // ================= phase 2: gated Gram blocks A and P ===================
@@ -493,15 +576,24 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
             while ((a + 1) * (a + 2) / 2 <= pi) ++a;
             const int bb = pi - a * (a + 1) / 2;
             const T* X = mat ? sQr : sKr;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int kk = 0; kk < DK; kk += KS) {
-                const typename E::Frag fa = lds_frag<E>(X, LDK, 16 * a, kk, lane);
-                const typename E::Frag fb = (bb < a)
-                    ? lds_frag_scaled<E>(sKc, LDK, 16 * bb, kk, lane, sD + (a * NT + bb) * DK)
-                    : lds_frag<E>(sKc, LDK, 16 * bb, kk, lane);
-                acc = E::mma(fa, fb, acc);
+            constexpr int NK = DK / KS;
+            typename E::Frag fa[NK], fb[NK];
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                fa[q] = lds_frag<E>(X, LDK, 16 * a, q * KS, lane);
+                fb[q] = (bb < a)
+                    ? lds_frag_scaled<E>(sKc, LDK, 16 * bb, q * KS, lane, sD + (a * NT + bb) * DK)
+                    : lds_frag<E>(sKc, LDK, 16 * bb, q * KS, lane);
             }
+            __builtin_amdgcn_sched_barrier(0);   // all reads of the block before its MFMAs
+            // two independent accumulation chains, summed at the end
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NK; q += 2) {
+                acc = E::mma(fa[q], fb[q], acc);
+                if (q + 1 < NK) acc1 = E::mma(fa[q + 1], fb[q + 1], acc1);
+            }
+            acc += acc1;
             const int j = 16 * bb + r16;
             if (mat == 0) {
                 if (bb == a) {
@@ -537,14 +629,24 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
             for (int m = 0; m < C::OPW; ++m) ak[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             int ta0, vt0;
             ro_tile<C>(gw, 0, ta0, vt0);
-#pragma unroll 2
+            // transposed products: lane (r16, g4) of tile (ta, vt) holds token
+            // 16 ta + r16 and value columns 16 vt + 4 g4 + i
+#pragma unroll
             for (int kk = 0; kk < DK; kk += KS) {
-                const typename E::Frag fa = lds_frag_scaled<E>(sKr, LDK, 16 * ta0, kk, lane, sES + ta0 * DK);
+                const typename E::Frag fb = lds_frag_scaled<E>(sKr, LDK, 16 * ta0, kk, lane, sES + ta0 * DK);
+                typename E::Frag fa[C::OPW];
 #pragma unroll
                 for (int m = 0; m < C::OPW; ++m) {
                     int ta, vt;
                     ro_tile<C>(gw, m, ta, vt);
-                    if (vt < NVT) ak[m] = E::mma(fa, lds_frag<E>(sSt, LDK, 16 * vt, kk, lane), ak[m]);
+                    fa[m] = lds_frag<E>(sSt, LDK, 16 * (vt < NVT ? vt : 0), kk, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < C::OPW; ++m) {
+                    int ta, vt;
+                    ro_tile<C>(gw, m, ta, vt);
+                    if (vt < NVT) ak[m] = E::mma(fa[m], fb, ak[m]);
                 }
             }
 #pragma unroll
@@ -552,19 +654,17 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
                 int ta, vt;
                 ro_tile<C>(gw, m, ta, vt);
                 if (vt < NVT) {
-                    T rv[4];
+                    const int t = 16 * ta + r16;
+                    const float bt = sBeta[t];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * ta + 4 * g4 + i;
-                        const float vv = ident ? 0.f : vz[m][i];
-                        rv[i] = from_f32<T>(sBeta[t] * (vv - ak[m][i]));
+                        const float vv = ident ? 0.f : to_f32(vz[m][i]);
+                        sRt[(16 * vt + 4 * g4 + i) * LCH + t] = from_f32<T>(bt * (vv - ak[m][i]));
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sRt[(16 * vt + r16) * LCH + 16 * ta + 4 * g4 + i] = rv[i];
                 }
             }
-            if (ch + 1 < nchunks) load_vz(cs + CH);   // v of the next chunk
-        } else if (wave == 4 && lane < 16 * NT) {
+        }
+        if (wave == 4 && lane < 16 * NT) {
             // L_aa^{-1} of the 16x16 unit lower-triangular diagonal blocks, one
             // column per lane, right-looking forward substitution
             const int a = lane >> 4, jj = lane & 15;
@@ -598,6 +698,7 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
                 st_row<16>(sTt + (16 * a + jj) * LCH + 16 * a, xr);
             }
         }
+        if (!lowg && !AUG && yd_base) store_y();   // outputs of the previous chunk
         __syncthreads();
 
         // ================= phase 4: off-diagonal blocks of L^{-1} ==============
@@ -633,13 +734,19 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
             const int ti = wave + C::NW * m;
             if (ti < C::NOT) {
                 const int ta = ti / NVT, vt = ti % NVT;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                constexpr int NK = (CH + KS - 1) / KS;
                 const int kend = 16 * (ta + 1);
+                typename E::Frag fa[NK], fb[NK];
 #pragma unroll
-                for (int kk = 0; kk < CH; kk += KS)
-                    if (kk < kend)
-                        acc = E::mma(lds_frag_lim<E>(sT, LCH, 16 * ta, kk, lane, CH),
-                                     lds_frag_lim<E>(sRt, LCH, 16 * vt, kk, lane, CH), acc);
+                for (int q = 0; q < NK; ++q) {
+                    fa[q] = lds_frag_lim<E, CH>(sT, LCH, 16 * ta, q * KS, lane);
+                    fb[q] = lds_frag_lim<E, CH>(sRt, LCH, 16 * vt, q * KS, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < NK; ++q)
+                    if (q * KS < kend) acc = E::mma(fa[q], fb[q], acc);
                 T dv4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dv4[i] = from_f32<T>(acc[i]);
@@ -651,69 +758,91 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
 
         // ================= phase 6: state update  |  outputs ===================
         if (lowg) {
+            {
+                f32x4_t eg[C::SPW];
 #pragma unroll
-            for (int m = 0; m < C::SPW; ++m) {
-                const int si = gw + 4 * m, ct = si / NVT;
+                for (int m = 0; m < C::SPW; ++m) {
+                    const int ct = (gw + 4 * m) / NVT;
+                    eg[m] = *reinterpret_cast<const f32x4_t*>(sEGC + 16 * ct + 4 * g4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[m][i] *= sEGC[16 * ct + 4 * g4 + i];
+                for (int m = 0; m < C::SPW; ++m) S[m] *= eg[m];
             }
 #pragma unroll
             for (int kk = 0; kk < CH; kk += KS) {
+                // all fragments of the k step first, then the MFMAs; every state
+                // tile of the wave has value tile gw % NVT (NVT divides 4)
+                typename E::Frag fa[C::SPW];
+                const typename E::Frag fb = lds_frag_lim<E, CH>(sDt, LCH, 16 * (gw % NVT), kk, lane);
 #pragma unroll
                 for (int m = 0; m < C::SPW; ++m) {
-                    const int si = gw + 4 * m, ct = si / NVT, vt = si % NVT;
-                    S[m] = E::mma(lds_frag_lim<E>(sKt, LCH, 16 * ct, kk, lane, CH),
-                                  lds_frag_lim<E>(sDt, LCH, 16 * vt, kk, lane, CH), S[m]);
+                    const int ct = (gw + 4 * m) / NVT;
+                    fa[m] = lds_frag_lim<E, CH>(sKt, LCH, 16 * ct, kk, lane);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < C::SPW; ++m) S[m] = E::mma(fa[m], fb, S[m]);
             }
         } else if (!AUG) {
-            // O = (Q e^G) S_old + P Delta, y = scale O sigmoid(z)
+            // O = (Q e^G) S_old + P Delta, y = scale O sigmoid(z); transposed
+            // products as for R: lane holds token 16 ta + r16, columns 16 vt + 4 g4 + i
             f32x4_t ao[C::OPW];
 #pragma unroll
             for (int m = 0; m < C::OPW; ++m) ao[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             int ta0, vt0;
             ro_tile<C>(gw, 0, ta0, vt0);
-#pragma unroll 2
+#pragma unroll
             for (int kk = 0; kk < DK; kk += KS) {
-                const typename E::Frag fa = lds_frag_scaled<E>(sQr, LDK, 16 * ta0, kk, lane, sES + ta0 * DK);
+                const typename E::Frag fb = lds_frag_scaled<E>(sQr, LDK, 16 * ta0, kk, lane, sES + ta0 * DK);
+                typename E::Frag fa[C::OPW];
 #pragma unroll
                 for (int m = 0; m < C::OPW; ++m) {
                     int ta, vt;
                     ro_tile<C>(gw, m, ta, vt);
-                    if (vt < NVT) ao[m] = E::mma(fa, lds_frag<E>(sSt, LDK, 16 * vt, kk, lane), ao[m]);
+                    fa[m] = lds_frag<E>(sSt, LDK, 16 * (vt < NVT ? vt : 0), kk, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < C::OPW; ++m) {
+                    int ta, vt;
+                    ro_tile<C>(gw, m, ta, vt);
+                    if (vt < NVT) ao[m] = E::mma(fa[m], fb, ao[m]);
                 }
             }
-            T* ychunk = gy + ((t0 + cs) * H + h) * DV + vcol0 + r16;
             const int kend = 16 * (ta0 + 1);
 #pragma unroll
             for (int kk = 0; kk < CH; kk += KS) {
                 if (kk < kend) {
-                    const typename E::Frag fa = lds_frag_lim<E>(sP, LCH, 16 * ta0, kk, lane, CH);
+                    const typename E::Frag fb = lds_frag_lim<E, CH>(sP, LCH, 16 * ta0, kk, lane);
+                    typename E::Frag fa[C::OPW];
 #pragma unroll
                     for (int m = 0; m < C::OPW; ++m) {
                         int ta, vt;
                         ro_tile<C>(gw, m, ta, vt);
-                        if (vt < NVT) ao[m] = E::mma(fa, lds_frag_lim<E>(sDt, LCH, 16 * vt, kk, lane, CH), ao[m]);
+                        fa[m] = lds_frag_lim<E, CH>(sDt, LCH, 16 * (vt < NVT ? vt : 0), kk, lane);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int m = 0; m < C::OPW; ++m) {
+                        int ta, vt;
+                        ro_tile<C>(gw, m, ta, vt);
+                        if (vt < NVT) ao[m] = E::mma(fa[m], fb, ao[m]);
                     }
                 }
             }
 #pragma unroll
             for (int m = 0; m < C::OPW; ++m) {
-                int ta, vt;
-                ro_tile<C>(gw, m, ta, vt);
-                if (vt < NVT) {
+                float o[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * ta + 4 * g4 + i;
-                        if (t < nvalid) {
-                            float o = p.scale * ao[m][i];
-                            if (gated) o *= sigmoid(vz[m][i]);
-                            gstore(ychunk + t * HDV + 16 * vt, o);
-                        }
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = p.scale * ao[m][i];
+                    if (gated) o[i] *= sigmoid(to_f32(vz[m][i]));
                 }
+                st_vec4(yd[m], o);
             }
-            if (gated && ch + 1 < nchunks) load_vz(cs + CH);   // z of the next chunk
+            yd_base = gy + ((t0 + cs) * H + h) * DV + vcol0 + 4 * g4;
+            yd_nvalid = nvalid;
         }
         __syncthreads();  // every read of the old S^T is done
         if (lowg) {
@@ -727,6 +856,8 @@ __global__ __launch_bounds__(C::NTHR) void prefill_kernel(PrefillParams p) {
         }
         __syncthreads();
     }
+
+    if (!lowg && !AUG && yd_base) store_y();   // outputs of the last chunk
 
     // ---- final state ---------------------------------------------------------
     if (lowg && p.sfin && n >= p.final_seq_lo) {
