@@ -107,10 +107,12 @@ def bench_headline(args, torch, kda, kda_inputs, dev):
     d = {n: getattr(inp, n).to(dev) for n in ("q", "k", "v", "z", "g", "beta")}
     y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
     fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, C, 1, T),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C, y=y,
-                      final_state=fs)
+                      final_state=fs, workspace=ws)
 
     ms, wall = time_steps(step, args.steps, args.warmup, torch)
     log(f"headline: {ms:.4f} ms per step ({args.steps} steps, wall {wall:.3f} s)")
@@ -156,17 +158,19 @@ def bench_varlen(args, torch, kda, kda_inputs, dev):
     T = sum(lens)
     y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
     fs = torch.empty(len(lens), H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, w["chunk"], len(lens), T),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], z=d["z"],
-                      initial_state=d["s0"], chunk=w["chunk"], y=y, final_state=fs)
+                      initial_state=d["s0"], chunk=w["chunk"], y=y, final_state=fs, workspace=ws)
 
     ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, len(lens), True, True)
     out = dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3),
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                tflops=prefill_flops(T, H, dk, dv, w["chunk"]) / (ms * 1e-3) / 1e12)
-    del d, y, fs
+    del d, y, fs, ws
     torch.cuda.empty_cache()
     return out
 
@@ -176,7 +180,8 @@ def bench_kcp(args, torch, kda, kda_inputs, dev):
     H, dk, dv, T, S = w["H"], w["dk"], w["dv"], w["lens"][0], w["segments"]
     log(f"kcp_long_sequence: T={T} H={H} segments={S}")
     d = gpu_inputs(torch, [T], H, dk, dv, False, 0.0, kda_inputs.workload_seed(3), dev)
-    ws = torch.empty(kda.kcp_workspace_size(H, dk, dv, S), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda.kcp_workspace_size(kda.KDA_BF16, H, dk, dv, w["chunk"], T, S),
+                     dtype=torch.uint8, device=dev)
     y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
     fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
 
@@ -300,7 +305,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS,
                      "traffic": counter_traffic("prefill"),
-                     "kernel": "prefill_kernel (kModeSeq, bf16, dk=dv=128, chunk 64)",
+                     "kernel": ("kda_chunk_fwd = chunk_prep_kernel + chunk_state_kernel "
+                                "(bf16, dk=dv=128, chunk 64); time of the whole call"),
                      "bytes_per_launch": head["bytes"]},
         "mfma": {"achieved": head["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": head["tflops"] / BF16_MFMA_PEAK_TFLOPS,

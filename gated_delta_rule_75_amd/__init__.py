@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "KDAError", "lib", "library_path", "kda_version", "kda_status_string",
-    "chunk_fwd", "kcp_scan", "kcp_workspace_size", "decode_step",
+    "chunk_fwd", "chunk_fwd_workspace_size", "kcp_scan", "kcp_workspace_size", "decode_step",
     "KDA_BF16", "KDA_F32",
 ]
 
@@ -30,8 +30,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 
 # Every symbol include/kda.h declares.
-SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd", "kda_kcp_workspace_size",
-           "kda_kcp_scan", "kda_decode_step")
+SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
+           "kda_kcp_workspace_size", "kda_kcp_scan", "kda_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -58,9 +58,12 @@ def lib() -> ctypes.CDLL:
     L.kda_version.restype = i
     L.kda_status_string.argtypes = [i]
     L.kda_status_string.restype = ctypes.c_char_p
-    L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i64]
+    L.kda_chunk_fwd_workspace_size.restype = sz
+    L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                vp, sz, vp]
     L.kda_chunk_fwd.restype = i
-    L.kda_kcp_workspace_size.argtypes = [i, i, i, i]
+    L.kda_kcp_workspace_size.argtypes = [i, i, i, i, i, i64, i]
     L.kda_kcp_workspace_size.restype = sz
     L.kda_kcp_scan.argtypes = [i, i, i, i, i, f, i64, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                sz, vp]
@@ -132,13 +135,20 @@ def _check_inputs(q, k, v, g, beta, z):
     return dt, T, H, dk, dv
 
 
+def chunk_fwd_workspace_size(dtype: int, H: int, dk: int, dv: int, chunk: int, num_seqs: int,
+                             T_total: int) -> int:
+    return int(lib().kda_chunk_fwd_workspace_size(dtype, H, dk, dv, chunk, num_seqs, T_total))
+
+
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=None,
               initial_state=None, output_final_state: bool = True, chunk: int = 64,
               scale: float = 1.0, y: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Prefill over packed sequences; returns (y, final_state or None)."""
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill over packed sequences; returns (y, final_state or None).  The
+    workspace (uint8 device tensor) is allocated when not given."""
     dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
-    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state)
+    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state, workspace)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
@@ -152,15 +162,22 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=Non
     for name, s in (("initial_state", initial_state), ("final_state", final_state)):
         if s is not None and (s.dtype != torch.float32 or s.shape != (N, H, dk, dv)):
             raise ValueError(f"{name} must be float32 [{N}, {H}, {dk}, {dv}]")
+    if workspace is None:
+        need = chunk_fwd_workspace_size(dt, H, dk, dv, chunk, N, T)
+        if need == 0:
+            raise KDAError("kda_chunk_fwd_workspace_size", 2)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib().kda_chunk_fwd(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens), _ptr(q),
                              _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
-                             _ptr(initial_state), _ptr(final_state), _ptr(y), _stream(dev))
+                             _ptr(initial_state), _ptr(final_state), _ptr(y), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(dev))
     _check("kda_chunk_fwd", st)
     return y, final_state
 
 
-def kcp_workspace_size(H: int, dk: int, dv: int, num_segments: int) -> int:
-    return int(lib().kda_kcp_workspace_size(H, dk, dv, num_segments))
+def kcp_workspace_size(dtype: int, H: int, dk: int, dv: int, chunk: int, T: int,
+                       num_segments: int) -> int:
+    return int(lib().kda_kcp_workspace_size(dtype, H, dk, dv, chunk, T, num_segments))
 
 
 def kcp_scan(q, k, v, g, beta, num_segments: int, z=None, initial_state=None, chunk: int = 64,
@@ -169,7 +186,7 @@ def kcp_scan(q, k, v, g, beta, num_segments: int, z=None, initial_state=None, ch
     """One long sequence split into segments composed by a prefix scan; returns (y, final_state)."""
     dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
     dev = _dev(q, k, v, g, beta, z, initial_state, workspace, y, final_state)
-    need = kcp_workspace_size(H, dk, dv, num_segments)
+    need = kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments)
     if need == 0:
         raise KDAError("kda_kcp_workspace_size", 2)
     if workspace is None:

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "kcp.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk_prep.hip", "chunk_state.hip", "kcp.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

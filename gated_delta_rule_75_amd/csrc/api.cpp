@@ -8,17 +8,74 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t elt_align(kda_dtype dt) { return dt == KDA_BF16 ? 4 : 8; }
+
+// The prefill kernels move q, k, v, z, y in runs of four elements.
+size_t vec_align(kda_dtype dt) { return dt == KDA_BF16 ? 8 : 16; }
 
 bool head_shape_ok(int dk, int dv) { return (dk == 64 && dv == 64) || (dk == 128 && dv == 128); }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of the two-pass prefill: sequence plan, then the per-(chunk, head)
+// product arrays, each 256-byte aligned.
+struct Layout {
+    size_t chunk_off, order, wn, qt, kht, pm, ut, gam, total;
+};
+
+Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs, int64_t nchunks) {
+    const kda::TwoPassDims d = kda::twopass_dims((int)dt, dk, dv, chunk);
+    const size_t nb = (size_t)nchunks * H;
+    Layout l;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes, 256); return at; };
+    l.chunk_off = take((size_t)(num_seqs + 1) * 4);
+    l.order = take((size_t)num_seqs * 4);
+    l.wn = take(nb * d.wn() * d.esz);
+    l.qt = take(nb * d.qt() * d.esz);
+    l.kht = take(nb * d.kht() * d.esz);
+    l.pm = take(nb * d.pm() * d.esz);
+    l.ut = take(nb * d.ut() * d.esz);
+    l.gam = take(nb * d.gam() * 4);
+    l.total = o;
+    return l;
+}
+
+kda::TwoPassBufs bufs_at(void* ws, const Layout& l) {
+    char* b = static_cast<char*>(ws);
+    kda::TwoPassBufs x;
+    x.wn = b + l.wn;
+    x.qt = b + l.qt;
+    x.kht = b + l.kht;
+    x.pm = b + l.pm;
+    x.ut = b + l.ut;
+    x.gam = reinterpret_cast<float*>(b + l.gam);
+    return x;
+}
+
+// Upper bound on the chunks of packed sequences: sum ceil(len_n / C) <= T/C + N.
+int64_t varlen_chunks(int64_t T_total, int chunk, int num_seqs) { return T_total / chunk + num_seqs; }
+
+int64_t seg_chunks(int64_t seg_len, int chunk, int num_seqs) {
+    return (int64_t)num_seqs * ((seg_len + chunk - 1) / chunk);
+}
+
+// Value tiles per scan wave: two (half the operand traffic per column) when
+// that still leaves many workgroups; a scan workgroup covers 64 NVT state
+// columns (4 waves of 16 NVT).
+int pick_nvt(int64_t chains, int dvt) {
+    if (dvt % 128 != 0) return 1;
+#ifdef KDA_SCAN_NVT
+    return KDA_SCAN_NVT;
+#endif
+    return chains * (dvt / 128) >= 1024 ? 2 : 1;
+}
 
 // Byte sizes of the KCP workspace parts.
 void kcp_parts(int H, int dk, int dv, int nseg, size_t* pairs, size_t* starts) {
@@ -43,24 +100,38 @@ const char* kda_status_string(kda_status s) {
     return "KDA_ERR_UNKNOWN";
 }
 
+size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs,
+                                    int64_t T_total) {
+    if ((dt != KDA_BF16 && dt != KDA_F32) || H <= 0 || num_seqs <= 0 || T_total < 0) return 0;
+    if (!kda::prefill_supported((int)dt, dk, dv, chunk)) return 0;
+    return twopass_layout(dt, H, dk, dv, chunk, num_seqs, varlen_chunks(T_total, chunk, num_seqs)).total;
+}
+
 kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
                          int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
                          const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const void* z, const float* initial_state,
-                         float* final_state, void* y, void* stream) {
+                         float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
     if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
     if (H <= 0 || num_seqs <= 0 || T_total < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARGUMENT;
     if ((int64_t)num_seqs * H > (int64_t)1 << 28) return KDA_ERR_INVALID_ARGUMENT;
+    if (T_total / 16 + num_seqs > ((int64_t)1 << 31) / H) return KDA_ERR_INVALID_ARGUMENT;
     if (!head_shape_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (!kda::prefill_supported((int)dt, dk, dv, chunk)) return KDA_ERR_UNSUPPORTED;
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !y)) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t ea = elt_align(dt);
+    if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t ea = vec_align(dt);
     if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
-        !aligned(y, ea) || !aligned(g, 8) || !aligned(beta, 4) || !aligned(cu_seqlens, 4) ||
-        !aligned(initial_state, 16) || !aligned(final_state, 16))
+        !aligned(y, ea) || !aligned(g, 16) || !aligned(beta, 4) || !aligned(cu_seqlens, 4) ||
+        !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256))
         return KDA_ERR_INVALID_ARGUMENT;
-    kda::PrefillArgs a{};
+    const int64_t nchunks = cu_seqlens ? varlen_chunks(T_total, chunk, num_seqs)
+                                       : seg_chunks(T_total, chunk, num_seqs);
+    const Layout l = twopass_layout(dt, H, dk, dv, chunk, num_seqs, varlen_chunks(T_total, chunk, num_seqs));
+    if (workspace_bytes < l.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    kda::TwoPassArgs a{};
     a.dtype = (int)dt;
     a.H = H;
     a.dk = dk;
@@ -81,17 +152,32 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
     a.final_state = final_state;
     a.final_seq_lo = 0;
     a.y = y;
-    a.mode = cu_seqlens ? 1 : 0;
-    a.vs = 0;
+    a.mode = cu_seqlens ? kda::kModeVarlen : kda::kModeSeq;
+    a.nvt = pick_nvt((int64_t)num_seqs * H, dv);
+    a.bufs = bufs_at(workspace, l);
+    a.chunk_cap = varlen_chunks(T_total, chunk, num_seqs);
     a.stream = stream;
-    return from_hip(kda::launch_prefill(a));
+    int32_t* chunk_off = nullptr;
+    int32_t* order = nullptr;
+    if (cu_seqlens) {
+        chunk_off = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.chunk_off);
+        order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.order);
+        if (kda::launch_varlen_plan(num_seqs, cu_seqlens, chunk, chunk_off, order, stream) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
+    if (kda::launch_chunk_prep(a, chunk_off, nchunks) != hipSuccess) return KDA_ERR_HIP;
+    return from_hip(kda::launch_chunk_state(a, chunk_off, order));
 }
 
-size_t kda_kcp_workspace_size(int H, int dk, int dv, int num_segments) {
-    if (H <= 0 || num_segments <= 0 || !head_shape_ok(dk, dv)) return 0;
+size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int64_t T,
+                              int num_segments) {
+    if ((dt != KDA_BF16 && dt != KDA_F32) || H <= 0 || num_segments <= 0 || T < num_segments) return 0;
+    if (!kda::prefill_supported((int)dt, dk, dv, chunk)) return 0;
     size_t pairs, starts;
     kcp_parts(H, dk, dv, num_segments, &pairs, &starts);
-    return pairs + starts;
+    const int64_t seg_len = (T + num_segments - 1) / num_segments;
+    return pairs + starts +
+           twopass_layout(dt, H, dk, dv, chunk, num_segments, seg_chunks(seg_len, chunk, num_segments)).total;
 }
 
 kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float scale, int64_t T,
@@ -101,23 +187,27 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
                         void* workspace, size_t workspace_bytes, void* stream) {
     if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
     if (H <= 0 || num_segments <= 0 || T < num_segments) return KDA_ERR_INVALID_ARGUMENT;
+    if (T / 16 + num_segments > ((int64_t)1 << 31) / H) return KDA_ERR_INVALID_ARGUMENT;
     if (!head_shape_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (!kda::prefill_supported((int)dt, dk, dv, chunk)) return KDA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !g || !beta || !y || !workspace) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t ea = elt_align(dt);
+    const size_t ea = vec_align(dt);
     if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
-        !aligned(y, ea) || !aligned(g, 8) || !aligned(beta, 4) || !aligned(workspace, 256) ||
+        !aligned(y, ea) || !aligned(g, 16) || !aligned(beta, 4) || !aligned(workspace, 256) ||
         !aligned(initial_state, 16) || !aligned(final_state, 16))
         return KDA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < kda_kcp_workspace_size(H, dk, dv, num_segments))
+    if (workspace_bytes < kda_kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments))
         return KDA_ERR_WORKSPACE_TOO_SMALL;
     size_t pbytes, sbytes;
     kcp_parts(H, dk, dv, num_segments, &pbytes, &sbytes);
     float* pairs = static_cast<float*>(workspace);
     float* starts = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes);
-    const int64_t seg_len = (T + num_segments - 1) / num_segments;
+    void* tp = static_cast<char*>(workspace) + pbytes + sbytes;
     // segments hold seg_len tokens each; with T not a multiple, trailing ones may be empty
-    kda::PrefillArgs a{};
+    const int64_t seg_len = (T + num_segments - 1) / num_segments;
+    const int64_t nchunks = seg_chunks(seg_len, chunk, num_segments);
+    const Layout l = twopass_layout(dt, H, dk, dv, chunk, num_segments, nchunks);
+    kda::TwoPassArgs a{};
     a.dtype = (int)dt;
     a.H = H;
     a.dk = dk;
@@ -134,29 +224,33 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.g = g;
     a.beta = beta;
     a.z = z;
+    a.bufs = bufs_at(tp, l);
+    a.chunk_cap = nchunks;
     a.stream = stream;
-    a.vs = 0;
+    // the chunk products serve both passes over the segments
+    if (kda::launch_chunk_prep(a, nullptr, nchunks) != hipSuccess) return KDA_ERR_HIP;
     // phase 1: (M, Sloc) of every segment, as the state that the augmented value
     // block [0 | v] builds from the augmented start [I | 0]
-    a.mode = 2;
+    a.mode = kda::kModePairs;
+    a.nvt = pick_nvt((int64_t)num_segments * H, dk + dv);
     a.initial_state = nullptr;
     a.final_state = pairs;
     a.final_seq_lo = 0;
     a.y = nullptr;
-    hipError_t e = kda::launch_prefill(a);
-    if (e != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
     // phase 2: entering state of every segment
-    e = kda::launch_kcp_scan(H, dk, dv, num_segments, pairs, initial_state, starts, final_state,
-                             (hipStream_t)stream);
-    if (e != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_kcp_scan(H, dk, dv, num_segments, pairs, initial_state, starts, final_state,
+                             (hipStream_t)stream) != hipSuccess)
+        return KDA_ERR_HIP;
     // phase 3: outputs of every segment from its entering state; the last
     // segment's final state is the sequence's final state
-    a.mode = 3;
+    a.mode = kda::kModeFinish;
+    a.nvt = pick_nvt((int64_t)num_segments * H, dv);
     a.initial_state = starts;
     a.final_state = final_state;
     a.final_seq_lo = num_segments - 1;
     a.y = y;
-    return from_hip(kda::launch_prefill(a));
+    return from_hip(kda::launch_chunk_state(a, nullptr, nullptr));
 }
 
 kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float scale,
@@ -192,3 +286,13 @@ kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float sca
 }
 
 }  // extern "C"
+
+namespace kda {
+
+bool prefill_supported(int dtype, int dk, int dv, int chunk) {
+    if (!((dk == 64 && dv == 64) || (dk == 128 && dv == 128))) return false;
+    if (chunk != 16 && chunk != 64) return false;
+    return dtype == 0 || dtype == 1;
+}
+
+}  // namespace kda

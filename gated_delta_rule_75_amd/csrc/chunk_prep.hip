@@ -1,0 +1,463 @@
+// Chunk preparation: every product of a chunk that does not involve the state
+// entering it, for all (chunk, head) pairs at once (the two-pass form and the
+// workspace layout are described in twopass.h).
+//
+// One workgroup (8 waves; 4 for dk = 64 with 16-token chunks) per (chunk, head):
+//  1. decay: each thread holds TPT consecutive tokens x 4 consecutive channels
+//     of g, k, q, v; the in-chunk running sum G of g is a per-thread sum plus
+//     a shuffle scan over the wave's token groups.
+//  2. gated Gram products A (k.k, strictly lower) and P (q.k, lower) on MFMA.
+//     The factor e^{G_t - G_j} is split at 16-token sub-tile references so no
+//     operand exceeds e^{16 |g_min|}: page "Exercices", Niveau 2 Q8 sizes
+//     g_min = -5 for exactly this (16 tokens give e^80, inside the bf16
+//     range).  Row operand x_t e^{G_t - R_a(t)} <= 1, column operand
+//     k_j e^{R_b(j) - G_j} <= e^80, and for an off-diagonal block (a, b) the
+//     column factor e^{R_a - R_b} <= 1, applied while loading the fragment.
+//  3. L = I + diag(beta) A is unit lower triangular; its inverse is blocked:
+//     16 x 16 diagonal blocks by forward substitution, then off-diagonal
+//     blocks level by level, X_ab = -X_aa sum_{b<=c<a} L_ac X_cb (fp32).
+//  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA.
+// Qt, Kh and gam leave straight from the decay phase; the tiles of W, U and
+// P leave as they are produced.
+#include "launch.h"
+#include "twopass.h"
+
+namespace kda {
+
+struct PrepParams {
+    int H, num_seqs, cps;   // cps: chunks per segment when cu_seqlens is NULL
+    float scale;
+    int64_t T_total, seg_len;
+    const int32_t* cu_seqlens;
+    const int32_t* chunk_off;  // [num_seqs + 1] chunk offsets of packed sequences, or NULL
+    const void *q, *k, *v;
+    const float *g, *beta;
+    TwoPassBufs ws;
+};
+
+template <typename E_, int DK_, int CH_>
+struct PrepCfg {
+    using E = E_;
+    using K = KBlk<E_>;
+    using T = typename E::T;
+    static constexpr int DK = DK_, DV = DK_, CH = CH_;
+    static constexpr int NT = CH / 16, NCT = DK / 16, NPAIR = NT * (NT + 1) / 2;
+    static constexpr int CP = (CH + K::KB - 1) / K::KB * K::KB;
+    static constexpr int NKT = CP / K::KB;                  // k-blocks over tokens
+    static constexpr int NPM = pm_frags(NT, NKT, K::KB);    // stored fragments of Pm
+    static constexpr int NW = (DK == 64 && CH == 16) ? 4 : 8, NTHR = 64 * NW;
+    // decay-phase mapping: wave w owns channels [w DK/NW, (w+1) DK/NW); lane =
+    // (token group tg, channel group cg) holds TPT tokens x 4 channels
+    static constexpr int CGW = DK / (4 * NW), TGW = 64 / CGW, TPT = CH / TGW;
+    static_assert(TPT >= 1 && TPT * TGW == CH && 16 % TPT == 0, "decay mapping");
+    static constexpr int PADE = 16 / (int)sizeof(T);
+    static constexpr int LK = DK + PADE;  // pitch of [token][channel] tables
+    static constexpr int LC = CP + PADE;  // pitch of [row][token] tables
+    static constexpr int BLK = 16 * 17;   // fp32 16x16 block, pitch 17
+    static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+    static constexpr size_t SZ_TAB = (size_t)CH * LK * sizeof(T);
+    static constexpr size_t SZ_X1 = 3 * SZ_TAB;                       // Kr, Qr, Kc
+    static constexpr size_t SZ_KVT = al((size_t)DK * LC * sizeof(T));  // Kt^T or V^T
+    static constexpr size_t SZ_LB = al((size_t)CH * LC * sizeof(T));
+    static constexpr size_t SZ_X2 = 2 * SZ_KVT + SZ_LB;                // after the Gram
+    static constexpr size_t O_KR = 0, O_QR = SZ_TAB, O_KC = 2 * SZ_TAB;
+    static constexpr size_t O_KTT = 0, O_VTT = SZ_KVT, O_LB = 2 * SZ_KVT;
+    static constexpr size_t O_M = O_LB;  // level scratch, before L^{-1} diag(beta) is written
+    static constexpr size_t SZ_X = al(SZ_X1 > SZ_X2 ? SZ_X1 : SZ_X2);
+    static constexpr size_t O_L = SZ_X;                         // blocks of beta A
+    static constexpr size_t O_Z = O_L + (size_t)NPAIR * BLK * 4;  // blocks of L^{-1}
+    static constexpr int ND = NT * (NT - 1) / 2;
+    static constexpr size_t O_D = O_Z + (size_t)NPAIR * BLK * 4;   // e^{R_a - R_b}, a > b
+    static constexpr size_t O_BETA = O_D + (size_t)(ND > 0 ? ND : 1) * DK * 4;
+    static constexpr size_t BYTES = O_BETA + (size_t)CH * 4;
+    static_assert((size_t)(NT > 1 ? NT - 1 : 1) * BLK * 4 <= SZ_LB, "level scratch");
+    static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+__device__ __forceinline__ int pair_index(int a, int b) { return a * (a + 1) / 2 + b; }
+
+// four consecutive elements <-> fp32
+__device__ __forceinline__ f32x4_t ld4f(const __bf16* p) {
+    const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
+    return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4_t ld4f(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+__device__ __forceinline__ void st4(__bf16* p, float a, float b, float c, float d) {
+    *reinterpret_cast<bf16x4_t*>(p) = bf16x4_t{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
+    using E = typename C::E;
+    using K = typename C::K;
+    using T = typename C::T;
+    constexpr int DK = C::DK, DV = C::DV, CH = C::CH, NT = C::NT, NCT = C::NCT, CP = C::CP;
+    constexpr int LK = C::LK, LC = C::LC, BLK = C::BLK, NTHR = C::NTHR, NW = C::NW;
+    constexpr int CGW = C::CGW, TGW = C::TGW, TPT = C::TPT;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T* sKr = reinterpret_cast<T*>(smem + C::O_KR);
+    T* sQr = reinterpret_cast<T*>(smem + C::O_QR);
+    T* sKc = reinterpret_cast<T*>(smem + C::O_KC);
+    T* sKtT = reinterpret_cast<T*>(smem + C::O_KTT);
+    T* sVtT = reinterpret_cast<T*>(smem + C::O_VTT);
+    T* sLB = reinterpret_cast<T*>(smem + C::O_LB);
+    float* sM = reinterpret_cast<float*>(smem + C::O_M);
+    float* sL = reinterpret_cast<float*>(smem + C::O_L);
+    float* sZ = reinterpret_cast<float*>(smem + C::O_Z);
+    float* sD = reinterpret_cast<float*>(smem + C::O_D);
+    float* sBeta = reinterpret_cast<float*>(smem + C::O_BETA);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int H = p.H;
+    const int64_t wsb = blockIdx.x;  // (chunk, head) block of the workspace
+    const int h = (int)(wsb % H);
+    const int gc = (int)(wsb / H);
+
+    // ---- locate the chunk ----------------------------------------------------
+    int64_t ts;
+    int nvalid;
+    if (p.chunk_off) {
+        if (gc >= p.chunk_off[p.num_seqs]) return;
+        int lo = 0, hi = p.num_seqs;  // chunk_off[lo] <= gc < chunk_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.chunk_off[mid] <= gc) lo = mid;
+            else hi = mid;
+        }
+        ts = p.cu_seqlens[lo] + (int64_t)(gc - p.chunk_off[lo]) * CH;
+        const int64_t rem = p.cu_seqlens[lo + 1] - ts;
+        nvalid = (int)(rem < CH ? rem : CH);
+    } else {
+        const int n = gc / p.cps;
+        if (n >= p.num_seqs) return;
+        const int64_t s0 = (int64_t)n * p.seg_len;
+        const int64_t s1 = s0 + p.seg_len < p.T_total ? s0 + p.seg_len : p.T_total;
+        ts = s0 + (int64_t)(gc % p.cps) * CH;
+        if (ts >= s1) return;  // past the end of a short last segment
+        nvalid = (int)(s1 - ts < CH ? s1 - ts : CH);
+    }
+    // never read past T_total, whatever the offsets say
+    if (ts >= p.T_total) return;
+    if (ts + nvalid > p.T_total) nvalid = (int)(p.T_total - ts);
+
+    T* Wn = static_cast<T*>(p.ws.wn) + wsb * (CH * DK);
+    T* Qt = static_cast<T*>(p.ws.qt) + wsb * (CH * DK);
+    T* KhT = static_cast<T*>(p.ws.kht) + wsb * (DK * CP);
+    T* Pm = static_cast<T*>(p.ws.pm) + wsb * (C::NPM * 64 * (K::KB / 4));
+    T* UT = static_cast<T*>(p.ws.ut) + wsb * (DV * CH);
+    float* gam = p.ws.gam + wsb * DK;
+
+    // ---- 1. loads and decay ----------------------------------------------------
+    const int tg = lane / CGW, cg = lane % CGW;
+    const int c0 = wave * (DK / NW) + 4 * cg;
+    const int tl0 = tg * TPT;
+    const T* gq = static_cast<const T*>(p.q);
+    const T* gk = static_cast<const T*>(p.k);
+    const T* gv = static_cast<const T*>(p.v);
+    f32x4_t G[TPT], kx[TPT], qx[TPT], vx[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int t = tl0 + i;
+        const bool ok = t < nvalid;
+        const int64_t row = (ts + (ok ? t : 0)) * H + h;
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(p.g + row * DK + c0);
+        const f32x4_t kk = ld4f(gk + row * DK + c0);
+        const f32x4_t qq = ld4f(gq + row * DK + c0);
+        const f32x4_t vv = ld4f(gv + row * DV + c0);
+        G[i] = ok ? gg : zero;
+        kx[i] = ok ? kk : zero;
+        qx[i] = ok ? qq : zero;
+        vx[i] = ok ? vv : zero;
+    }
+    if (tid < CH) sBeta[tid] = tid < nvalid ? p.beta[(ts + tid) * H + h] : 0.f;
+
+    // running sum over the thread's tokens, then over the wave's token groups
+#pragma unroll
+    for (int i = 1; i < TPT; ++i) G[i] += G[i - 1];
+    {
+        f32x4_t inc = G[TPT - 1];
+#pragma unroll
+        for (int d = 1; d < TGW; d <<= 1) {
+            f32x4_t y;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) y[ch] = __shfl_up(inc[ch], d * CGW, 64);
+            if (tg >= d) inc += y;
+        }
+        const f32x4_t ex = inc - G[TPT - 1];
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) G[i] += ex;
+    }
+    // sub-tile references R_b = G at token 16 b - 1 (R_0 = 0) and G_C
+    f32x4_t Rb[NT], Ro, GC;
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+        const int src = (b == 0 ? 0 : (16 * b) / TPT - 1) * CGW + cg;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) Rb[b][ch] = __shfl(G[TPT - 1][ch], src, 64);
+        if (b == 0) Rb[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+        const int a = tl0 / 16;
+        const int src = (a == 0 ? 0 : (16 * a) / TPT - 1) * CGW + cg;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            Ro[ch] = __shfl(G[TPT - 1][ch], src, 64);
+            GC[ch] = __shfl(G[TPT - 1][ch], (TGW - 1) * CGW + cg, 64);
+        }
+        if (a == 0) Ro = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (tg == 0) {
+#pragma unroll
+        for (int a = 1; a < NT; ++a)
+#pragma unroll
+            for (int b = 0; b < a; ++b) {
+                float* d = sD + (a * (a - 1) / 2 + b) * DK + c0;
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) d[ch] = __expf(Rb[a][ch] - Rb[b][ch]);
+            }
+        st4(gam + c0, __expf(GC[0]), __expf(GC[1]), __expf(GC[2]), __expf(GC[3]));
+    }
+    const float scale = p.scale;
+    f32x4_t kh[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int t = tl0 + i;
+        f32x4_t kr, qr, kc, qt;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            const float Gv = G[i][ch];
+            const float er = __expf(Gv - Ro[ch]);   // <= 1
+            const float ec = __expf(Ro[ch] - Gv);   // <= e^80
+            const float eg = __expf(Gv);
+            kr[ch] = kx[i][ch] * er;
+            qr[ch] = qx[i][ch] * er;
+            kc[ch] = kx[i][ch] * ec;
+            qt[ch] = scale * qx[i][ch] * eg;
+            kh[i][ch] = kx[i][ch] * __expf(GC[ch] - Gv);
+            kx[i][ch] *= eg;  // K e^G, the W operand
+        }
+        st4(sKr + t * LK + c0, kr[0], kr[1], kr[2], kr[3]);
+        st4(sQr + t * LK + c0, qr[0], qr[1], qr[2], qr[3]);
+        st4(sKc + t * LK + c0, kc[0], kc[1], kc[2], kc[3]);
+        st4(Qt + frag_elem<K>((c0 / K::KB) * NT + t / 16, t, c0), qt[0], qt[1], qt[2], qt[3]);
+    }
+    // Kh^T rows: TPT consecutive tokens of each of the thread's channels
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+        const int c = c0 + ch;
+        if constexpr (TPT >= 4) {
+#pragma unroll
+            for (int r = 0; r < TPT; r += 4) {
+                const int t = tl0 + r;
+                st4(KhT + frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t), kh[r][ch], kh[r + 1][ch],
+                    kh[r + 2][ch], kh[r + 3][ch]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) {
+                const int t = tl0 + i;
+                KhT[frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t)] = from_f32<T>(kh[i][ch]);
+            }
+        }
+    }
+    // zero padding past C (k-blocks over tokens) and the P tiles above the
+    // diagonal that share a k-block with a diagonal tile
+    if constexpr (CP > CH) {
+        for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
+            const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
+            KhT[frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t)] = from_f32<T>(0.f);
+        }
+        for (int idx = tid; idx < CH * (CP - CH); idx += NTHR) {
+            const int t = idx / (CP - CH), j = CH + idx % (CP - CH);
+            Pm[frag_elem<K>(pm_frag_index(t / 16, j / K::KB, C::NKT, K::KB), t, j)] = from_f32<T>(0.f);
+        }
+    }
+    if constexpr (K::TPB == 2 && NT > 1) {
+        for (int idx = tid; idx < (NT / 2) * 256; idx += NTHR) {
+            const int a = 2 * (idx >> 8), e = idx & 255;
+            const int t = 16 * a + (e >> 4), j = 16 * (a + 1) + (e & 15);
+            Pm[frag_elem<K>(pm_frag_index(a, j / K::KB, C::NKT, K::KB), t, j)] = from_f32<T>(0.f);
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. gated Gram products -------------------------------------------------
+    for (int task = wave; task < C::NPAIR; task += NW) {
+        int a = 0;
+        while ((a + 1) * (a + 2) / 2 <= task) ++a;
+        const int b = task - a * (a + 1) / 2;
+        const float* dsc = sD + (a > b ? (a * (a - 1) / 2 + b) : 0) * DK;
+        f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int kk = 0; kk < DK; kk += E::KSTEP) {
+            const typename E::Frag fc = a > b ? lds_frag_scaled<E>(sKc, LK, 16 * b, kk, lane, dsc)
+                                              : lds_frag<E>(sKc, LK, 16 * b, kk, lane);
+            const typename E::Frag fr = lds_frag<E>(sKr, LK, 16 * a, kk, lane);
+            const typename E::Frag fq = lds_frag<E>(sQr, LK, 16 * a, kk, lane);
+            accA = E::mma(fr, fc, accA);  // A[t][j]
+            accP = E::mma(fc, fq, accP);  // P^T[j][t]
+        }
+        // beta_t A[t][j] (strictly lower): lane holds rows 16a+4g4+i, column 16b+l16
+        float* Lb = sL + pair_index(a, b) * BLK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            Lb[r * 17 + l16] = (a > b || l16 < r) ? sBeta[16 * a + r] * accA[i] : 0.f;
+        }
+        // scale P[t][j] (j <= t): lane holds token 16a+l16, columns 16b+4g4+i
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = (a > b || 4 * g4 + i <= l16) ? scale * accP[i] : 0.f;
+        const int j0 = 16 * b + 4 * g4;
+        st4(Pm + frag_elem<K>(pm_frag_index(a, j0 / K::KB, C::NKT, K::KB), l16, j0), pv[0], pv[1], pv[2], pv[3]);
+    }
+    __syncthreads();
+
+    // ---- 3. operands of W and U; inverse of L ----------------------------------
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+        T* kt = sKtT + (c0 + ch) * LC + tl0;
+        T* vt = sVtT + (c0 + ch) * LC + tl0;
+        if constexpr (TPT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < TPT; i += 4) {
+                st4(kt + i, kx[i][ch], kx[i + 1][ch], kx[i + 2][ch], kx[i + 3][ch]);
+                st4(vt + i, vx[i][ch], vx[i + 1][ch], vx[i + 2][ch], vx[i + 3][ch]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) {
+                kt[i] = from_f32<T>(kx[i][ch]);
+                vt[i] = from_f32<T>(vx[i][ch]);
+            }
+        }
+    }
+    if constexpr (CP > CH) {
+        for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
+            const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
+            sKtT[c * LC + t] = from_f32<T>(0.f);
+            sVtT[c * LC + t] = from_f32<T>(0.f);
+        }
+    }
+    if (wave < NT) {  // diagonal block `wave`, one column per lane (lanes >= 16 repeat)
+        const float* Lb = sL + pair_index(wave, wave) * BLK;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float s = (t == l16) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < t; ++m) s -= Lb[t * 17 + m] * x[m];
+            x[t] = s;
+        }
+        if (lane < 16) {
+            float* Zb = sZ + pair_index(wave, wave) * BLK;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) Zb[t * 17 + l16] = x[t];
+        }
+    }
+    __syncthreads();
+    for (int l = 1; l < NT; ++l) {
+        const int nb = NT - l;
+        for (int idx = tid; idx < nb * 256; idx += NTHR) {
+            const int b = idx >> 8, r = (idx >> 4) & 15, col = idx & 15, a = b + l;
+            float s = 0.f;
+            for (int c = b; c < a; ++c) {
+                const float* La = sL + pair_index(a, c) * BLK + r * 17;
+                const float* Zc = sZ + pair_index(c, b) * BLK + col;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) s += La[m] * Zc[m * 17];
+            }
+            sM[b * BLK + r * 17 + col] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nb * 256; idx += NTHR) {
+            const int b = idx >> 8, r = (idx >> 4) & 15, col = idx & 15, a = b + l;
+            const float* Za = sZ + pair_index(a, a) * BLK + r * 17;
+            float s = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) s += Za[m] * sM[b * BLK + m * 17 + col];
+            sZ[pair_index(a, b) * BLK + r * 17 + col] = -s;
+        }
+        __syncthreads();
+    }
+    // L^{-1} diag(beta), zero above the diagonal blocks and past C
+    for (int idx = tid; idx < CH * CP; idx += NTHR) {
+        const int t = idx / CP, j = idx % CP;
+        const int a = t >> 4, b = j >> 4;
+        float x = 0.f;
+        if (j < CH && b <= a) x = sZ[pair_index(a, b) * BLK + (t & 15) * 17 + (j & 15)] * sBeta[j];
+        sLB[t * LC + j] = from_f32<T>(x);
+    }
+    __syncthreads();
+
+    // ---- 4. W^T = (K e^G)^T (L^{-1} diag(beta))^T and U = L^{-1} diag(beta) V ----
+    for (int task = wave; task < NCT * NT; task += NW) {
+        const int ct = task / NT, ta = task % NT;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 16 * (ta + 1); kk += E::KSTEP)
+            acc = E::mma(lds_frag<E>(sKtT, LC, 16 * ct, kk, lane), lds_frag<E>(sLB, LC, 16 * ta, kk, lane),
+                         acc);
+        // lane holds W[16ta+l16][16ct+4g4+i]; stored negated
+        const int c = 16 * ct + 4 * g4;
+        st4(Wn + frag_elem<K>((c / K::KB) * NT + ta, l16, c), -acc[0], -acc[1], -acc[2], -acc[3]);
+    }
+    for (int task = wave; task < NT * (DV / 16); task += NW) {
+        const int ta = task % NT, vt = task / NT;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 16 * (ta + 1); kk += E::KSTEP)
+            acc = E::mma(lds_frag<E>(sLB, LC, 16 * ta, kk, lane), lds_frag<E>(sVtT, LC, 16 * vt, kk, lane),
+                         acc);
+        // lane holds U[16ta+4g4+i][16vt+l16]: the accumulator-layout tile (vt, ta)
+        st4(UT + ((vt * NT + ta) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <class C>
+static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nblocks) {
+    if (nblocks <= 0) return hipSuccess;
+    PrepParams p;
+    p.H = a.H;
+    p.num_seqs = a.num_seqs;
+    p.cps = (int)((a.seg_len + a.chunk - 1) / a.chunk);
+    p.scale = a.scale;
+    p.T_total = a.T_total;
+    p.seg_len = a.seg_len;
+    p.cu_seqlens = a.cu_seqlens;
+    p.chunk_off = chunk_off;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.g = a.g;
+    p.beta = a.beta;
+    p.ws = a.bufs;
+    auto kern = chunk_prep_kernel<C>;
+    if (C::BYTES > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)C::BYTES);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::NTHR), C::BYTES, (hipStream_t)a.stream, p);
+    return hipGetLastError();
+}
+
+template <class E, int DK>
+static hipError_t launch_prep_dk(const TwoPassArgs& a, const int32_t* co, int64_t nb) {
+    if (a.chunk == 64) return launch_prep_cfg<PrepCfg<E, DK, 64>>(a, co, nb);
+    return launch_prep_cfg<PrepCfg<E, DK, 16>>(a, co, nb);
+}
+
+hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks) {
+    const int64_t nb = nchunks * a.H;
+    if (a.dtype == 0)
+        return a.dk == 128 ? launch_prep_dk<BF16, 128>(a, chunk_off, nb) : launch_prep_dk<BF16, 64>(a, chunk_off, nb);
+    return a.dk == 128 ? launch_prep_dk<F32, 128>(a, chunk_off, nb) : launch_prep_dk<F32, 64>(a, chunk_off, nb);
+}
+
+}  // namespace kda

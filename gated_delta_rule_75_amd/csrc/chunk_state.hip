@@ -1,0 +1,505 @@
+// State scan: carries the state of every (sequence, head) through its chunks
+// with the per-chunk products the preparation kernel stored (twopass.h):
+//     Delta = U + Wn S,   O = Qt S + Pm Delta,   S <- gam * S + Kh^T Delta,
+//     y = O * sigmoid(z).
+//
+// State columns evolve independently.  A workgroup of NW waves owns
+// 16 NVT NW consecutive columns of one (sequence, head); each wave owns
+// 16 NVT of them and keeps its part of S and Delta in MFMA accumulator tiles,
+// fed back as operands straight from the lanes that hold them (the k-block
+// order of twopass.h).  The chunk operands every wave needs (Wn, Qt, Kh^T,
+// Pm, gam) are copied once per workgroup into LDS by direct global-to-LDS
+// loads, double-buffered so chunk c+1 streams in while chunk c is computed.
+// In LDS each operand fragment (16 rows x one k-block) is stored in lane
+// order, 16 bytes per lane, so that every wave reads a fragment with one
+// conflict-free 16-byte access per lane.  U^T and z, private to a wave, go
+// straight to registers one chunk ahead.
+// Products (lane layout: rows 4*(l/16)+i, column l%16 of a 16x16 tile):
+//     Delta [t][v]  += Wn[t][c] . S[c][v]            A = Wn rows,   B = S
+//     O^T  [v][t]   += S^T[v][c] . Qt^T[c][t]        A = S,         B = Qt rows
+//                    + Delta^T[v][j] . Pm^T[j][t]    A = Delta,     B = Pm rows
+//     S    [c][v]   += Kh^T[c][t] . Delta[t][v]      A = Kh^T rows, B = Delta
+// so a lane of O^T holds four consecutive value columns of one token, and
+// the gate input z and the output y move in 8-byte (bf16) runs.
+//
+// The workgroups of one chain take ids with equal residue mod 8, which places
+// them on one XCD, so they share the chunk operands through its L2.
+#include "launch.h"
+#include "twopass.h"
+
+namespace kda {
+
+struct StateParams {
+    int H, num_seqs, nchains, nvg, dvt, final_seq_lo, cps;
+    int chunk_cap;  // chunks the workspace holds
+    int64_t T_total, seg_len;
+    const int32_t* cu_seqlens;
+    const int32_t* chunk_off;
+    const int32_t* order;
+    const void* z;
+    void* y;
+    const float* s0;
+    float* sfin;
+    TwoPassBufs ws;
+};
+
+template <typename E_, int DK_, int DV_, int CH_, int NVT_, int MODE_>
+struct StCfg {
+    using E = E_;
+    using K = KBlk<E_>;
+    using T = typename K::T;
+    static constexpr int DK = DK_, DV = DV_, CH = CH_, NVT = NVT_, MODE = MODE_;
+    static constexpr bool AUG = MODE_ == kModePairs;
+    static constexpr int NW = 4, NTHR = 64 * NW;
+    static constexpr int CW = 16 * NVT * NW;            // state columns per workgroup
+    static constexpr int NTT = CH / 16, NCT = DK / 16;
+    static constexpr int KB = K::KB, TPB = K::TPB;
+    static constexpr int NKC = DK / KB;                 // k-blocks over channels
+    static constexpr int CP = (CH + KB - 1) / KB * KB;
+    static constexpr int NKT = CP / KB;                 // k-blocks over tokens
+    static_assert(NKC * TPB == NCT, "channel k-blocks");
+    static constexpr int NPM = pm_frags(NTT, NKT, KB);  // stored fragments of Pm
+    // fragment index ranges in an LDS buffer (1 KiB each)
+    static constexpr int F_W = 0, N_W = NKC * NTT;
+    static constexpr int F_Q = F_W + N_W, N_Q = AUG ? 0 : NKC * NTT;
+    static constexpr int F_K = F_Q + N_Q, N_K = NCT * NKT;
+    static constexpr int F_P = F_K + N_K, N_P = AUG ? 0 : NPM;
+    static constexpr int F_G = F_P + N_P;               // gam: dk fp32, repeated to fill 1 KiB
+    static constexpr int NF = F_G + 1;
+    static constexpr int FPW = (NF + NW - 1) / NW;      // fragment loads per wave
+    static constexpr int BUF = NF * 1024;
+    static constexpr int NBUF = 2 * BUF <= 150 * 1024 ? 2 : 1;
+    static constexpr int BYTES = NBUF * BUF;
+};
+
+template <typename T> struct VecT4;
+template <> struct VecT4<__bf16> { using type = bf16x4_t; };
+template <> struct VecT4<float> { using type = f32x4_t; };
+__device__ __forceinline__ f32x4_t to_f32x4(bf16x4_t v) {
+    return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4_t to_f32x4(f32x4_t v) { return v; }
+__device__ __forceinline__ void st4s(__bf16* p, f32x4_t x) {
+    *reinterpret_cast<bf16x4_t*>(p) = bf16x4_t{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+__device__ __forceinline__ void st4s(float* p, f32x4_t x) { *reinterpret_cast<f32x4_t*>(p) = x; }
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds + 16 i.  (A __device__ wrapper: the builtin written directly in a
+// kernel template hides the kernel from the host compilation pass.)
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n < 64), other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that leaves global loads in flight.  __syncthreads()
+// waits for every outstanding vector-memory operation (its fence covers the
+// direct-to-LDS prefetch too); here the caller waits for exactly the loads it
+// needs.  Pending LDS reads finish first, so no wave still reads a buffer
+// that another wave's prefetch overwrites after the barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
+    using K = typename C::K;
+    using T = typename C::T;
+    using Frag = typename K::Frag;
+    using T4 = typename VecT4<T>::type;
+    constexpr int DK = C::DK, DV = C::DV, CH = C::CH, NVT = C::NVT, NTT = C::NTT, NCT = C::NCT;
+    constexpr int KB = C::KB, TPB = C::TPB, NKC = C::NKC, NKT = C::NKT, CP = C::CP, NW = C::NW;
+    constexpr int KPL = KB / 4;  // k values per lane
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int g4 = lane >> 4, l16 = lane & 15;
+
+    const int blk = blockIdx.x, r = blk >> 3;
+    const int slot = (r / p.nvg) * 8 + (blk & 7), vg = r % p.nvg;
+    if (slot >= p.nchains) return;
+    const int H = p.H, h = slot % H;
+    const int n = p.order ? p.order[slot / H] : slot / H;
+    int64_t t0, len;
+    int cbase;
+    if (p.cu_seqlens) {
+        t0 = p.cu_seqlens[n];
+        len = p.cu_seqlens[n + 1] - t0;
+        cbase = p.chunk_off[n];
+    } else {
+        t0 = (int64_t)n * p.seg_len;
+        const int64_t t1 = t0 + p.seg_len < p.T_total ? t0 + p.seg_len : p.T_total;
+        len = t1 - t0;
+        cbase = n * p.cps;
+    }
+    // stay inside T_total and the workspace whatever the offsets say
+    if (t0 >= p.T_total) len = 0;
+    else if (t0 + len > p.T_total) len = p.T_total - t0;
+    int nch = len > 0 ? (int)((len + CH - 1) / CH) : 0;
+    if (cbase + nch > p.chunk_cap) nch = cbase < p.chunk_cap ? p.chunk_cap - cbase : 0;
+    const int dvt = p.dvt;
+    const int colw = vg * C::CW + wave * 16 * NVT;  // first state column of the wave
+    const bool ident = C::AUG && colw < DK;         // transition columns: start I, values 0
+    const int vcol0 = C::AUG ? colw - DK : colw;    // its first column of v / z / y
+
+    // ---- state ---------------------------------------------------------------
+    f32x4_t S[NCT][NVT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+            const int col = colw + 16 * vt + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ct][vt][i] = (C::AUG && col == 16 * ct + 4 * g4 + i) ? 1.f : 0.f;
+        }
+    if (!C::AUG && p.s0) {
+        const float* s0 = p.s0 + ((int64_t)n * H + h) * DK * (int64_t)dvt;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[ct][vt][i] = s0[(int64_t)(16 * ct + 4 * g4 + i) * dvt + colw + 16 * vt + l16];
+    }
+
+    const T* gz = static_cast<const T*>(p.z);
+    T* gy = static_cast<T*>(p.y);
+
+    // ---- operand staging -----------------------------------------------------
+    // Fragment f of a chunk into LDS: lane i fetches the 16 bytes it (and the
+    // same lane of every other wave) will read.  Wave w stages fragments
+    // w, w + NW, ...; where a fragment sits in the workspace does not depend
+    // on the chunk, so each is resolved once here to (array, block stride,
+    // lane offset).
+    const char* fbase[C::FPW];
+    int64_t fstride[C::FPW];
+    int foff[C::FPW];
+#pragma unroll
+    for (int j = 0; j < C::FPW; ++j) {
+        int f = wave + NW * j;
+        f = f < C::NF ? f : C::NF - 1;   // the last wave repeats its last fragment
+        constexpr int FB = 64 * KPL * (int)sizeof(T);   // bytes of one fragment
+        if (f < C::F_Q) {
+            fbase[j] = static_cast<const char*>(p.ws.wn);
+            fstride[j] = (int64_t)CH * DK * sizeof(T);
+            foff[j] = (f - C::F_W) * FB;
+        } else if (f < C::F_K) {
+            fbase[j] = static_cast<const char*>(p.ws.qt);
+            fstride[j] = (int64_t)CH * DK * sizeof(T);
+            foff[j] = (f - C::F_Q) * FB;
+        } else if (f < C::F_P) {
+            fbase[j] = static_cast<const char*>(p.ws.kht);
+            fstride[j] = (int64_t)DK * CP * sizeof(T);
+            foff[j] = (f - C::F_K) * FB;
+        } else if (f < C::F_G) {
+            fbase[j] = static_cast<const char*>(p.ws.pm);
+            fstride[j] = (int64_t)C::NPM * FB;
+            foff[j] = (f - C::F_P) * FB;
+        } else {
+            fbase[j] = reinterpret_cast<const char*>(p.ws.gam);
+            fstride[j] = (int64_t)DK * sizeof(float);
+            foff[j] = -16 * lane + 16 * (lane % (DK / 4));   // dk floats, repeated
+        }
+        foff[j] += 16 * lane;
+    }
+    auto stage = [&](int c, int b) {
+        const int64_t wsb = (int64_t)(cbase + c) * H + h;
+        char* buf = smem + b * C::BUF;
+#pragma unroll
+        for (int j = 0; j < C::FPW; ++j) {
+            const int f = wave + NW * j < C::NF ? wave + NW * j : C::NF - 1;
+            lds_dma16(fbase[j] + wsb * fstride[j] + foff[j], buf + f * 1024);
+        }
+    };
+    auto frag = [&](const char* buf, int f) -> Frag {
+        return *reinterpret_cast<const Frag*>(buf + f * 1024 + 16 * lane);
+    };
+    // U^T and z of the wave's columns, one chunk ahead in registers
+    T4 ut[NTT][NVT], zz[NTT][NVT];
+    auto load_uz = [&](int c) {
+        const int64_t wsb = (int64_t)(cbase + c) * H + h;
+        const T* UT = static_cast<const T*>(p.ws.ut) + wsb * (DV * CH);
+#pragma unroll
+        for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
+                const int vtg = ident ? 0 : vcol0 / 16 + vt;   // value tile of the U^T block
+                ut[ta][vt] = *reinterpret_cast<const T4*>(UT + ((vtg * NTT + ta) * 64 + lane) * 4);
+            }
+        if (!C::AUG && gz) {
+            const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta) {
+                const int t = 16 * ta + l16 < nv ? 16 * ta + l16 : nv - 1;
+                const int64_t row = ((t0 + (int64_t)c * CH + t) * H + h) * DV;
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+                    zz[ta][vt] = *reinterpret_cast<const T4*>(gz + row + vcol0 + 16 * vt + 4 * g4);
+            }
+        }
+    };
+
+    if (nch > 0) {
+        stage(0, 0);
+        load_uz(0);
+    }
+    for (int c = 0; c < nch; ++c) {
+        const char* buf = smem + (c % C::NBUF) * C::BUF;
+        T4 utc[NTT][NVT], zzc[NTT][NVT];
+#pragma unroll
+        for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
+                utc[ta][vt] = ut[ta][vt];
+                zzc[ta][vt] = zz[ta][vt];
+            }
+        const int nvalid = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+        if constexpr (C::NBUF == 2) {
+            barrier_keep_loads();                          // buffer (c+1)%2 is free
+            const int cn = c + 1 < nch ? c + 1 : c;        // the last chunk refetches its own
+            stage(cn, (c + 1) & 1);
+            wait_vmcnt<C::FPW>();                          // this wave's part of chunk c
+            load_uz(cn);
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_keep_loads();                              // every wave's part of chunk c
+
+        // Delta = U + Wn S
+        Frag sf[NKC][NVT];
+#pragma unroll
+        for (int s = 0; s < NKC; ++s)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+                sf[s][vt] = K::from_acc(S[s * TPB][vt], S[s * TPB + TPB - 1][vt]);
+        f32x4_t D[NTT][NVT];
+#pragma unroll
+        for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = ident ? f32x4_t{0.f, 0.f, 0.f, 0.f} : to_f32x4(utc[ta][vt]);
+#pragma unroll
+        for (int s = 0; s < NKC; ++s)
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta) {
+                const Frag wf = frag(buf, C::F_W + s * NTT + ta);
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(wf, sf[s][vt], D[ta][vt]);
+            }
+        Frag df[NKT][NVT];
+#pragma unroll
+        for (int u = 0; u < NKT; ++u)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
+                const int t1 = u * TPB + TPB - 1;
+                df[u][vt] = K::from_acc(D[u * TPB][vt], t1 < NTT ? D[t1 < NTT ? t1 : 0][vt]
+                                                                 : f32x4_t{0.f, 0.f, 0.f, 0.f});
+            }
+
+        // S <- gam * S + Kh^T Delta
+        const float* gbuf = reinterpret_cast<const float*>(buf + C::F_G * 1024);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(gbuf + 16 * ct + 4 * g4);
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) S[ct][vt] *= gm;
+#pragma unroll
+            for (int u = 0; u < NKT; ++u) {
+                const Frag kf = frag(buf, C::F_K + ct * NKT + u);
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) S[ct][vt] = K::mma(kf, df[u][vt], S[ct][vt]);
+            }
+        }
+
+        if constexpr (!C::AUG) {
+            // O^T = S_old^T Qt^T + Delta^T Pm^T, then the gate; stores last
+            f32x4_t O[NVT][NTT];
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta) O[vt][ta] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKC; ++s)
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta) {
+                    const Frag qf = frag(buf, C::F_Q + s * NTT + ta);
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) O[vt][ta] = K::mma(sf[s][vt], qf, O[vt][ta]);
+                }
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                for (int u = 0; u < NKT; ++u)
+                    if (u * KB <= 16 * ta + 15) {
+                        const Frag pf = frag(buf, C::F_P + pm_frag_index(ta, u, NKT, KB));
+#pragma unroll
+                        for (int vt = 0; vt < NVT; ++vt) O[vt][ta] = K::mma(df[u][vt], pf, O[vt][ta]);
+                    }
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) {
+                    f32x4_t o = O[vt][ta];
+                    if (gz) {
+                        const f32x4_t zf = to_f32x4(zzc[ta][vt]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[i] *= sigmoid(zf[i]);
+                    }
+                    O[vt][ta] = o;
+                }
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta) {
+                const int t = 16 * ta + l16;
+                if (t < nvalid) {
+                    const int64_t row = ((t0 + (int64_t)c * CH + t) * H + h) * DV;
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) st4s(gy + row + vcol0 + 16 * vt + 4 * g4, O[vt][ta]);
+                }
+            }
+        }
+        if constexpr (C::NBUF == 1) {
+            barrier_keep_loads();                          // buffer free for the next chunk
+            if (c + 1 < nch) {
+                stage(c + 1, 0);
+                load_uz(c + 1);
+            }
+        }
+    }
+
+    // ---- final state ---------------------------------------------------------
+    if (p.sfin && n >= p.final_seq_lo) {
+        const int64_t sb = ((int64_t)(n - p.final_seq_lo) * H + h) * DK * (int64_t)dvt;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
+                const int col = colw + 16 * vt + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p.sfin[sb + (int64_t)(16 * ct + 4 * g4 + i) * dvt + col] = S[ct][vt][i];
+            }
+    }
+}
+
+// Chunk offsets of packed sequences and a longest-first order of them.
+__global__ __launch_bounds__(256) void varlen_plan_kernel(int N, const int32_t* __restrict__ cu, int CH,
+                                                          int32_t* __restrict__ chunk_off,
+                                                          int32_t* __restrict__ order) {
+    __shared__ int buf[256];
+    const int tid = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < N; base += 256) {
+        const int i = base + tid;
+        int x = 0;
+        if (i < N) {
+            const int l = cu[i + 1] - cu[i];
+            x = l > 0 ? (l + CH - 1) / CH : 0;
+        }
+        buf[tid] = x;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int y = tid >= d ? buf[tid - d] : 0;
+            __syncthreads();
+            buf[tid] += y;
+            __syncthreads();
+        }
+        if (i < N) chunk_off[i] = carry + buf[tid] - x;
+        carry += buf[255];
+        __syncthreads();
+    }
+    if (tid == 0) chunk_off[N] = carry;
+    for (int i = tid; i < N; i += 256) {
+        int rank = i;
+        if (N <= 1024) {
+            const int li = cu[i + 1] - cu[i];
+            rank = 0;
+            for (int j = 0; j < N; ++j) {
+                const int lj = cu[j + 1] - cu[j];
+                rank += (lj > li) || (lj == li && j < i);
+            }
+        }
+        order[rank] = i;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <class C>
+static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order) {
+    StateParams p;
+    p.chunk_cap = (int)a.chunk_cap;
+    p.H = a.H;
+    p.num_seqs = a.num_seqs;
+    p.nchains = a.num_seqs * a.H;
+    p.dvt = C::AUG ? a.dk + a.dv : a.dv;
+    p.nvg = p.dvt / C::CW;
+    p.final_seq_lo = a.final_seq_lo;
+    p.cps = (int)((a.seg_len + a.chunk - 1) / a.chunk);
+    p.T_total = a.T_total;
+    p.seg_len = a.seg_len;
+    p.cu_seqlens = a.cu_seqlens;
+    p.chunk_off = chunk_off;
+    p.order = order;
+    p.z = a.z;
+    p.y = a.y;
+    p.s0 = a.initial_state;
+    p.sfin = a.final_state;
+    p.ws = a.bufs;
+    if (p.nchains == 0) return hipSuccess;
+    auto kern = chunk_state_kernel<C>;
+    if (C::BYTES > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
+        if (e != hipSuccess) return e;
+    }
+    const long nblk = (long)((p.nchains + 7) / 8) * 8 * p.nvg;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NTHR), C::BYTES, (hipStream_t)a.stream, p);
+    return hipGetLastError();
+}
+
+template <class E, int DK, int CH, int MODE>
+static hipError_t launch_state_nvt(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
+    if (a.nvt == 1) return launch_state_cfg<StCfg<E, DK, DK, CH, 1, MODE>>(a, co, ord);
+    return launch_state_cfg<StCfg<E, DK, DK, CH, 2, MODE>>(a, co, ord);
+}
+
+template <class E, int DK, int CH>
+static hipError_t launch_state_mode(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
+    switch (a.mode) {
+        case kModeSeq: return launch_state_nvt<E, DK, CH, kModeSeq>(a, co, ord);
+        case kModeVarlen: return launch_state_nvt<E, DK, CH, kModeVarlen>(a, co, ord);
+        case kModePairs: return launch_state_nvt<E, DK, CH, kModePairs>(a, co, ord);
+        default: return launch_state_nvt<E, DK, CH, kModeFinish>(a, co, ord);
+    }
+}
+
+template <class E, int DK>
+static hipError_t launch_state_dk(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
+    if (a.chunk == 64) return launch_state_mode<E, DK, 64>(a, co, ord);
+    return launch_state_mode<E, DK, 16>(a, co, ord);
+}
+
+hipError_t launch_chunk_state(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order) {
+    if (a.dtype == 0)
+        return a.dk == 128 ? launch_state_dk<BF16, 128>(a, chunk_off, order)
+                           : launch_state_dk<BF16, 64>(a, chunk_off, order);
+    return a.dk == 128 ? launch_state_dk<F32, 128>(a, chunk_off, order)
+                       : launch_state_dk<F32, 64>(a, chunk_off, order);
+}
+
+hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int chunk, int32_t* chunk_off,
+                              int32_t* order, void* stream) {
+    hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, num_seqs, cu_seqlens,
+                       chunk, chunk_off, order);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "twopass.h"
+
 namespace kda {
 
 struct DecodeArgs {
@@ -19,7 +21,16 @@ struct DecodeArgs {
     void* stream;
 };
 
-struct PrefillArgs {
+// Modes of the state scan.  Distinct instantiations keep the profiler
+// statistics of the different call sites apart.
+enum ScanMode : int {
+    kModeSeq = 0,     // one sequence, or equal segments (no offsets array)
+    kModeVarlen = 1,  // packed sequences given by cu_seqlens
+    kModePairs = 2,   // KCP segment pairs: augmented state [I | 0], values [0 | v], no outputs
+    kModeFinish = 3,  // KCP outputs of every segment from its entering state
+};
+
+struct TwoPassArgs {
     int dtype;  // 0 bf16, 1 fp32
     int H, dk, dv, chunk;
     float scale;
@@ -31,19 +42,28 @@ struct PrefillArgs {
     const float *g, *beta;
     const void* z;
     const float* initial_state;  // [num_seqs, H, dk, dv] or NULL
-    float* final_state;          // see final_seq_lo and mode 2
+    float* final_state;          // see final_seq_lo; mode 2: [num_seqs, H, dk, dk + dv]
     int final_seq_lo;            // only sequences n >= final_seq_lo write final_state[n - lo]
     void* y;                     // NULL only in mode 2
-    int mode;                    // 0 one sequence / equal segments, 1 varlen (cu_seqlens),
-                                 // 2 KCP pairs: value width dk + dv, identity start on the first
-                                 //   dk columns, final_state gets [num_seqs, H, dk, dk + dv],
-                                 // 3 KCP segment outputs
-    int vs;                      // value-slice width per workgroup (0 = library choice)
+    int mode;                    // ScanMode
+    int nvt;                     // 16-column value tiles per scan wave (1 or 2)
+    TwoPassBufs bufs;            // chunk products (workspace)
+    int64_t chunk_cap;           // chunks the workspace arrays hold
     void* stream;
 };
 
 bool prefill_supported(int dtype, int dk, int dv, int chunk);
-hipError_t launch_prefill(const PrefillArgs& a);
+
+// Chunk offsets ([num_seqs + 1]) and a longest-first order ([num_seqs]) of
+// packed sequences.
+hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int chunk, int32_t* chunk_off,
+                              int32_t* order, void* stream);
+// Products of every (chunk, head) into a.bufs; nchunks bounds the chunk count
+// (chunk_off, when given, holds the exact offsets).
+hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks);
+// The sequential pass over the chunks of every (sequence, head).
+hipError_t launch_chunk_state(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order);
+
 hipError_t launch_decode(const DecodeArgs& a);
 
 // KCP phase 2: starts[s] = M_{s-1} starts[s-1] + Sloc_{s-1}, starts[0] = S0.

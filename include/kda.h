@@ -28,8 +28,10 @@
  *   g           [T_total, H, dk]       fp32, natural log of the decay alpha
  *   beta        [T_total, H]           fp32
  *   states      [N, H, dk, dv]         fp32 (N = sequences or requests)
- * Pointers to bf16 data must be 4-byte aligned, fp32 data 8-byte aligned,
- * states 16-byte aligned.
+ * Alignment: kda_chunk_fwd and kda_kcp_scan move q, k, v, z and y in runs of
+ * four elements, so those need 8 bytes (bf16) or 16 bytes (fp32), and g 16
+ * bytes; kda_decode_step needs 4 bytes (bf16) or 8 bytes (fp32) and g 8.
+ * States are 16-byte aligned, workspaces 256-byte aligned.
  *
  * Preconditions (documented, not checked on the hot path):
  *   - q and k are L2-normalised per (token, head): page "Exercices",
@@ -41,8 +43,7 @@
  *   - cu_seqlens is non-decreasing, cu_seqlens[0] = 0,
  *     cu_seqlens[num_seqs] = T_total.
  *
- * Supported sizes: (dk, dv) in {(64, 64), (128, 128)}; chunk in {16, 64},
- * except fp32 inputs with dk = 128, which support chunk = 16 only.
+ * Supported sizes: (dk, dv) in {(64, 64), (128, 128)}; chunk in {16, 64}.
  * Anything else returns KDA_ERR_UNSUPPORTED.
  */
 #ifndef LIBKDA_KDA_H
@@ -94,20 +95,42 @@ const char* kda_status_string(kda_status status);
  *   final_state     fp32 [num_seqs, H, dk, dv] or NULL (not written).  May
  *                   alias initial_state (each state is read before written).
  *   y               output [T_total, H, dv] in dtype dt; must not alias inputs.
+ *   workspace       device buffer of at least kda_chunk_fwd_workspace_size
+ *                   bytes for the same (dt, H, dk, dv, chunk, num_seqs,
+ *                   T_total), 256-byte aligned; overwritten.
+ *
+ * Two passes on `stream`: every (chunk, head) first forms the products of its
+ * chunk that do not involve the entering state (the gated Gram products, the
+ * inverse of the unit lower-triangular I + diag(beta) A, and the operands
+ * derived from them) into the workspace, all chunks at once; then one pass
+ * per (sequence, head) carries the state through its chunks.
  */
 kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
                          int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
                          const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const void* z, const float* initial_state,
-                         float* final_state, void* y, void* stream);
+                         float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd
+ * needs: per (chunk, head) about 3 dk C + dv C + C^2 / 2 elements of dtype dt
+ * plus dk fp32 (70.5 KiB at bf16, dk = dv = 128, C = 64), for up to
+ * T_total / chunk + num_seqs chunks.  Returns 0 for invalid or unsupported
+ * sizes.
+ */
+size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs,
+                                    int64_t T_total);
 
 /*
  * kda_kcp_workspace_size -- bytes of device workspace kda_kcp_scan needs for
- * H heads split into num_segments segments: the segment pairs
- * (M [dk x dk], Sloc [dk x dv]) and the entering states [dk x dv], all fp32.
- * Returns 0 for invalid or unsupported sizes.
+ * H heads of a T-token sequence split into num_segments segments: the segment
+ * pairs (M [dk x dk], Sloc [dk x dv]) and the entering states [dk x dv], all
+ * fp32, plus the chunk products of kda_chunk_fwd over the segments.  Returns 0
+ * for invalid or unsupported sizes.
  */
-size_t kda_kcp_workspace_size(int H, int dk, int dv, int num_segments);
+size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int64_t T,
+                              int num_segments);
 
 /*
  * kda_kcp_scan -- one long sequence of T tokens split into num_segments equal
@@ -117,7 +140,8 @@ size_t kda_kcp_workspace_size(int H, int dk, int dv, int num_segments);
  * (M2, S2) o (M1, S1) = (M2 M1, M2 S1 + S2) (page "Exercices", Niveau 3
  * Q21-Q22; page "Reproduire Kimi K3", "Le script de vérification").  Three
  * phases on `stream`: pairs of all segments in parallel, a scan of the pairs
- * giving every segment its entering state, then every segment's outputs.  The
+ * giving every segment its entering state, then every segment's outputs (the
+ * chunk products are formed once and serve the first and third phases).  The
  * result equals kda_chunk_fwd on the same sequence up to rounding.
  *
  *   T, num_segments  T >= num_segments >= 1.

@@ -93,3 +93,69 @@ def chunk_forward(q, k, v, g, beta, z=None, S0=None, C=64, scale=1.0):
         y[c0:c0 + n] = scale * O[:n]
         S = np.exp(G[-1])[:, None] * S + (kc * np.exp(G[-1] - G)).T @ Delta
     return y, S
+
+
+# ---------------------------------------------------------------------------
+# Two-pass form.  Everything in a chunk that does not involve the entering
+# state is formed first, for every chunk at once ("prep"); a sequential pass
+# then carries the state through the chunks with three products each.
+#   W  = (I + diag(beta) A)^{-1} diag(beta) (K * e^G)      [C, dk]
+#   U  = (I + diag(beta) A)^{-1} diag(beta) V              [C, dv]
+#   Qt = scale (Q * e^G)     Pm = scale P                  [C, dk], [C, C]
+#   Kh = K * e^{G_C - G]     gam = e^{G_C}                 [C, dk], [dk]
+# and per chunk, with S the entering state:
+#   Delta = U - W S,  O = Qt S + Pm Delta,  S <- gam * S + Kh^T Delta.
+# The prep side forms the gated Gram products with one reference per
+# 16-token sub-tile: row operand X_t e^{G_t - R_a(t)} (<= 1), column operand
+# K_j e^{R_b(j) - G_j} (<= e^80), and for an off-diagonal block (a, b) the
+# column factor e^{R_a - R_b} (<= 1).
+# ---------------------------------------------------------------------------
+def chunk_prep(q, k, v, g, beta, C=64, scale=1.0):
+    """Per-chunk products of one head; returns a list of dicts (one per chunk)."""
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    T, dk = k.shape
+    nt = C // 16
+    out = []
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        pad = lambda x: np.concatenate([x[c0:c0 + n], np.zeros((C - n,) + x.shape[1:])])
+        qc, kc, vc, gc, bc = pad(q), pad(k), pad(v), pad(g), pad(beta)
+        G = np.cumsum(gc, axis=0)
+        R = np.array([G[16 * a - 1] if a > 0 else np.zeros(dk) for a in range(nt)])
+        sub = np.arange(C) // 16
+        er = np.exp(G - R[sub])                      # <= 1
+        ec = np.exp(R[sub] - G)                      # <= e^{16 |g_min|}
+        Kr, Qr, Kc = kc * er, qc * er, kc * ec
+        A = np.zeros((C, C))
+        P = np.zeros((C, C))
+        for a in range(nt):
+            ta = slice(16 * a, 16 * a + 16)
+            for b in range(a + 1):
+                tb = slice(16 * b, 16 * b + 16)
+                col = Kc[tb] * np.exp(R[a] - R[b])   # factor <= 1 (1 on the diagonal)
+                A[ta, tb] = Kr[ta] @ col.T
+                P[ta, tb] = Qr[ta] @ col.T
+        A = np.tril(A, -1)
+        P = np.tril(P, 0)
+        Linv = _blocked_unit_lower_inverse(np.eye(C) + bc[:, None] * A)
+        LB = Linv * bc[None, :]
+        eG = np.exp(G)
+        out.append(dict(W=LB @ (kc * eG), U=LB @ vc, Qt=scale * qc * eG, Pm=scale * P,
+                        Kh=kc * np.exp(G[-1] - G), gam=np.exp(G[-1]), n=n))
+    return out
+
+
+def state_scan(prep, dv, z=None, S0=None):
+    """Sequential pass over prep's chunks; returns (y, S_T)."""
+    dk = prep[0]["W"].shape[1] if prep else 0
+    S = np.zeros((dk, dv)) if S0 is None else _f64(S0).copy()
+    ys = []
+    for ch in prep:
+        Delta = ch["U"] - ch["W"] @ S
+        O = ch["Qt"] @ S + ch["Pm"] @ Delta
+        S = ch["gam"][:, None] * S + ch["Kh"].T @ Delta
+        ys.append(O[:ch["n"]])
+    y = np.concatenate(ys) if ys else np.zeros((0, dv))
+    if z is not None:
+        y = y / (1.0 + np.exp(-_f64(z)))
+    return y, S

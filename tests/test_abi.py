@@ -31,16 +31,16 @@ def test_header_declares_what_the_binding_knows():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert L.kda_version() == 10000
+    assert L.kda_version() == 10100
     assert kda.kda_status_string(0) == "KDA_OK"
     assert kda.kda_status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
     assert kda.kda_status_string(99) == "KDA_ERR_UNKNOWN"
 
 
 def _fwd(L, dt=BF16, H=2, dk=128, dv=128, chunk=64, N=1, T=64, cu=None, q=P, k=P, v=P, g=P,
-         beta=P, z=None, s0=None, sf=None, y=P):
+         beta=P, z=None, s0=None, sf=None, y=P, ws=P, wsb=1 << 40):
     return L.kda_chunk_fwd(dt, H, dk, dv, chunk, 1.0, N, T, cu, q, k, v, g, beta, z, s0, sf, y,
-                           None)
+                           ws, wsb, None)
 
 
 def test_chunk_fwd_rejects_bad_arguments(L):
@@ -52,26 +52,70 @@ def test_chunk_fwd_rejects_bad_arguments(L):
     assert _fwd(L, q=None) == INVALID
     assert _fwd(L, y=None) == INVALID
     assert _fwd(L, beta=None) == INVALID
-    assert _fwd(L, q=ctypes.c_void_p((1 << 20) + 2)) == INVALID  # bf16 pairs need 4-byte alignment
-    assert _fwd(L, g=ctypes.c_void_p((1 << 20) + 4)) == INVALID  # fp32 pairs need 8-byte alignment
+    assert _fwd(L, q=ctypes.c_void_p((1 << 20) + 4)) == INVALID  # bf16 runs of 4 need 8-byte alignment
+    assert _fwd(L, dt=F32, v=ctypes.c_void_p((1 << 20) + 8)) == INVALID  # fp32 runs of 4: 16 bytes
+    assert _fwd(L, g=ctypes.c_void_p((1 << 20) + 8)) == INVALID  # g in runs of 4: 16 bytes
     assert _fwd(L, s0=ctypes.c_void_p((1 << 20) + 8)) == INVALID # states need 16-byte alignment
+    assert _fwd(L, ws=None) == INVALID
+    assert _fwd(L, ws=ctypes.c_void_p((1 << 20) + 128)) == INVALID  # workspace: 256 bytes
+    need = L.kda_chunk_fwd_workspace_size(BF16, 2, 128, 128, 64, 1, 64)
+    assert _fwd(L, wsb=need - 1) == WS_SMALL
 
 
 def test_chunk_fwd_rejects_unsupported_shapes(L):
     assert _fwd(L, dk=96, dv=96) == UNSUPPORTED
     assert _fwd(L, dk=128, dv=64) == UNSUPPORTED
     assert _fwd(L, chunk=32) == UNSUPPORTED
-    assert _fwd(L, dt=F32, dk=128, dv=128, chunk=64) == UNSUPPORTED
+
+
+def _pm_frags(C, kb):
+    """Fragments (16 tokens x one k-block of kb tokens) of P on or below its diagonal."""
+    return sum(1 for ta in range(C // 16) for u in range(-(-C // kb)) if u * kb <= 16 * ta + 15)
+
+
+def _chunk_block_bytes(elt, dk, dv, C, CP):
+    """Bytes of the chunk products of one (chunk, head): Wn, Qt [C, dk], Kh^T [dk, CP],
+    U^T [dv, C] in the input dtype, the 1 KiB fragments of Pm on or below the
+    diagonal, and gam [dk] fp32."""
+    kb = 32 if elt == 2 else 16
+    return (2 * C * dk + dk * CP + dv * C) * elt + _pm_frags(C, kb) * 1024 + dk * 4
+
+
+def _rnd(x):
+    return (x + 255) // 256 * 256
+
+
+def test_chunk_fwd_workspace_size(L):
+    H, dk, dv, C, N, T = 96, 128, 128, 64, 1, 8192
+    nb = (T // C + N) * H
+    parts = [N + 1, N]   # chunk offsets and order, int32
+    parts = [_rnd(4 * x) for x in parts]
+    for n in (C * dk, C * dk, dk * C, _pm_frags(C, 32) * 512, dv * C):
+        parts.append(_rnd(nb * n * 2))
+    parts.append(_rnd(nb * dk * 4))
+    assert L.kda_chunk_fwd_workspace_size(BF16, H, dk, dv, C, N, T) == sum(parts)
+    # per (chunk, head) 70.5 KiB at this shape: 6 of the 8 fragments of P are stored
+    assert _pm_frags(64, 32) == 6
+    assert _chunk_block_bytes(2, dk, dv, C, C) == 72192
+    # bf16 k-blocks are 32 tokens: chunk 16 pads K^T and P to 32 columns
+    small = L.kda_chunk_fwd_workspace_size(BF16, 1, 64, 64, 16, 1, 16)
+    assert small >= 2 * _chunk_block_bytes(2, 64, 64, 16, 32)
+    assert L.kda_chunk_fwd_workspace_size(BF16, H, 96, 96, C, N, T) == 0
+    assert L.kda_chunk_fwd_workspace_size(BF16, 0, dk, dv, C, N, T) == 0
+    assert L.kda_chunk_fwd_workspace_size(BF16, H, dk, dv, 32, N, T) == 0
 
 
 def test_kcp_workspace_size(L):
-    H, dk, dv, S = 4, 128, 128, 256
+    H, dk, dv, S, T, C = 4, 128, 128, 256, 1 << 20, 64
     pairs = S * H * dk * (dk + dv) * 4
     starts = S * H * dk * dv * 4
-    assert L.kda_kcp_workspace_size(H, dk, dv, S) == pairs + starts
-    assert L.kda_kcp_workspace_size(H, 96, 96, S) == 0
-    assert L.kda_kcp_workspace_size(0, dk, dv, S) == 0
-    assert L.kda_kcp_workspace_size(H, dk, dv, 0) == 0
+    need = L.kda_kcp_workspace_size(BF16, H, dk, dv, C, T, S)
+    nb = S * (T // S // C) * H
+    assert need >= pairs + starts + nb * _chunk_block_bytes(2, dk, dv, C, C)
+    assert need <= pairs + starts + nb * _chunk_block_bytes(2, dk, dv, C, C) + 16 * 256 + 8 * S
+    assert L.kda_kcp_workspace_size(BF16, H, 96, 96, C, T, S) == 0
+    assert L.kda_kcp_workspace_size(BF16, 0, dk, dv, C, T, S) == 0
+    assert L.kda_kcp_workspace_size(BF16, H, dk, dv, C, T, 0) == 0
 
 
 def _kcp(L, T=4096, S=4, ws=P, wsb=1 << 40, dk=128, chunk=64, dt=BF16, y=P):
@@ -87,7 +131,7 @@ def test_kcp_rejects_bad_arguments(L):
     assert _kcp(L, y=None) == INVALID
     assert _kcp(L, dk=96) == UNSUPPORTED
     assert _kcp(L, chunk=8) == UNSUPPORTED
-    need = L.kda_kcp_workspace_size(2, 128, 128, 4)
+    need = L.kda_kcp_workspace_size(BF16, 2, 128, 128, 64, 4096, 4)
     assert _kcp(L, wsb=need - 1) == WS_SMALL
 
 

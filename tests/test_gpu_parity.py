@@ -112,12 +112,13 @@ def test_prefill_fp32_d64(kda, chunk, stress):
     assert_parity(f"fp32 d64 c{chunk} {stress}", inp, y, fs, yo, so, TOL["f32"])
 
 
+@pytest.mark.parametrize("chunk", [16, 64])
 @pytest.mark.parametrize("stress", [None, "chunk"])
-def test_prefill_fp32_d128_chunk16(kda, stress):
+def test_prefill_fp32_d128(kda, chunk, stress):
     inp = kda_inputs.make_workload(1, stress, lens=[197], H=2, dtype="f32", s0_std=0.05)
-    y, fs = run_prefill(kda, inp, chunk=16)
+    y, fs = run_prefill(kda, inp, chunk=chunk)
     yo, so = oracle_prefill(inp)
-    assert_parity(f"fp32 d128 c16 {stress}", inp, y, fs, yo, so, TOL["f32"])
+    assert_parity(f"fp32 d128 c{chunk} {stress}", inp, y, fs, yo, so, TOL["f32"])
 
 
 @pytest.mark.parametrize("chunk", [64, 16])
@@ -145,6 +146,26 @@ def test_prefill_varlen_with_ragged_and_empty_sequences(kda):
     assert_parity("varlen ragged", inp, y, fs, yo, so, TOL["bf16"])
     # the empty sequence passes its initial state through unchanged
     np.testing.assert_array_equal(fs[4].numpy(), inp.S0[4].numpy())
+
+
+def test_prefill_varlen_many_short_sequences(kda):
+    """More than 1024 packed sequences (no longest-first reordering), lengths 0..40."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 41, 1100).tolist()
+    inp = kda_inputs.make_prefill(lens, 1, 64, 64, "bf16", True, 0.05, 78, 8.0, 4.0)
+    y, fs = run_prefill(kda, inp, chunk=16)
+    yo, so = oracle_prefill(inp)
+    assert_parity("varlen 1100 short", inp, y, fs, yo, so, TOL["bf16"])
+
+
+def test_prefill_many_chains_wide_scan_waves(kda):
+    """Enough (sequence, head) chains that each scan wave takes 32 state columns."""
+    rng = np.random.default_rng(6)
+    lens = rng.integers(1, 200, 16).tolist()
+    inp = kda_inputs.make_prefill(lens, 64, 64, 64, "bf16", True, 0.05, 79, 8.0, 4.0)
+    y, fs = run_prefill(kda, inp, chunk=64)
+    yo, so = oracle_prefill(inp)
+    assert_parity("varlen 1024 chains", inp, y, fs, yo, so, TOL["bf16"])
 
 
 def test_prefill_varlen_workload_shape_reduced(kda):
@@ -225,7 +246,8 @@ def test_prefill_final_state_may_alias_initial_state(kda):
 
 
 # ---------------------------------------------------------------- KCP
-@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 64, 16), ("bf16", 64, 64)])
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 64, 16), ("bf16", 64, 64),
+                                           ("f32", 128, 64), ("bf16", 128, 16)])
 def test_kcp_scan_matches_sequential_oracle(kda, dtype, d, chunk):
     inp = kda_inputs.make_workload(3, "segment", lens=[4096], H=2, dk=d, dv=d, dtype=dtype,
                                    s0_std=0.05, gated=True)
