@@ -15,7 +15,7 @@
 //     column factor e^{R_a - R_b} <= 1, applied while loading the fragment.
 //  3. L = I + diag(beta) A is unit lower triangular; its inverse is blocked:
 //     16 x 16 diagonal blocks by forward substitution, then off-diagonal
-//     blocks level by level, X_ab = -X_aa sum_{b<=c<a} L_ac X_cb (fp32).
+//     blocks level by level, X_ab = -X_aa sum_{b<=c<a} L_ac X_cb (fp32 MFMA).
 //  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA.
 // Qt, Kh and gam leave straight from the decay phase; the tiles of W, U and
 // P leave as they are produced.
@@ -62,7 +62,6 @@ struct PrepCfg {
     static constexpr size_t SZ_X2 = 2 * SZ_KVT + SZ_LB;                // after the Gram
     static constexpr size_t O_KR = 0, O_QR = SZ_TAB, O_KC = 2 * SZ_TAB;
     static constexpr size_t O_KTT = 0, O_VTT = SZ_KVT, O_LB = 2 * SZ_KVT;
-    static constexpr size_t O_M = O_LB;  // level scratch, before L^{-1} diag(beta) is written
     static constexpr size_t SZ_X = al(SZ_X1 > SZ_X2 ? SZ_X1 : SZ_X2);
     static constexpr size_t O_L = SZ_X;                         // blocks of beta A
     static constexpr size_t O_Z = O_L + (size_t)NPAIR * BLK * 4;  // blocks of L^{-1}
@@ -70,7 +69,6 @@ struct PrepCfg {
     static constexpr size_t O_D = O_Z + (size_t)NPAIR * BLK * 4;   // e^{R_a - R_b}, a > b
     static constexpr size_t O_BETA = O_D + (size_t)(ND > 0 ? ND : 1) * DK * 4;
     static constexpr size_t BYTES = O_BETA + (size_t)CH * 4;
-    static_assert((size_t)(NT > 1 ? NT - 1 : 1) * BLK * 4 <= SZ_LB, "level scratch");
     static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
@@ -104,13 +102,13 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
     T* sKtT = reinterpret_cast<T*>(smem + C::O_KTT);
     T* sVtT = reinterpret_cast<T*>(smem + C::O_VTT);
     T* sLB = reinterpret_cast<T*>(smem + C::O_LB);
-    float* sM = reinterpret_cast<float*>(smem + C::O_M);
     float* sL = reinterpret_cast<float*>(smem + C::O_L);
     float* sZ = reinterpret_cast<float*>(smem + C::O_Z);
     float* sD = reinterpret_cast<float*>(smem + C::O_D);
     float* sBeta = reinterpret_cast<float*>(smem + C::O_BETA);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l16 = lane & 15, g4 = lane >> 4;
     const int H = p.H;
     const int64_t wsb = blockIdx.x;  // (chunk, head) block of the workspace
@@ -293,14 +291,24 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
         const int b = task - a * (a + 1) / 2;
         const float* dsc = sD + (a > b ? (a * (a - 1) / 2 + b) : 0) * DK;
         f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int kk = 0; kk < DK; kk += E::KSTEP) {
-            const typename E::Frag fc = a > b ? lds_frag_scaled<E>(sKc, LK, 16 * b, kk, lane, dsc)
-                                              : lds_frag<E>(sKc, LK, 16 * b, kk, lane);
-            const typename E::Frag fr = lds_frag<E>(sKr, LK, 16 * a, kk, lane);
-            const typename E::Frag fq = lds_frag<E>(sQr, LK, 16 * a, kk, lane);
-            accA = E::mma(fr, fc, accA);  // A[t][j]
-            accP = E::mma(fc, fq, accP);  // P^T[j][t]
+        // all fragments of the task first, then the products
+        constexpr int NKS = DK / E::KSTEP;
+        constexpr int UNR = NKS < 4 ? NKS : 4;
+        for (int k0 = 0; k0 < NKS; k0 += UNR) {
+            typename E::Frag fc[UNR], fr[UNR], fq[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int kk = (k0 + u) * E::KSTEP;
+                fc[u] = a > b ? lds_frag_scaled<E>(sKc, LK, 16 * b, kk, lane, dsc)
+                              : lds_frag<E>(sKc, LK, 16 * b, kk, lane);
+                fr[u] = lds_frag<E>(sKr, LK, 16 * a, kk, lane);
+                fq[u] = lds_frag<E>(sQr, LK, 16 * a, kk, lane);
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                accA = E::mma(fr[u], fc[u], accA);  // A[t][j]
+                accP = E::mma(fc[u], fq[u], accP);  // P^T[j][t]
+            }
         }
         // beta_t A[t][j] (strictly lower): lane holds rows 16a+4g4+i, column 16b+l16
         float* Lb = sL + pair_index(a, b) * BLK;
@@ -361,27 +369,30 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
         }
     }
     __syncthreads();
+    // off-diagonal blocks, level l = a - b: wave b forms M = sum_{b<=c<a} L_ac X_cb
+    // and X_ab = -X_aa M with fp32 MFMAs (16x16x4, four per 16-wide reduction);
+    // M stays in the accumulator and feeds the second product directly, MFMA i
+    // taking row 4 g + i of it (the reduction order of the accumulator layout)
     for (int l = 1; l < NT; ++l) {
-        const int nb = NT - l;
-        for (int idx = tid; idx < nb * 256; idx += NTHR) {
-            const int b = idx >> 8, r = (idx >> 4) & 15, col = idx & 15, a = b + l;
-            float s = 0.f;
+        const int b = wave, a = b + l;
+        if (b < NT - l) {
+            f32x4_t m = {0.f, 0.f, 0.f, 0.f};
             for (int c = b; c < a; ++c) {
-                const float* La = sL + pair_index(a, c) * BLK + r * 17;
-                const float* Zc = sZ + pair_index(c, b) * BLK + col;
+                const float* La = sL + pair_index(a, c) * BLK;
+                const float* Zc = sZ + pair_index(c, b) * BLK;
 #pragma unroll
-                for (int m = 0; m < 16; ++m) s += La[m] * Zc[m * 17];
+                for (int ks = 0; ks < 4; ++ks)
+                    m = __builtin_amdgcn_mfma_f32_16x16x4f32(La[l16 * 17 + 4 * ks + g4], Zc[(4 * ks + g4) * 17 + l16],
+                                                             m, 0, 0, 0);
             }
-            sM[b * BLK + r * 17 + col] = s;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < nb * 256; idx += NTHR) {
-            const int b = idx >> 8, r = (idx >> 4) & 15, col = idx & 15, a = b + l;
-            const float* Za = sZ + pair_index(a, a) * BLK + r * 17;
-            float s = 0.f;
+            const float* Za = sZ + pair_index(a, a) * BLK;
+            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 16; ++m) s += Za[m] * sM[b * BLK + m * 17 + col];
-            sZ[pair_index(a, b) * BLK + r * 17 + col] = -s;
+            for (int i = 0; i < 4; ++i)
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(Za[l16 * 17 + 4 * g4 + i], m[i], x, 0, 0, 0);
+            float* Zab = sZ + pair_index(a, b) * BLK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Zab[(4 * g4 + i) * 17 + l16] = -x[i];
         }
         __syncthreads();
     }
