@@ -30,9 +30,17 @@ COMMON = [
 ]
 
 
+# MFMA results in ordinary VGPRs: the scan and preparation kernels scale and
+# convert accumulators with VALU instructions, which cannot read AGPRs
+PER_SOURCE = {
+    "chunk_state.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "chunk_prep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_SOURCE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

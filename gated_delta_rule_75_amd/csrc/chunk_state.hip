@@ -24,6 +24,8 @@
 //
 // The workgroups of one chain take ids with equal residue mod 8, which places
 // them on one XCD, so they share the chunk operands through its L2.
+#include <type_traits>
+
 #include "launch.h"
 #include "twopass.h"
 
@@ -79,10 +81,11 @@ __device__ __forceinline__ f32x4_t to_f32x4(bf16x4_t v) {
     return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ __forceinline__ f32x4_t to_f32x4(f32x4_t v) { return v; }
-__device__ __forceinline__ void st4s(__bf16* p, f32x4_t x) {
-    *reinterpret_cast<bf16x4_t*>(p) = bf16x4_t{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+template <typename T> __device__ __forceinline__ typename VecT4<T>::type from_f32x4(f32x4_t x);
+template <> __device__ __forceinline__ bf16x4_t from_f32x4<__bf16>(f32x4_t x) {
+    return bf16x4_t{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
 }
-__device__ __forceinline__ void st4s(float* p, f32x4_t x) { *reinterpret_cast<f32x4_t*>(p) = x; }
+template <> __device__ __forceinline__ f32x4_t from_f32x4<float>(f32x4_t x) { return x; }
 
 // 16 bytes per lane from global memory straight into LDS: lane i writes
 // lds + 16 i.  (A __device__ wrapper: the builtin written directly in a
@@ -213,15 +216,19 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
         foff[j] += 16 * lane;
     }
-    auto stage = [&](int c, int b) {
+    // fragments [J0, J1) of this wave's share of chunk c into LDS buffer b
+    auto stage = [&](int c, int b, auto J0, auto J1) {
         const int64_t wsb = (int64_t)(cbase + c) * H + h;
         char* buf = smem + b * C::BUF;
 #pragma unroll
-        for (int j = 0; j < C::FPW; ++j) {
+        for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
             const int f = wave + NW * j < C::NF ? wave + NW * j : C::NF - 1;
             lds_dma16(fbase[j] + wsb * fstride[j] + foff[j], buf + f * 1024);
         }
     };
+    using J_0 = std::integral_constant<int, 0>;
+    using J_H = std::integral_constant<int, C::FPW / 2>;
+    using J_E = std::integral_constant<int, C::FPW>;
     auto frag = [&](const char* buf, int f) -> Frag {
         return *reinterpret_cast<const Frag*>(buf + f * 1024 + 16 * lane);
     };
@@ -250,12 +257,34 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
     };
 
+    // outputs of the previous chunk, stored in the middle of the next one so
+    // that the wait at the top of a chunk never waits for them
+    using T4s = T4;
+    T4s yd[NTT][NVT];
+    int64_t yd_row0 = 0;
+    int yd_nvalid = 0;
+    auto store_y = [&]() {
+#pragma unroll
+        for (int ta = 0; ta < NTT; ++ta) {
+            const int t = 16 * ta + l16;
+            if (t < yd_nvalid) {
+                const int64_t row = (yd_row0 + (int64_t)t * H) * DV;   // token t, head h
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+                    *reinterpret_cast<T4s*>(gy + row + vcol0 + 16 * vt + 4 * g4) = yd[ta][vt];
+            }
+        }
+    };
+
     if (nch > 0) {
-        stage(0, 0);
+        stage(0, 0, J_0{}, J_E{});
         load_uz(0);
     }
     for (int c = 0; c < nch; ++c) {
         const char* buf = smem + (c % C::NBUF) * C::BUF;
+        const int nb = (c + 1) % C::NBUF;
+        const int cn = c + 1 < nch ? c + 1 : c;   // the last chunk refetches its own (harmless)
+        wait_vmcnt<0>();                           // chunk c (and U^T, z) of this wave
         T4 utc[NTT][NVT], zzc[NTT][NVT];
 #pragma unroll
         for (int ta = 0; ta < NTT; ++ta)
@@ -265,16 +294,9 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 zzc[ta][vt] = zz[ta][vt];
             }
         const int nvalid = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
-        if constexpr (C::NBUF == 2) {
-            barrier_keep_loads();                          // buffer (c+1)%2 is free
-            const int cn = c + 1 < nch ? c + 1 : c;        // the last chunk refetches its own
-            stage(cn, (c + 1) & 1);
-            wait_vmcnt<C::FPW>();                          // this wave's part of chunk c
-            load_uz(cn);
-        } else {
-            wait_vmcnt<0>();
-        }
-        barrier_keep_loads();                              // every wave's part of chunk c
+        // every wave's part of chunk c has landed, and every wave is done with
+        // the buffer the next chunk goes to
+        barrier_keep_loads();
 
         // Delta = U + Wn S
         Frag sf[NKC][NVT];
@@ -296,6 +318,10 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
                 for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(wf, sf[s][vt], D[ta][vt]);
             }
+        if constexpr (!C::AUG) {
+            if (yd_nvalid > 0) store_y();
+        }
+        if constexpr (C::NBUF == 2) stage(cn, nb, J_0{}, J_H{});
         Frag df[NKT][NVT];
 #pragma unroll
         for (int u = 0; u < NKT; ++u)
@@ -320,9 +346,13 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 for (int vt = 0; vt < NVT; ++vt) S[ct][vt] = K::mma(kf, df[u][vt], S[ct][vt]);
             }
         }
+        if constexpr (C::NBUF == 2) {
+            stage(cn, nb, J_H{}, J_E{});
+            load_uz(cn);
+        }
 
         if constexpr (!C::AUG) {
-            // O^T = S_old^T Qt^T + Delta^T Pm^T, then the gate; stores last
+            // O^T = S_old^T Qt^T + Delta^T Pm^T, then the gate
             f32x4_t O[NVT][NTT];
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt)
@@ -355,25 +385,21 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) o[i] *= sigmoid(zf[i]);
                     }
-                    O[vt][ta] = o;
+                    yd[ta][vt] = from_f32x4<T>(o);
                 }
-#pragma unroll
-            for (int ta = 0; ta < NTT; ++ta) {
-                const int t = 16 * ta + l16;
-                if (t < nvalid) {
-                    const int64_t row = ((t0 + (int64_t)c * CH + t) * H + h) * DV;
-#pragma unroll
-                    for (int vt = 0; vt < NVT; ++vt) st4s(gy + row + vcol0 + 16 * vt + 4 * g4, O[vt][ta]);
-                }
-            }
+            yd_row0 = (t0 + (int64_t)c * CH) * H + h;
+            yd_nvalid = nvalid;
         }
         if constexpr (C::NBUF == 1) {
-            barrier_keep_loads();                          // buffer free for the next chunk
+            barrier_keep_loads();                  // buffer free for the next chunk
             if (c + 1 < nch) {
-                stage(c + 1, 0);
+                stage(c + 1, 0, J_0{}, J_E{});
                 load_uz(c + 1);
             }
         }
+    }
+    if constexpr (!C::AUG) {
+        if (yd_nvalid > 0) store_y();             // outputs of the last chunk
     }
 
     // ---- final state ---------------------------------------------------------
