@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "KDAError", "lib", "library_path", "kda_version", "kda_status_string",
-    "chunk_fwd", "chunk_fwd_workspace_size", "kcp_scan", "kcp_workspace_size", "decode_step",
+    "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_checkpointed", "kcp_scan",
+    "kcp_workspace_size", "decode_step",
     "KDA_BF16", "KDA_F32",
 ]
 
@@ -31,7 +32,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 
 # Every symbol include/kda.h declares.
 SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
-           "kda_kcp_workspace_size", "kda_kcp_scan", "kda_decode_step")
+           "kda_chunk_fwd_checkpointed", "kda_kcp_workspace_size", "kda_kcp_scan",
+           "kda_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -63,6 +65,9 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
+    L.kda_chunk_fwd_checkpointed.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, i, vp, vp, i64, vp, sz, vp]
+    L.kda_chunk_fwd_checkpointed.restype = i
     L.kda_kcp_workspace_size.argtypes = [i, i, i, i, i, i64, i]
     L.kda_kcp_workspace_size.restype = sz
     L.kda_kcp_scan.argtypes = [i, i, i, i, i, f, i64, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -173,6 +178,33 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=Non
                              workspace.numel() * workspace.element_size(), _stream(dev))
     _check("kda_chunk_fwd", st)
     return y, final_state
+
+
+def chunk_fwd_checkpointed(q, k, v, g, beta, interval: int, cu_seqlens=None, z=None,
+                           initial_state=None, chunk: int = 64, scale: float = 1.0):
+    """Prefill that also saves the state every `interval` tokens of each sequence.
+    Returns (y, final_state, checkpoints [T // interval, H, dk, dv] (rows past
+    offsets[-1] unused), offsets int32 [N + 1] (device))."""
+    dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state)
+    N = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
+    fs = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    cap = max(T // interval, 1)
+    ck = torch.empty(cap, H, dk, dv, dtype=torch.float32, device=dev)
+    offs = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    need = chunk_fwd_workspace_size(dt, H, dk, dv, chunk, N, T)
+    if need == 0:
+        raise KDAError("kda_chunk_fwd_workspace_size", 2)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().kda_chunk_fwd_checkpointed(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens),
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                                          _ptr(initial_state), _ptr(fs), _ptr(y), interval,
+                                          _ptr(ck), _ptr(offs), cap, _ptr(ws), need, _stream(dev))
+    _check("kda_chunk_fwd_checkpointed", st)
+    return y, fs, ck, offs
 
 
 def kcp_workspace_size(dtype: int, H: int, dk: int, dv: int, chunk: int, T: int,

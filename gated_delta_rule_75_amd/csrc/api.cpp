@@ -107,12 +107,17 @@ size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chu
     return twopass_layout(dt, H, dk, dv, chunk, num_seqs, varlen_chunks(T_total, chunk, num_seqs)).total;
 }
 
-kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
-                         int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
-                         const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const void* z, const float* initial_state,
-                         float* final_state, void* y, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_fwd, optionally saving the state every ckpt_interval tokens.
+kda_status chunk_fwd_impl(kda_dtype dt, int H, int dk, int dv, int chunk, float scale, int num_seqs,
+                          int64_t T_total, const int32_t* cu_seqlens, const void* q, const void* k,
+                          const void* v, const float* g, const float* beta, const void* z,
+                          const float* initial_state, float* final_state, void* y, int ckpt_interval,
+                          float* checkpoints, int32_t* ckpt_offsets, int64_t ckpt_capacity,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
     if (H <= 0 || num_seqs <= 0 || T_total < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARGUMENT;
@@ -122,6 +127,13 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
     if (!kda::prefill_supported((int)dt, dk, dv, chunk)) return KDA_ERR_UNSUPPORTED;
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !y)) return KDA_ERR_INVALID_ARGUMENT;
     if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+    const bool ckpt = ckpt_interval != 0;
+    if (ckpt) {
+        if (ckpt_interval < 0 || ckpt_interval % chunk != 0) return KDA_ERR_INVALID_ARGUMENT;
+        if (!ckpt_offsets || (!checkpoints && T_total >= ckpt_interval)) return KDA_ERR_INVALID_ARGUMENT;
+        if (ckpt_capacity < T_total / ckpt_interval) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned(checkpoints, 16) || !aligned(ckpt_offsets, 4)) return KDA_ERR_INVALID_ARGUMENT;
+    }
     const size_t ea = vec_align(dt);
     if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
         !aligned(y, ea) || !aligned(g, 16) || !aligned(beta, 4) || !aligned(cu_seqlens, 4) ||
@@ -156,17 +168,52 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
     a.nvt = pick_nvt((int64_t)num_seqs * H, dv);
     a.bufs = bufs_at(workspace, l);
     a.chunk_cap = varlen_chunks(T_total, chunk, num_seqs);
+    a.ckpt = ckpt ? checkpoints : nullptr;
+    a.ckpt_off = ckpt ? ckpt_offsets : nullptr;
+    a.ckpt_every = ckpt ? ckpt_interval / chunk : 1;
+    a.ckpt_cap = ckpt ? ckpt_capacity : 0;
     a.stream = stream;
     int32_t* chunk_off = nullptr;
     int32_t* order = nullptr;
     if (cu_seqlens) {
         chunk_off = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.chunk_off);
         order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.order);
-        if (kda::launch_varlen_plan(num_seqs, cu_seqlens, chunk, chunk_off, order, stream) != hipSuccess)
+    }
+    if (cu_seqlens || ckpt) {
+        if (kda::launch_varlen_plan(num_seqs, cu_seqlens, T_total, chunk, ckpt ? ckpt_interval : 0, chunk_off,
+                                    order, ckpt ? ckpt_offsets : nullptr, stream) != hipSuccess)
             return KDA_ERR_HIP;
     }
     if (kda::launch_chunk_prep(a, chunk_off, nchunks) != hipSuccess) return KDA_ERR_HIP;
     return from_hip(kda::launch_chunk_state(a, chunk_off, order));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                         int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                         const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const void* z, const float* initial_state,
+                         float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    return chunk_fwd_impl(dt, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta, z,
+                          initial_state, final_state, y, 0, nullptr, nullptr, 0, workspace, workspace_bytes,
+                          stream);
+}
+
+kda_status kda_chunk_fwd_checkpointed(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                                      int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                                      const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const void* z, const float* initial_state,
+                                      float* final_state, void* y, int ckpt_interval, float* checkpoints,
+                                      int32_t* ckpt_offsets, int64_t ckpt_capacity, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    if (ckpt_interval <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    return chunk_fwd_impl(dt, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta, z,
+                          initial_state, final_state, y, ckpt_interval, checkpoints, ckpt_offsets,
+                          ckpt_capacity, workspace, workspace_bytes, stream);
 }
 
 size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int64_t T,

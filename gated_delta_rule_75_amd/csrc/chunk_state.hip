@@ -43,6 +43,10 @@ struct StateParams {
     const float* s0;
     float* sfin;
     TwoPassBufs ws;
+    float* ckpt;
+    const int32_t* ckpt_off;
+    int ckpt_every;
+    int64_t ckpt_cap;
 };
 
 template <typename E_, int DK_, int DV_, int CH_, int NVT_, int MODE_>
@@ -350,6 +354,22 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             stage(cn, nb, J_H{}, J_E{});
             load_uz(cn);
         }
+        if constexpr (!C::AUG) {
+            // prefix-cache checkpoint: the state after this chunk
+            if (p.ckpt && (c + 1) % p.ckpt_every == 0 && (int64_t)(c + 1) * CH <= len) {
+                const int64_t row = p.ckpt_off[n] + (c + 1) / p.ckpt_every - 1;
+                if (row < p.ckpt_cap) {
+                    float* dst = p.ckpt + (row * H + h) * DK * (int64_t)DV;
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                dst[(16 * ct + 4 * g4 + i) * DV + colw + 16 * vt + l16] = S[ct][vt][i];
+                }
+            }
+        }
 
         if constexpr (!C::AUG) {
             // O^T = S_old^T Qt^T + Delta^T Pm^T, then the gate
@@ -416,40 +436,60 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     }
 }
 
-// Chunk offsets of packed sequences and a longest-first order of them.
-__global__ __launch_bounds__(256) void varlen_plan_kernel(int N, const int32_t* __restrict__ cu, int CH,
+// Per-sequence plan: chunk offsets, a longest-first order, checkpoint offsets
+// (each output optional).  One workgroup; prefix sums in rounds of 256.
+__global__ __launch_bounds__(256) void varlen_plan_kernel(int N, const int32_t* __restrict__ cu, int64_t T_total,
+                                                          int CH, int ckpt_interval,
                                                           int32_t* __restrict__ chunk_off,
-                                                          int32_t* __restrict__ order) {
-    __shared__ int buf[256];
+                                                          int32_t* __restrict__ order,
+                                                          int32_t* __restrict__ ckpt_off) {
+    __shared__ int buf[2][256];
     const int tid = threadIdx.x;
-    int carry = 0;
+    auto seq_len = [&](int i) -> int64_t {
+        if (!cu) return T_total;
+        const int64_t l = (int64_t)cu[i + 1] - cu[i];
+        return l > 0 ? l : 0;
+    };
+    int carry0 = 0, carry1 = 0;
     for (int base = 0; base < N; base += 256) {
         const int i = base + tid;
-        int x = 0;
+        int x0 = 0, x1 = 0;
         if (i < N) {
-            const int l = cu[i + 1] - cu[i];
-            x = l > 0 ? (l + CH - 1) / CH : 0;
+            const int64_t l = seq_len(i);
+            x0 = (int)((l + CH - 1) / CH);
+            x1 = ckpt_interval > 0 ? (int)(l / ckpt_interval) : 0;
         }
-        buf[tid] = x;
+        buf[0][tid] = x0;
+        buf[1][tid] = x1;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {
-            const int y = tid >= d ? buf[tid - d] : 0;
+            const int y0 = tid >= d ? buf[0][tid - d] : 0;
+            const int y1 = tid >= d ? buf[1][tid - d] : 0;
             __syncthreads();
-            buf[tid] += y;
+            buf[0][tid] += y0;
+            buf[1][tid] += y1;
             __syncthreads();
         }
-        if (i < N) chunk_off[i] = carry + buf[tid] - x;
-        carry += buf[255];
+        if (i < N) {
+            if (chunk_off) chunk_off[i] = carry0 + buf[0][tid] - x0;
+            if (ckpt_off) ckpt_off[i] = carry1 + buf[1][tid] - x1;
+        }
+        carry0 += buf[0][255];
+        carry1 += buf[1][255];
         __syncthreads();
     }
-    if (tid == 0) chunk_off[N] = carry;
+    if (tid == 0) {
+        if (chunk_off) chunk_off[N] = carry0;
+        if (ckpt_off) ckpt_off[N] = carry1;
+    }
+    if (!order) return;
     for (int i = tid; i < N; i += 256) {
         int rank = i;
         if (N <= 1024) {
-            const int li = cu[i + 1] - cu[i];
+            const int64_t li = seq_len(i);
             rank = 0;
             for (int j = 0; j < N; ++j) {
-                const int lj = cu[j + 1] - cu[j];
+                const int64_t lj = seq_len(j);
                 rank += (lj > li) || (lj == li && j < i);
             }
         }
@@ -479,6 +519,10 @@ static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_of
     p.s0 = a.initial_state;
     p.sfin = a.final_state;
     p.ws = a.bufs;
+    p.ckpt = a.ckpt;
+    p.ckpt_off = a.ckpt_off;
+    p.ckpt_every = a.ckpt_every > 0 ? a.ckpt_every : 1;
+    p.ckpt_cap = a.ckpt_cap;
     if (p.nchains == 0) return hipSuccess;
     auto kern = chunk_state_kernel<C>;
     if (C::BYTES > 64 * 1024) {
@@ -521,10 +565,11 @@ hipError_t launch_chunk_state(const TwoPassArgs& a, const int32_t* chunk_off, co
                        : launch_state_dk<F32, 64>(a, chunk_off, order);
 }
 
-hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int chunk, int32_t* chunk_off,
-                              int32_t* order, void* stream) {
+hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int64_t T_total, int chunk,
+                              int ckpt_interval, int32_t* chunk_off, int32_t* order, int32_t* ckpt_off,
+                              void* stream) {
     hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, num_seqs, cu_seqlens,
-                       chunk, chunk_off, order);
+                       T_total, chunk, ckpt_interval, chunk_off, order, ckpt_off);
     return hipGetLastError();
 }
 

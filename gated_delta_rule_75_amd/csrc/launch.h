@@ -49,15 +49,24 @@ struct TwoPassArgs {
     int nvt;                     // 16-column value tiles per scan wave (1 or 2)
     TwoPassBufs bufs;            // chunk products (workspace)
     int64_t chunk_cap;           // chunks the workspace arrays hold
+    // prefix-cache checkpoints (modes 0 and 1): the state after every
+    // ckpt_every chunks of a sequence, at row ckpt_off[n] + j of ckpt
+    float* ckpt;                 // [capacity, H, dk, dv] or NULL
+    const int32_t* ckpt_off;     // device [num_seqs + 1]
+    int ckpt_every;
+    int64_t ckpt_cap;
     void* stream;
 };
 
 bool prefill_supported(int dtype, int dk, int dv, int chunk);
 
-// Chunk offsets ([num_seqs + 1]) and a longest-first order ([num_seqs]) of
-// packed sequences.
-hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int chunk, int32_t* chunk_off,
-                              int32_t* order, void* stream);
+// Per-sequence plan, each output optional: chunk offsets ([num_seqs + 1]),
+// a longest-first order ([num_seqs]) and checkpoint offsets ([num_seqs + 1],
+// floor(len / ckpt_interval) rows per sequence).  cu_seqlens NULL means one
+// sequence of T_total tokens.
+hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int64_t T_total, int chunk,
+                              int ckpt_interval, int32_t* chunk_off, int32_t* order, int32_t* ckpt_off,
+                              void* stream);
 // Products of every (chunk, head) into a.bufs; nchunks bounds the chunk count
 // (chunk_off, when given, holds the exact offsets).
 hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks);

@@ -123,6 +123,36 @@ size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chu
                                     int64_t T_total);
 
 /*
+ * kda_chunk_fwd_checkpointed -- kda_chunk_fwd that also saves the state every
+ * ckpt_interval tokens of each sequence, for a prefix cache (page
+ * "Exercices", Niveau 3 Q26: on a hybrid model a cached prefix is reusable
+ * only at a boundary where the KDA state was saved, and the pages decouple the
+ * 512-token hash granularity from allocation; the boundaries here are every
+ * ckpt_interval tokens).
+ *
+ *   ckpt_interval    tokens between checkpoints: a positive multiple of chunk.
+ *   checkpoints      fp32 [capacity, H, dk, dv]: checkpoint j of sequence n,
+ *                    the state after its first (j + 1) ckpt_interval tokens,
+ *                    lands in row ckpt_offsets[n] + j, for
+ *                    j < floor(len_n / ckpt_interval).  Other rows untouched.
+ *   ckpt_offsets     device int32 [num_seqs + 1], written by the call: the
+ *                    prefix sum of floor(len_n / ckpt_interval).
+ *   ckpt_capacity    rows of checkpoints; at least T_total / ckpt_interval
+ *                    (which bounds the total), else KDA_ERR_INVALID_ARGUMENT.
+ *   all other arguments and the workspace: as kda_chunk_fwd.
+ * The checkpoints are states of the same computation as final_state (same
+ * rounding); each costs one extra write of the fp32 state.
+ */
+kda_status kda_chunk_fwd_checkpointed(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                                      int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                                      const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const void* z, const float* initial_state,
+                                      float* final_state, void* y, int ckpt_interval,
+                                      float* checkpoints, int32_t* ckpt_offsets,
+                                      int64_t ckpt_capacity, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * kda_kcp_workspace_size -- bytes of device workspace kda_kcp_scan needs for
  * H heads of a T-token sequence split into num_segments segments: the segment
  * pairs (M [dk x dk], Sloc [dk x dv]) and the entering states [dk x dv], all

@@ -191,6 +191,41 @@ def kcp(q, k, v, g, beta, seg_bounds, z=None, S0=None, scale: float = 1.0, want_
     return out
 
 
+def checkpoints(q, k, v, g, beta, cu_seqlens, interval: int, S_init=None, scale: float = 1.0,
+                nthreads: Optional[int] = None):
+    """States after every `interval` tokens of each packed sequence: the state a
+    prefix cache saves at a boundary (page "Exercices", Niveau 3 Q26).
+
+    Checkpoint j of sequence n is the state after its first (j + 1) interval
+    tokens, for j < floor(len_n / interval).  The sequential recurrence runs
+    span by span, each span starting from the previous one's fp64 state.
+    Returns (ckpt [sum_n floor(len_n / interval), H, dk, dv] fp64,
+             offsets [N + 1] int64: sequence n's checkpoints start at offsets[n]).
+    """
+    cu = [int(x) for x in np.asarray(cu_seqlens).tolist()]
+    N = len(cu) - 1
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    counts = [max(cu[n + 1] - cu[n], 0) // interval for n in range(N)]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    out = np.zeros((int(offs[-1]), H, dk, dv))
+    heads = [(0, h) for h in range(H)]
+    for n in range(N):
+        state = np.zeros((H, dk, dv))
+        if S_init is not None:
+            S_np = (S_init.detach().cpu().to(torch.float64).numpy()
+                    if isinstance(S_init, torch.Tensor) else np.asarray(S_init, dtype=np.float64))
+            state[...] = S_np[n]
+        for j in range(counts[n]):
+            sl = slice(cu[n] + j * interval, cu[n] + (j + 1) * interval)
+            pick = lambda t: None if t is None else t[sl]
+            _, state = recurrence(pick(q), pick(k), pick(v), pick(g), pick(beta), [0, interval],
+                                  chains=heads, chain_states=state, scale=scale, want_y=False,
+                                  nthreads=nthreads)
+            out[offs[n] + j] = state
+    return out, offs
+
+
 def compose(M2, S2, M1, S1):
     """(M2, S2) o (M1, S1) = (M2 M1, M2 S1 + S2) in fp64, via the C oracle."""
     lib = _load()

@@ -62,6 +62,20 @@ def test_chunk_fwd_rejects_bad_arguments(L):
     assert _fwd(L, wsb=need - 1) == WS_SMALL
 
 
+def test_chunk_fwd_checkpointed_rejects_bad_arguments(L):
+    def ck(interval=128, cap=64, ckpt=P, offs=P, chunk=64, T=8192):
+        return L.kda_chunk_fwd_checkpointed(BF16, 2, 128, 128, chunk, 1.0, 1, T, None, P, P, P, P,
+                                            P, None, None, None, P, interval, ckpt, offs, cap, P,
+                                            1 << 40, None)
+    assert ck(interval=0) == INVALID
+    assert ck(interval=-64) == INVALID
+    assert ck(interval=96) == INVALID              # not a multiple of the chunk
+    assert ck(cap=63) == INVALID                   # fewer rows than T / interval
+    assert ck(offs=None) == INVALID
+    assert ck(ckpt=None) == INVALID
+    assert ck(ckpt=ctypes.c_void_p((1 << 20) + 8)) == INVALID
+
+
 def test_chunk_fwd_rejects_unsupported_shapes(L):
     assert _fwd(L, dk=96, dv=96) == UNSUPPORTED
     assert _fwd(L, dk=128, dv=64) == UNSUPPORTED

@@ -245,6 +245,42 @@ def test_prefill_final_state_may_alias_initial_state(kda):
     assert_parity("aliased state", inp, y.cpu(), st.cpu(), yo, so, TOL["bf16"])
 
 
+# ---------------------------------------------------------------- prefix-cache checkpoints
+@pytest.mark.parametrize("chunk,interval", [(64, 128), (16, 48), (64, 64)])
+def test_prefill_checkpoints_match_oracle(kda, chunk, interval):
+    """States every `interval` tokens of ragged packed sequences (one shorter than
+    the interval, one an exact multiple) against the oracle's checkpoints."""
+    lens = [300, 40, 256, 129, 0, 1]
+    inp = kda_inputs.make_prefill(lens, 3, 128, 128, "bf16", True, 0.05, 81, 8.0, 4.0)
+    y, fs, ck, offs = kda.chunk_fwd_checkpointed(
+        inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(), inp.beta.cuda(), interval,
+        cu_seqlens=inp.cu_seqlens.cuda(), z=inp.z.cuda(), initial_state=inp.S0.cuda(), chunk=chunk)
+    torch.cuda.synchronize()
+    co, oo = oracle.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, interval,
+                                S_init=inp.S0)
+    assert offs.cpu().tolist() == oo.tolist()      # integer offsets: exact
+    n = int(oo[-1])
+    e = rel_l2(ck[:n].cpu().double().numpy(), co)
+    log(f"[parity] checkpoints c{chunk} every {interval}: {n} states, rel_l2={e:.3e}")
+    assert e <= TOL["bf16"]
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"checkpointed prefill c{chunk}", inp, y.cpu(), fs.cpu(), yo, so, TOL["bf16"])
+
+
+def test_prefill_checkpoints_single_sequence_fp32(kda):
+    inp = kda_inputs.make_workload(0, "chunk", lens=[256], s0_std=0.3)
+    y, fs, ck, offs = kda.chunk_fwd_checkpointed(
+        inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(), inp.beta.cuda(), 32,
+        initial_state=inp.S0.cuda(), chunk=16)
+    torch.cuda.synchronize()
+    co, oo = oracle.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, 32,
+                                S_init=inp.S0)
+    assert offs.cpu().tolist() == oo.tolist() == [0, 8]
+    e = rel_l2(ck.cpu().double().numpy(), co)
+    log(f"[parity] checkpoints fp32 single sequence: rel_l2={e:.3e}")
+    assert e <= TOL["f32"]
+
+
 # ---------------------------------------------------------------- KCP
 @pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 64, 16), ("bf16", 64, 64),
                                            ("f32", 128, 64), ("bf16", 128, 16)])

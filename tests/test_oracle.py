@@ -310,3 +310,46 @@ def test_generator_recipe():
     small2 = kda_inputs.make_workload(2, H=2, lmin=3, lmax=40)
     assert small2.num_seqs == 16 and all(3 <= n <= 40 for n in small2.lengths())
     assert small2.q.dtype == torch.bfloat16 and small2.S0.shape == (16, 2, 128, 128)
+
+
+# ---------------------------------------------------------------- prefix-cache checkpoints
+def test_oracle_checkpoints_are_brute_force_prefix_states(oracle_mod):
+    """Checkpoint j = the state after (j+1)*interval tokens, by explicit transition
+    matrices on each prefix (page "Exercices", Niveau 3 Q26)."""
+    from oracle import brute
+    inp = kda_inputs.make_prefill([37, 20, 8], 2, 6, 5, "f32", False, 0.4, 31)
+    ck, offs = oracle_mod.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, 8,
+                                      S_init=inp.S0)
+    assert offs.tolist() == [0, 4, 6, 7]
+    cu = inp.cu_seqlens.tolist()
+    for n in range(3):
+        for j in range(offs[n + 1] - offs[n]):
+            for h in range(2):
+                sl = slice(cu[n], cu[n] + 8 * (j + 1))
+                _, S = brute.sequence(inp.q[sl, h], inp.k[sl, h], inp.v[sl, h], inp.g[sl, h],
+                                      inp.beta[sl, h], S0=inp.S0[n, h])
+                np.testing.assert_allclose(ck[offs[n] + j, h], S, rtol=0, atol=1e-12)
+
+
+def test_oracle_checkpoint_at_the_end_is_the_final_state(oracle_mod):
+    inp = kda_inputs.make_prefill([64, 128], 2, 8, 8, "f32", True, 0.2, 32)
+    ck, offs = oracle_mod.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, 32,
+                                      S_init=inp.S0)
+    _, st = oracle_mod.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
+                                  S_init=inp.S0)
+    np.testing.assert_allclose(ck[offs[1] - 1], st[0:2], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ck[offs[2] - 1], st[2:4], rtol=0, atol=1e-13)
+
+
+def test_oracle_resume_from_a_checkpoint(oracle_mod):
+    """Running the rest of a sequence from a checkpoint reproduces the uncut run."""
+    inp = kda_inputs.make_prefill([96], 1, 8, 8, "f32", True, 0.0, 33)
+    ck, _ = oracle_mod.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, 32)
+    y_full, s_full = oracle_mod.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
+                                           z=inp.z)
+    sl = slice(32, 96)
+    y_rest, s_rest = oracle_mod.recurrence(inp.q[sl], inp.k[sl], inp.v[sl], inp.g[sl],
+                                           inp.beta[sl], [0, 64], z=inp.z[sl],
+                                           chain_states=ck[0])
+    np.testing.assert_allclose(y_rest, y_full[32:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(s_rest, s_full, rtol=0, atol=1e-13)
