@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "KDAError", "lib", "library_path", "kda_version", "kda_status_string",
     "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_checkpointed", "kcp_scan",
-    "kcp_workspace_size", "decode_step",
+    "kcp_workspace_size", "decode_step", "decode_replay",
     "KDA_BF16", "KDA_F32",
 ]
 
@@ -33,7 +33,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 # Every symbol include/kda.h declares.
 SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
            "kda_chunk_fwd_checkpointed", "kda_kcp_workspace_size", "kda_kcp_scan",
-           "kda_decode_step")
+           "kda_decode_step", "kda_decode_replay")
 
 
 class KDAError(RuntimeError):
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.kda_kcp_scan.restype = i
     L.kda_decode_step.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_decode_step.restype = i
+    L.kda_decode_replay.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_decode_replay.restype = i
     _lib = L
     return L
 
@@ -248,4 +250,37 @@ def decode_step(q, k, v, g, beta, state, z=None, scale: float = 1.0,
     st = lib().kda_decode_step(dt, N, H, dk, dv, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                _ptr(beta), _ptr(z), _ptr(state), _ptr(y), _stream(dev))
     _check("kda_decode_step", st)
+    return y
+
+
+def decode_replay(q, k, v, g, beta, state, accepted=None, z=None, scale: float = 1.0,
+                  want_y: bool = True, y: Optional[torch.Tensor] = None):
+    """Speculative-decoding replay.  q, k, g: [N, Td, H, dk]; v, z: [N, Td, H, dv];
+    beta [N, Td, H]; state fp32 [N, H, dk, dv] (overwritten with the state after
+    accepted[n] tokens when `accepted` (int32 [N]) is given).  Returns y
+    [N, Td, H, dv] or None."""
+    dt = _dt(q)
+    N, Td, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("k", k), ("v", v), ("z", z)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, Td, H, dv) or \
+            beta.shape != (N, Td, H) or (z is not None and z.shape != v.shape):
+        raise ValueError("replay inputs must be [N, Td, H, d] (beta [N, Td, H])")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
+        raise ValueError("state must be float32 [N, H, dk, dv]")
+    if accepted is not None and (accepted.dtype != torch.int32 or accepted.shape != (N,)):
+        raise ValueError("accepted must be int32 [N]")
+    dev = _dev(q, k, v, g, beta, z, state, accepted, y)
+    if want_y and y is None:
+        y = torch.empty(N, Td, H, dv, dtype=q.dtype, device=dev)
+    if not want_y:
+        y = None
+    st = lib().kda_decode_replay(dt, N, Td, H, dk, dv, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                 _ptr(beta), _ptr(z), _ptr(accepted), _ptr(state), _ptr(y),
+                                 _stream(dev))
+    _check("kda_decode_replay", st)
     return y

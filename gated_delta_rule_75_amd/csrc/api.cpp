@@ -332,6 +332,41 @@ kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float sca
     return from_hip(kda::launch_decode(a));
 }
 
+kda_status kda_decode_replay(kda_dtype dt, int N, int Td, int H, int dk, int dv, float scale,
+                             const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const void* z, const int32_t* accepted,
+                             float* state, void* y, void* stream) {
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
+    if (N < 0 || Td <= 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)N * H > (int64_t)1 << 30 || (int64_t)N * Td * H > (int64_t)1 << 31)
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!head_shape_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (!y && !accepted) return KDA_ERR_INVALID_ARGUMENT;   // nothing to produce
+    if (N > 0 && (!q || !k || !v || !g || !beta || !state)) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t ea = elt_align(dt);
+    if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
+        !aligned(y, ea) || !aligned(g, 8) || !aligned(beta, 4) || !aligned(state, 16) ||
+        !aligned(accepted, 4))
+        return KDA_ERR_INVALID_ARGUMENT;
+    kda::DecodeArgs a{};
+    a.dtype = (int)dt;
+    a.N = N;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.z = z;
+    a.state = state;
+    a.y = y;
+    a.stream = stream;
+    return from_hip(kda::launch_replay(a, Td, accepted));
+}
+
 }  // extern "C"
 
 namespace kda {

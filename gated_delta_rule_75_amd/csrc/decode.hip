@@ -102,6 +102,127 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
     }
 }
 
+// Speculative-decoding replay (page "Exercices", Niveau 3 Q27: the state after
+// any accepted prefix is fixed by the draft tokens' inputs, so only those are
+// kept and the recurrence is replayed on chip).  One workgroup per
+// (request, head) loads the state once, runs the decode step above for each of
+// the request's draft tokens with the state in registers, emits every draft
+// token's output (when y is given), keeps a copy of the state after the
+// accepted prefix, and writes that copy back (when accepted is given).
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H, const T* __restrict__ q,
+                                                     const T* __restrict__ k, const T* __restrict__ v,
+                                                     const float* __restrict__ g,
+                                                     const float* __restrict__ beta,
+                                                     const T* __restrict__ z,
+                                                     const int32_t* __restrict__ accepted,
+                                                     float* __restrict__ state, T* __restrict__ y) {
+    constexpr int CG = DV / 4;
+    constexpr int RG = 256 / CG;
+    constexpr int RPT = DK / RG;
+    static_assert(RG * CG == 256 && RPT * RG == DK, "replay tiling");
+
+    __shared__ float s_k[DK], s_q[DK], s_a[DK];
+    __shared__ float s_u[RG][DV + 4], s_w[RG][DV + 4];
+    __shared__ float s_delta[DV];
+    __shared__ float s_kq;
+
+    const int nh = blockIdx.x, n = nh / H, h = nh % H;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    int acc = 0;
+    if (accepted) {
+        acc = accepted[n];
+        acc = acc < 0 ? 0 : (acc > Td ? Td : acc);
+    }
+    const int steps = y ? Td : acc;   // without outputs only the accepted prefix matters
+    if (steps == 0) return;
+    float* st = state + (int64_t)nh * DK * DV;
+
+    f32x4_t S[RPT], Sc[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[r] = *reinterpret_cast<const f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg);
+    for (int t = 0; t < steps; ++t) {
+        const int64_t tok = ((int64_t)n * Td + t) * H + h;
+        const int64_t kb = tok * DK, vb = tok * DV;
+        for (int c = tid; c < DK; c += 256) {
+            s_k[c] = gload(k + kb + c);
+            s_q[c] = gload(q + kb + c);
+            s_a[c] = fast_exp(g[kb + c]);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            float pk = 0.f;
+            for (int c = tid; c < DK; c += kWave) pk += s_k[c] * s_q[c];
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) pk += __shfl_xor(pk, off);
+            if (tid == 0) s_kq = pk;
+        }
+        f32x4_t u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int row = r * RG + rg;
+            S[r] *= s_a[row];
+            u += s_k[row] * S[r];
+            w += s_q[row] * S[r];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s_u[rg][4 * cg + i] = u[i];
+            s_w[rg][4 * cg + i] = w[i];
+        }
+        __syncthreads();
+        if (tid < DV) {
+            const int j = tid;
+            float U = 0.f, W = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                U += s_u[r][j];
+                W += s_w[r][j];
+            }
+            const float d = beta[tok] * (gload(v + vb + j) - U);
+            s_delta[j] = d;
+            if (y) {
+                float o = scale * (W + s_kq * d);
+                if (z) o *= sigmoid(gload(z + vb + j));
+                gstore(y + vb + j, o);
+            }
+        }
+        __syncthreads();
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&s_delta[4 * cg]);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) S[r] += s_k[r * RG + rg] * d4;
+        if (t + 1 == acc) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) Sc[r] = S[r];
+        }
+        __syncthreads();  // s_k, s_delta are rewritten by the next token
+    }
+    if (acc > 0) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            __builtin_nontemporal_store(Sc[r], reinterpret_cast<f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg));
+    }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_replay_t(const DecodeArgs& a, int Td, const int32_t* accepted) {
+    if (a.N == 0) return hipSuccess;
+    hipLaunchKernelGGL((replay_kernel<T, DK, DV>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
+                       (hipStream_t)a.stream, Td, a.scale, a.H, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, a.g, a.beta, (const T*)a.z, accepted, a.state, (T*)a.y);
+    return hipGetLastError();
+}
+
+hipError_t launch_replay(const DecodeArgs& a, int Td, const int32_t* accepted) {
+    if (a.dtype == 0) {
+        if (a.dk == 128) return launch_replay_t<__bf16, 128, 128>(a, Td, accepted);
+        return launch_replay_t<__bf16, 64, 64>(a, Td, accepted);
+    }
+    if (a.dk == 128) return launch_replay_t<float, 128, 128>(a, Td, accepted);
+    return launch_replay_t<float, 64, 64>(a, Td, accepted);
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     if (a.N == 0) return hipSuccess;

@@ -74,6 +74,10 @@ hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int
 hipError_t launch_chunk_state(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order);
 
 hipError_t launch_decode(const DecodeArgs& a);
+// Td draft tokens per request (inputs [N, Td, H, d]) against the resident
+// states: outputs of all of them (a.y, optional) and the state after the first
+// accepted[n] written back (accepted optional).
+hipError_t launch_replay(const DecodeArgs& a, int Td, const int32_t* accepted);
 
 // KCP phase 2: starts[s] = M_{s-1} starts[s-1] + Sloc_{s-1}, starts[0] = S0.
 hipError_t launch_kcp_scan(int H, int dk, int dv, int nseg, const float* pairs,

@@ -203,6 +203,35 @@ kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float sca
                            const float* beta, const void* z, float* state, void* y,
                            void* stream);
 
+/*
+ * kda_decode_replay -- speculative decoding: Td draft tokens per request
+ * replayed against the resident states (page "Exercices", Niveau 3 Q27: the
+ * state after any accepted prefix is fully determined by the draft tokens'
+ * projected inputs, which are much smaller than the state, so only those are
+ * kept; the recurrence is replayed on chip and the verified state written
+ * back).  One pass reads each state once.
+ *
+ *   N, Td            requests (>= 0) and draft tokens per request (>= 1).
+ *   q, k, v, z       [N, Td, H, d] in dtype dt (z may be NULL): draft token t
+ *                    of request n at [n, t].
+ *   g, beta          [N, Td, H, dk] and [N, Td, H] fp32.
+ *   accepted         device int32 [N] or NULL.  Given: the state of request n
+ *                    is overwritten with the state after its first accepted[n]
+ *                    draft tokens (clamped to [0, Td]; 0 leaves it as is).
+ *                    NULL: the states are only read.
+ *   state            fp32 [N, H, dk, dv], resident.
+ *   y                [N, Td, H, dv] or NULL: the output of every draft token,
+ *                    each computed from the state before the call (the
+ *                    verification pass).
+ * At least one of y and accepted must be given.  A verify call (y, no
+ * accepted) followed by a commit call (accepted, no y) leaves the states as
+ * if the accepted tokens had gone through kda_decode_step one by one.
+ */
+kda_status kda_decode_replay(kda_dtype dt, int N, int Td, int H, int dk, int dv, float scale,
+                             const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const void* z, const int32_t* accepted,
+                             float* state, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

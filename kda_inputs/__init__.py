@@ -12,7 +12,8 @@ storage dtype.
 Recipe (fixed draw order, one torch CPU generator per workload):
     lengths (varlen only), q, k, v, z (gated only), beta pre-activation,
     g pre-activation, initial state (if any).
-All draws are i.i.d. N(0, 1) except the initial state (N(0, std)).  q and k are
+All draws are i.i.d. N(0, 1) except the initial state (N(0, std)) and the
+accepted draft lengths of a replay (uniform integers).  q and k are
 normalised per (token, head) in fp32, then q, k, v, z are rounded to the
 storage dtype (bf16 by round-to-nearest-even, or kept fp32).  beta and g stay
 fp32.  Decode pools draw P independent token sets after the state.
@@ -185,6 +186,38 @@ def make_decode_workload(stress: Optional[str] = None, **override) -> DecodeInpu
     seed = override.get("seed", workload_seed(4, stress))
     return make_decode(w["N"], w["H"], w["dk"], w["dv"], w["dtype"], w["gated"], w["s0_std"],
                        w["pool"], seed, g_shift, beta_shift)
+
+
+@dataclasses.dataclass
+class ReplayInputs:
+    """Draft tokens of speculative decoding: Td tokens per request against the
+    resident states, plus the accepted prefix length of each request."""
+    q: torch.Tensor        # [N, Td, H, dk]
+    k: torch.Tensor
+    v: torch.Tensor        # [N, Td, H, dv]
+    z: Optional[torch.Tensor]
+    g: torch.Tensor        # [N, Td, H, dk] fp32
+    beta: torch.Tensor     # [N, Td, H] fp32
+    S0: torch.Tensor       # [N, H, dk, dv] fp32
+    accepted: torch.Tensor  # [N] int32 in [0, Td]
+    N: int
+    Td: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str
+
+
+def make_replay(N: int, Td: int, H: int, dk: int, dv: int, dtype: str, gated: bool,
+                s0_std: float, seed: int, g_shift: float = 0.0,
+                beta_shift: float = 0.0) -> ReplayInputs:
+    """Draw order: state, draft tokens ([N, Td] prefix), accepted lengths
+    (uniform integers in [0, Td])."""
+    gen = torch.Generator().manual_seed(seed)
+    S0 = (torch.randn(N, H, dk, dv, generator=gen) * s0_std).contiguous()
+    q, k, v, z, beta, g = draw_tokens(gen, [N, Td], H, dk, dv, dtype, gated, g_shift, beta_shift)
+    acc = torch.randint(0, Td + 1, (N,), generator=gen).to(torch.int32)
+    return ReplayInputs(q, k, v, z, g, beta, S0, acc, N, Td, H, dk, dv, dtype)
 
 
 def draw_on_device(lens: List[int], H: int, dk: int, dv: int, gated: bool, s0_std: float,

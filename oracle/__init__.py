@@ -226,6 +226,36 @@ def checkpoints(q, k, v, g, beta, cu_seqlens, interval: int, S_init=None, scale:
     return out, offs
 
 
+def replay(rep, scale: float = 1.0, nthreads: Optional[int] = None):
+    """Speculative-decoding replay (page "Exercices", Niveau 3 Q27: the state
+    after any accepted prefix is fixed by the draft tokens' inputs, so only
+    those are kept and the recurrence is replayed).
+
+    rep: kda_inputs.ReplayInputs.  Each request's Td draft tokens run as one
+    sequence from its resident state.  Returns (y [N, Td, H, dv]: the outputs of
+    every draft token, committed [N, H, dk, dv]: the state after the first
+    accepted[n] tokens (the resident state where accepted[n] = 0)).
+    """
+    N, Td, H, dk, dv = rep.N, rep.Td, rep.H, rep.dk, rep.dv
+    flat = lambda t: None if t is None else t.reshape(N * Td, *t.shape[2:])
+    cu = np.arange(0, (N + 1) * Td, Td, dtype=np.int32)
+    y, _ = recurrence(flat(rep.q), flat(rep.k), flat(rep.v), flat(rep.g), flat(rep.beta), cu,
+                      z=flat(rep.z), S_init=rep.S0, scale=scale, nthreads=nthreads)
+    acc = [int(a) for a in rep.accepted.tolist()]
+    committed = rep.S0.to(torch.float64).numpy().copy()
+    for n in range(N):
+        if acc[n] == 0:
+            continue
+        sl = slice(n * Td, n * Td + acc[n])
+        pick = lambda t: None if t is None else flat(t)[sl]
+        _, st = recurrence(pick(rep.q), pick(rep.k), pick(rep.v), pick(rep.g), pick(rep.beta),
+                           [0, acc[n]], chains=[(0, h) for h in range(H)],
+                           chain_states=committed[n], scale=scale, want_y=False,
+                           nthreads=nthreads)
+        committed[n] = st
+    return y.reshape(N, Td, H, dv), committed
+
+
 def compose(M2, S2, M1, S1):
     """(M2, S2) o (M1, S1) = (M2 M1, M2 S1 + S2) in fp64, via the C oracle."""
     lib = _load()

@@ -166,3 +166,17 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(4, 1, 64)
     with pytest.raises(ValueError):
         kda.chunk_fwd(q, q, q, q, torch.zeros(4, 1))
+
+
+def test_decode_replay_rejects_bad_arguments(L):
+    def rp(dt=BF16, N=4, Td=3, H=2, dk=128, dv=128, acc=P, state=P, y=P, q=P):
+        return L.kda_decode_replay(dt, N, Td, H, dk, dv, 1.0, q, P, P, P, P, None, acc, state, y,
+                                   None)
+    assert rp(Td=0) == INVALID
+    assert rp(N=-1) == INVALID
+    assert rp(acc=None, y=None) == INVALID        # nothing to produce
+    assert rp(state=None) == INVALID
+    assert rp(q=None) == INVALID
+    assert rp(acc=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert rp(dk=96, dv=96) == UNSUPPORTED
+    assert rp(N=0) == OK                          # no requests: nothing launched

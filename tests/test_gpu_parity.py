@@ -245,6 +245,66 @@ def test_prefill_final_state_may_alias_initial_state(kda):
     assert_parity("aliased state", inp, y.cpu(), st.cpu(), yo, so, TOL["bf16"])
 
 
+# ---------------------------------------------------------------- speculative-decoding replay
+def _replay_dev(rep):
+    d = {n: getattr(rep, n).cuda() for n in ("q", "k", "v", "g", "beta")}
+    d["z"] = None if rep.z is None else rep.z.cuda()
+    return d
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_replay_verify_then_commit(kda, dtype, d):
+    rep = kda_inputs.make_replay(8, 5, 4, d, d, dtype, True, 0.05, 91, 8.0, 4.0)
+    rep.accepted[:2] = torch.tensor([0, 5], dtype=torch.int32)   # none and all accepted
+    x = _replay_dev(rep)
+    state = rep.S0.cuda()
+    y = kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state, z=x["z"], scale=0.5)
+    torch.cuda.synchronize()
+    # the verify pass only reads the states
+    assert torch.equal(state.cpu(), rep.S0)
+    kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                      accepted=rep.accepted.cuda(), z=x["z"], scale=0.5, want_y=False)
+    torch.cuda.synchronize()
+    yo, so = oracle.replay(rep, scale=0.5)
+    ey = rel_l2(y.cpu().double().numpy(), yo)
+    es = rel_l2(state.cpu().double().numpy(), so)
+    log(f"[parity] replay {dtype} d{d}: y={ey:.3e} committed={es:.3e}")
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    # nothing accepted: bit-identical state
+    assert torch.equal(state[0].cpu(), rep.S0[0])
+
+
+def test_replay_outputs_and_commit_in_one_call(kda):
+    rep = kda_inputs.make_replay(6, 4, 3, 128, 128, "bf16", True, 0.05, 92)
+    x = _replay_dev(rep)
+    state = rep.S0.cuda()
+    y = kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                          accepted=rep.accepted.cuda(), z=x["z"])
+    torch.cuda.synchronize()
+    yo, so = oracle.replay(rep)
+    assert rel_l2(y.cpu().double().numpy(), yo) <= TOL["bf16"]
+    assert rel_l2(state.cpu().double().numpy(), so) <= TOL["bf16"]
+
+
+def test_replay_full_acceptance_equals_decode_steps(kda):
+    """Accepting every draft token = Td calls of kda_decode_step (same kernels'
+    arithmetic per token, so the results agree to rounding)."""
+    rep = kda_inputs.make_replay(5, 3, 2, 128, 128, "bf16", True, 0.05, 93)
+    rep.accepted[:] = 3
+    x = _replay_dev(rep)
+    s_rep = rep.S0.cuda()
+    y_rep = kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], s_rep,
+                              accepted=rep.accepted.cuda(), z=x["z"])
+    s_dec = rep.S0.cuda()
+    for t in range(3):
+        y_t = kda.decode_step(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                              x["v"][:, t].contiguous(), x["g"][:, t].contiguous(),
+                              x["beta"][:, t].contiguous(), s_dec, z=x["z"][:, t].contiguous())
+        torch.cuda.synchronize()
+        assert rel_l2(y_rep[:, t].cpu().double().numpy(), y_t.cpu().double().numpy()) <= 1e-5
+    assert rel_l2(s_rep.cpu().double().numpy(), s_dec.cpu().double().numpy()) <= 1e-6
+
+
 # ---------------------------------------------------------------- prefix-cache checkpoints
 @pytest.mark.parametrize("chunk,interval", [(64, 128), (16, 48), (64, 64)])
 def test_prefill_checkpoints_match_oracle(kda, chunk, interval):

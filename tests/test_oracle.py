@@ -353,3 +353,38 @@ def test_oracle_resume_from_a_checkpoint(oracle_mod):
                                            chain_states=ck[0])
     np.testing.assert_allclose(y_rest, y_full[32:], rtol=0, atol=1e-13)
     np.testing.assert_allclose(s_rest, s_full, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- speculative-decoding replay
+def test_oracle_replay_matches_brute_force(oracle_mod):
+    """Replay outputs and the committed state after the accepted prefix, by
+    explicit transition matrices (page "Exercices", Niveau 3 Q27)."""
+    from oracle import brute
+    rep = kda_inputs.make_replay(3, 5, 2, 6, 4, "f32", True, 0.3, 41)
+    rep.accepted[:] = torch.tensor([0, 2, 5], dtype=torch.int32)
+    y, committed = oracle_mod.replay(rep, scale=0.7)
+    for n in range(3):
+        for h in range(2):
+            yb, _ = brute.sequence(rep.q[n, :, h], rep.k[n, :, h], rep.v[n, :, h], rep.g[n, :, h],
+                                   rep.beta[n, :, h], rep.z[n, :, h], S0=rep.S0[n, h], scale=0.7)
+            np.testing.assert_allclose(y[n, :, h], yb, rtol=0, atol=1e-12)
+            a = int(rep.accepted[n])
+            _, Sb = brute.sequence(rep.q[n, :a, h], rep.k[n, :a, h], rep.v[n, :a, h],
+                                   rep.g[n, :a, h], rep.beta[n, :a, h], S0=rep.S0[n, h])
+            np.testing.assert_allclose(committed[n, h], Sb, rtol=0, atol=1e-12)
+    # nothing accepted: the resident state is kept
+    np.testing.assert_array_equal(committed[0], rep.S0[0].double().numpy())
+
+
+def test_oracle_full_acceptance_equals_decode_steps(oracle_mod):
+    """Accepting every draft token equals Td single-token decode steps."""
+    rep = kda_inputs.make_replay(4, 3, 2, 8, 8, "f32", True, 0.1, 42)
+    rep.accepted[:] = 3
+    y, committed = oracle_mod.replay(rep)
+    dec = kda_inputs.DecodeInputs(rep.q.transpose(0, 1).contiguous(), rep.k.transpose(0, 1).contiguous(),
+                                  rep.v.transpose(0, 1).contiguous(), rep.z.transpose(0, 1).contiguous(),
+                                  rep.g.transpose(0, 1).contiguous(), rep.beta.transpose(0, 1).contiguous(),
+                                  rep.S0, 4, 2, 8, 8, "f32")
+    y_last, _, st = oracle_mod.decode_steps(dec, 3)
+    np.testing.assert_allclose(y[:, 2], y_last, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(committed.reshape(8, 8, 8), st, rtol=0, atol=1e-13)
