@@ -26,7 +26,8 @@ import time
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
-ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode")
+ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode", "prefill_checkpoints",
+                 "decode_replay")
 
 
 def log(msg: str) -> None:
@@ -238,6 +239,64 @@ def bench_decode(args, torch, kda, kda_inputs, dev):
     return out
 
 
+def bench_checkpoints(args, torch, kda, kda_inputs, dev):
+    """The K3 layer prefill saving the state every 512 tokens (the pages' prefix
+    hash granularity): 16 extra fp32 states per head."""
+    w = kda_inputs.WORKLOADS[1]
+    H, dk, dv, T, C = w["H"], w["dk"], w["dv"], w["lens"][0], w["chunk"]
+    interval = 512
+    d = gpu_inputs(torch, [T], H, dk, dv, True, 0.0, kda_inputs.workload_seed(1), dev)
+    ms, _ = time_steps(lambda: kda.chunk_fwd_checkpointed(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                          interval, z=d["z"], chunk=C),
+                       max(1, args.steps // 2), 2, torch)
+    nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True) + (T // interval) * H * dk * dv * 4
+    out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), interval=interval, checkpoints=T // interval,
+               gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del d
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_replay(args, torch, kda, kda_inputs, dev):
+    """Speculative decoding at the decode workload's shape: 4 draft tokens per
+    request, a verify pass (outputs of all drafts, state read only) and a commit
+    pass (state after each request's accepted prefix written back)."""
+    w = kda_inputs.WORKLOADS[4]
+    N, H, dk, dv, Td = w["N"], w["H"], w["dk"], w["dv"], 4
+    gen = torch.Generator(device=dev).manual_seed(kda_inputs.workload_seed(4) + 100)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    state = torch.randn(N, H, dk, dv, generator=gen, device=dev) * w["s0_std"]
+    x = dict(q=unit(torch.randn(N, Td, H, dk, generator=gen, device=dev)).to(torch.bfloat16),
+             k=unit(torch.randn(N, Td, H, dk, generator=gen, device=dev)).to(torch.bfloat16),
+             v=torch.randn(N, Td, H, dv, generator=gen, device=dev).to(torch.bfloat16),
+             z=torch.randn(N, Td, H, dv, generator=gen, device=dev).to(torch.bfloat16),
+             beta=torch.sigmoid(torch.randn(N, Td, H, generator=gen, device=dev)),
+             g=-5.0 * torch.sigmoid(torch.randn(N, Td, H, dk, generator=gen, device=dev)))
+    acc = torch.randint(0, Td + 1, (N,), generator=gen, device=dev).to(torch.int32)
+    y = torch.empty(N, Td, H, dv, dtype=torch.bfloat16, device=dev)
+    ms_v, _ = time_steps(lambda: kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                                                   z=x["z"], y=y), 20, 2, torch)
+    ms_c, _ = time_steps(lambda: kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                                                   accepted=acc, z=x["z"], want_y=False), 20, 2, torch)
+    st = H * dk * dv * 4                              # one request's states
+    tok = H * (2 * dk * 2 + dv * 2 * 2 + dk * 4 + 4)   # one draft token's inputs
+    a = [int(t) for t in acc.cpu().tolist()]
+    verify_bytes = N * st + N * Td * tok + N * Td * H * dv * 2
+    # a request that accepts nothing is skipped; the others read and write their states
+    commit_bytes = sum(2 * st + an * tok for an in a if an > 0)
+    out = dict(draft_tokens=Td, verify_ms=ms_v, commit_ms=ms_c,
+               verify_gbs=verify_bytes / (ms_v * 1e-3) / 1e9,
+               commit_gbs=commit_bytes / (ms_c * 1e-3) / 1e9,
+               accepted_mean=sum(a) / N,
+               draft_tokens_per_s=N * Td / (ms_v * 1e-3))
+    del state, x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,7 +304,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads (%s), 'all' or 'none'" % ",".join(ALL_WORKLOADS))
-    ap.add_argument("--cpu-sample-heads", type=int, default=48)
+    ap.add_argument("--cpu-sample-heads", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1000,
                     help="decode steps timed as one loop (the workload runs 1000)")
@@ -280,7 +339,8 @@ def main() -> int:
     workloads = {}
     for name in extras:
         fn = {"varlen_prefill": bench_varlen, "kcp_long_sequence": bench_kcp,
-              "decode": bench_decode}[name]
+              "decode": bench_decode, "prefill_checkpoints": bench_checkpoints,
+              "decode_replay": bench_replay}[name]
         workloads[name] = fn(args, torch, kda, kda_inputs, dev)
         log(f"{name}: {json.dumps(workloads[name])}")
     cpu, parity = (None, None)
