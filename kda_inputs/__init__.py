@@ -18,6 +18,11 @@ normalised per (token, head) in fp32, then q, k, v, z are rounded to the
 storage dtype (bf16 by round-to-nearest-even, or kept fp32).  beta and g stay
 fp32.  Decode pools draw P independent token sets after the state.
 
+Raw inputs of the fused input step (make_raw_prefill, make_raw_decode) are the
+same draws, in the same order, left unprocessed: q and k not normalised, and
+the pre-activations a = x - g_shift (decay) and b = x - beta_shift (beta),
+all rounded to the storage dtype.
+
 Shapes (token-major, channel fastest):
     q, k: [T, H, dk]   v, z: [T, H, dv]   g: [T, H, dk] fp32   beta: [T, H] fp32
     cu_seqlens: [N + 1] int32   S0: [N, H, dk, dv] fp32
@@ -246,6 +251,68 @@ def draw_on_device(lens: List[int], H: int, dk: int, dv: int, gated: bool, s0_st
     if lens:
         cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
     return KDAInputs(q, k, v, z, g, beta, cu, S0, H, dk, dv, "bf16")
+
+
+@dataclasses.dataclass
+class RawInputs:
+    """Inputs of the fused input step, in the storage dtype: q, k before
+    normalisation, a the decay pre-activation (per key channel), b the beta
+    pre-activation (per token and head).  Token shapes as in KDAInputs, with a
+    leading [P] (decode steps) or a packed [T] token axis."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    z: Optional[torch.Tensor]
+    a: torch.Tensor
+    b: torch.Tensor
+    cu_seqlens: Optional[torch.Tensor]
+    S0: Optional[torch.Tensor]
+    H: int
+    dk: int
+    dv: int
+    dtype: str
+
+
+def draw_raw_tokens(gen: torch.Generator, shape_prefix, H: int, dk: int, dv: int, dtype: str,
+                    gated: bool, g_shift: float = 0.0, beta_shift: float = 0.0):
+    """The draws of draw_tokens, unprocessed: (q, k, v, z, b, a) in the storage dtype."""
+    sp = tuple(shape_prefix)
+    td = _tdtype(dtype)
+    q = torch.randn(*sp, H, dk, generator=gen).to(td)
+    k = torch.randn(*sp, H, dk, generator=gen).to(td)
+    v = torch.randn(*sp, H, dv, generator=gen).to(td)
+    z = torch.randn(*sp, H, dv, generator=gen).to(td) if gated else None
+    b = (torch.randn(*sp, H, generator=gen) - beta_shift).to(td)
+    a = (torch.randn(*sp, H, dk, generator=gen) - g_shift).to(td)
+    return q, k, v, z, b.contiguous(), a.contiguous()
+
+
+def make_raw_prefill(lens: List[int], H: int, dk: int, dv: int, dtype: str, gated: bool,
+                     s0_std: float, seed: int, g_shift: float = 0.0,
+                     beta_shift: float = 0.0) -> RawInputs:
+    """Packed prefill inputs for the fused input step (draw order of make_prefill)."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = [int(x) for x in lens]
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    if lens:
+        cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    T = int(cu[-1])
+    q, k, v, z, b, a = draw_raw_tokens(gen, [T], H, dk, dv, dtype, gated, g_shift, beta_shift)
+    S0 = None
+    if s0_std > 0:
+        S0 = (torch.randn(len(lens), H, dk, dv, generator=gen) * s0_std).contiguous()
+    return RawInputs(q, k, v, z, a, b, cu, S0, H, dk, dv, dtype)
+
+
+def make_raw_decode(N: int, H: int, dk: int, dv: int, dtype: str, gated: bool, s0_std: float,
+                    steps: int, seed: int, g_shift: float = 0.0,
+                    beta_shift: float = 0.0) -> RawInputs:
+    """`steps` single-token input sets [steps, N, H, .] for the fused decode
+    step, after the state (draw order of make_decode)."""
+    gen = torch.Generator().manual_seed(seed)
+    S0 = (torch.randn(N, H, dk, dv, generator=gen) * s0_std).contiguous()
+    q, k, v, z, b, a = draw_raw_tokens(gen, [steps, N], H, dk, dv, dtype, gated, g_shift, beta_shift)
+    return RawInputs(q, k, v, z, a, b, None, S0, H, dk, dv, dtype)
 
 
 def varlen_lengths(seed: Optional[int] = None) -> List[int]:

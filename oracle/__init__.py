@@ -13,6 +13,11 @@ the KCP pair and its composition):
     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
     o_t = scale * S_t^T q_t,     y_t = o_t * sigmoid(z_t)  (gated)
 
+The fused input step (`gates`, `recurrence_fused`) forms the recurrence's
+inputs from raw ones in fp64: q and k scaled to unit length as
+x / sqrt(sum x^2 + eps), the log-decay g = g_min * sigmoid(a), beta =
+sigmoid(b); it then runs the same fp64 loop (dtype code F64: every input double).
+
 Every function here is pinned by the CPU tests (brute force, closed forms,
 invariants, the KCP identities); see the tests named test_oracle_*.
 """
@@ -31,7 +36,9 @@ _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
-BF16, F32 = 0, 1
+BF16, F32, F64 = 0, 1, 2
+G_MIN = -5.0          # lower bound of the log-decay (page "Exercices", Niveau 2 Q8)
+NORM_EPS = 1e-6       # x / sqrt(sum x^2 + eps) in the fused input step
 
 
 def build() -> str:
@@ -87,7 +94,9 @@ def _raw(t: Optional[torch.Tensor]):
         return BF16, t.view(torch.int16).numpy()
     if t.dtype == torch.float32:
         return F32, t.numpy()
-    raise TypeError(f"oracle inputs must be bf16 or fp32, got {t.dtype}")
+    if t.dtype == torch.float64:
+        return F64, t.numpy()
+    raise TypeError(f"oracle inputs must be bf16, fp32 or fp64, got {t.dtype}")
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -98,13 +107,21 @@ def _f32(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().to(torch.float32).numpy()
 
 
+def _gate(t: torch.Tensor, dt: int) -> np.ndarray:
+    """g or beta as the C oracle reads them: fp32, or fp64 when every input is fp64."""
+    if dt == F64:
+        return t.detach().cpu().contiguous().to(torch.float64).numpy()
+    return _f32(t)
+
+
 def recurrence(q, k, v, g, beta, cu_seqlens, z=None, S_init=None, scale: float = 1.0,
                chains: Optional[Sequence[Tuple[int, int]]] = None, want_y: bool = True,
                chain_states: Optional[np.ndarray] = None, nthreads: Optional[int] = None):
     """Sequential fp64 recurrence over packed sequences.
 
-    q, k: [T, H, dk]; v, z: [T, H, dv] (bf16 or fp32, same dtype);
-    g: [T, H, dk] fp32; beta: [T, H] fp32; cu_seqlens: [N+1] int.
+    q, k: [T, H, dk]; v, z: [T, H, dv] (bf16, fp32 or fp64, same dtype);
+    g: [T, H, dk], beta: [T, H]: fp32 (fp64 when q..z are fp64);
+    cu_seqlens: [N+1] int.
     S_init: [N, H, dk, dv] (any float dtype; widened to fp64) or None (zeros).
     chains: list of (seq, head) to run; None runs all of them.
     chain_states: fp64 [nchains, dk, dv] initial states in chain order
@@ -121,8 +138,8 @@ def recurrence(q, k, v, g, beta, cu_seqlens, z=None, S_init=None, scale: float =
         raise TypeError("q, k, v, z must share one dtype")
     T, H, dk = q.shape
     dv = v.shape[-1]
-    gn = _f32(g)
-    bn = _f32(beta)
+    gn = _gate(g, dt)
+    bn = _gate(beta, dt)
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     N = cu.size - 1
     if chains is None:
@@ -164,8 +181,8 @@ def kcp(q, k, v, g, beta, seg_bounds, z=None, S0=None, scale: float = 1.0, want_
     _, zn = _raw(z)
     T, H, dk = q.shape
     dv = v.shape[-1]
-    gn = _f32(g)
-    bn = _f32(beta)
+    gn = _gate(g, dt)
+    bn = _gate(beta, dt)
     sb = np.ascontiguousarray(np.asarray(seg_bounds, dtype=np.int64))
     nseg = sb.size - 1
     s0 = None
@@ -254,6 +271,45 @@ def replay(rep, scale: float = 1.0, nthreads: Optional[int] = None):
                            nthreads=nthreads)
         committed[n] = st
     return y.reshape(N, Td, H, dv), committed
+
+
+def gates(q_raw, k_raw, a, b, eps: float = NORM_EPS):
+    """The fused input step in fp64, from raw (unnormalised, pre-activation) inputs.
+
+    q_hat = q / sqrt(sum_c q_c^2 + eps), k_hat likewise (unit keys: page
+    "Exercices", Niveau 2 Q9; q is normalised the same way);
+    g = g_min * sigmoid(a) per key channel, in (g_min, 0) (bounded decay with
+    g_min = -5: same page, Q8, and the decay row of page "Ce qui est public et
+    ce qui ne l'est pas");
+    beta = sigmoid(b) per (token, head), in (0, 1) (the beta of the KDA
+    parametrisation, same table; W_beta, W_alpha are the low-rank projections
+    of page "Retrouver les 2,8 T de paramètres", Bloc 4).
+    Inputs are widened exactly; returns fp64 tensors (q_hat, k_hat, g, beta).
+    """
+    qd = q_raw.detach().cpu().to(torch.float64)
+    kd = k_raw.detach().cpu().to(torch.float64)
+    ad = a.detach().cpu().to(torch.float64)
+    bd = b.detach().cpu().to(torch.float64)
+    sig = lambda x: 1.0 / (1.0 + torch.exp(-x))
+    qh = qd / torch.sqrt((qd * qd).sum(-1, keepdim=True) + eps)
+    kh = kd / torch.sqrt((kd * kd).sum(-1, keepdim=True) + eps)
+    return qh.contiguous(), kh.contiguous(), (G_MIN * sig(ad)).contiguous(), sig(bd).contiguous()
+
+
+def _f64(t):
+    return None if t is None else t.detach().cpu().to(torch.float64).contiguous()
+
+
+def recurrence_fused(q_raw, k_raw, v, a, b, cu_seqlens, z=None, S_init=None, scale: float = 1.0,
+                     chains=None, want_y: bool = True, chain_states=None, nthreads=None):
+    """The recurrence fed by the fused input step: `gates` turns the raw inputs
+    into (q_hat, k_hat, g, beta) in fp64, v and z are widened exactly, and the
+    fp64 loop of `recurrence` runs on them.  Same arguments and returns as
+    `recurrence`, with q_raw, k_raw, a ([T, H, dk]) and b ([T, H]) in place of
+    q, k, g, beta."""
+    qh, kh, g, beta = gates(q_raw, k_raw, a, b)
+    return recurrence(qh, kh, _f64(v), g, beta, cu_seqlens, z=_f64(z), S_init=S_init, scale=scale,
+                      chains=chains, want_y=want_y, chain_states=chain_states, nthreads=nthreads)
 
 
 def compose(M2, S2, M1, S1):

@@ -45,6 +45,22 @@ def sequence(q, k, v, g, beta, z=None, S0=None, scale=1.0):
     return y, S
 
 
+def _sigmoid_tanh(x):
+    """sigmoid(x) = (1 + tanh(x / 2)) / 2, a route independent of exp."""
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def fused_sequence(q_raw, k_raw, v, a, b, z=None, S0=None, scale=1.0, eps=1e-6, g_min=-5.0):
+    """One head from raw inputs: unit q and k by x / hypot(||x||, sqrt(eps)),
+    g = g_min sigmoid(a), beta = sigmoid(b) (sigmoid through tanh), then
+    `sequence`.  q_raw, k_raw, a [T, dk]; v, z [T, dv]; b [T]."""
+    q_raw, k_raw, a, b = _np(q_raw), _np(k_raw), _np(a), _np(b)
+    se = np.sqrt(eps)
+    qh = np.stack([x / np.hypot(np.linalg.norm(x), se) for x in q_raw])
+    kh = np.stack([x / np.hypot(np.linalg.norm(x), se) for x in k_raw])
+    return sequence(qh, kh, v, g_min * _sigmoid_tanh(a), _sigmoid_tanh(b), z, S0, scale)
+
+
 def pair(k, v, g, beta):
     """KCP pair (M, Sloc) of one head's segment: M = A_T ... A_1, Sloc from zero."""
     k, v, g, beta = _np(k), _np(v), _np(g), _np(beta)

@@ -29,7 +29,10 @@
  * prefix over segments gives every segment its entering state.
  *
  * Inputs are read in place: bf16 values are given as their raw 16-bit
- * patterns and widened exactly; fp32 values are widened exactly.
+ * patterns and widened exactly; fp32 values are widened exactly.  With dtype
+ * KDAO_F64 every input (q, k, v, z and also g, beta) is double, which is how
+ * the fused-input path (gates and norms formed from raw inputs in double)
+ * reaches the same loop.
  */
 #include <math.h>
 #include <stdint.h>
@@ -41,6 +44,7 @@
 
 #define KDAO_BF16 0
 #define KDAO_F32 1
+#define KDAO_F64 2
 
 static double load_elt(int dtype, const void* base, int64_t i) {
     if (dtype == KDAO_BF16) {
@@ -49,8 +53,14 @@ static double load_elt(int dtype, const void* base, int64_t i) {
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dtype == KDAO_F64) return ((const double*)base)[i];
     return (double)((const float*)base)[i];
 }
+
+/* g and beta are fp32 unless the whole input set is double */
+static int gate_dtype(int dtype) { return dtype == KDAO_F64 ? KDAO_F64 : KDAO_F32; }
+
+static int dtype_ok(int dtype) { return dtype == KDAO_BF16 || dtype == KDAO_F32 || dtype == KDAO_F64; }
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
@@ -77,11 +87,11 @@ int kdao_max_threads(void) {
  * u has ncol entries.
  */
 static void token_step(int dtype, int dk, int ncol, double* X, const void* k, int64_t koff,
-                       const void* vt, int64_t voff, const float* g, int64_t goff, double beta,
+                       const void* vt, int64_t voff, const void* g, int64_t goff, double beta,
                        double* u) {
     /* (1) forget: row c scaled by alpha_c = exp(g_c) */
     for (int c = 0; c < dk; ++c) {
-        double a = exp((double)g[goff + c]);
+        double a = exp(load_elt(gate_dtype(dtype), g, goff + c));
         double* row = X + (int64_t)c * ncol;
         for (int j = 0; j < ncol; ++j) row[j] *= a;
     }
@@ -126,11 +136,12 @@ static void token_output(int dtype, int dk, int dv, const double* S, const void*
  * receives the outputs of those tokens when non-NULL.
  */
 static void run_tokens(int dtype, int H, int dk, int dv, double scale, int64_t t0, int64_t t1,
-                       int h, const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const void* z, double* S, double* y, double* u) {
+                       int h, const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const void* z, double* S, double* y, double* u) {
     for (int64_t t = t0; t < t1; ++t) {
         int64_t th = t * H + h;
-        token_step(dtype, dk, dv, S, k, th * dk, v, th * dv, g, th * dk, (double)beta[th], u);
+        token_step(dtype, dk, dv, S, k, th * dk, v, th * dv, g, th * dk,
+                   load_elt(gate_dtype(dtype), beta, th), u);
         if (y) token_output(dtype, dk, dv, S, q, th * dk, z, th * dv, scale, y + th * dv);
     }
 }
@@ -146,10 +157,10 @@ static void run_tokens(int dtype, int H, int dk, int dv, double scale, int64_t t
  * Returns 0, or -1 on an invalid argument.
  */
 int kdao_recurrence(int dtype, int num_seqs, const int32_t* cu_seqlens, int H, int dk, int dv,
-                    double scale, const void* q, const void* k, const void* v, const float* g,
-                    const float* beta, const void* z, int nchains, const int32_t* chains,
+                    double scale, const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, const void* z, int nchains, const int32_t* chains,
                     double* state, double* y, int nthreads) {
-    if (dtype != KDAO_BF16 && dtype != KDAO_F32) return -1;
+    if (!dtype_ok(dtype)) return -1;
     if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens || !state) return -1;
     if (!chains && nchains != num_seqs * H) return -1;
     set_threads(nthreads);
@@ -180,15 +191,16 @@ int kdao_recurrence(int dtype, int num_seqs, const int32_t* cu_seqlens, int H, i
  * state the segment builds from zero.
  */
 static void segment_pair(int dtype, int H, int dk, int dv, int64_t t0, int64_t t1, int h,
-                         const void* k, const void* v, const float* g, const float* beta,
+                         const void* k, const void* v, const void* g, const void* beta,
                          double* M, double* Sloc, double* u) {
     memset(M, 0, sizeof(double) * (size_t)dk * dk);
     for (int c = 0; c < dk; ++c) M[(int64_t)c * dk + c] = 1.0;
     memset(Sloc, 0, sizeof(double) * (size_t)dk * dv);
     for (int64_t t = t0; t < t1; ++t) {
         int64_t th = t * H + h;
-        token_step(dtype, dk, dk, M, k, th * dk, NULL, 0, g, th * dk, (double)beta[th], u);
-        token_step(dtype, dk, dv, Sloc, k, th * dk, v, th * dv, g, th * dk, (double)beta[th], u);
+        double b = load_elt(gate_dtype(dtype), beta, th);
+        token_step(dtype, dk, dk, M, k, th * dk, NULL, 0, g, th * dk, b, u);
+        token_step(dtype, dk, dv, Sloc, k, th * dk, v, th * dv, g, th * dk, b, u);
     }
 }
 
@@ -221,10 +233,10 @@ void kdao_compose(int dk, int dv, const double* M2, const double* S2, const doub
  * phase 2 folds the pairs in segment order, S <- M_i S + Sloc_i.
  */
 int kdao_kcp(int dtype, int64_t T, int H, int dk, int dv, double scale, const void* q,
-             const void* k, const void* v, const float* g, const float* beta, const void* z,
+             const void* k, const void* v, const void* g, const void* beta, const void* z,
              int nseg, const int64_t* seg_bounds, const double* S0, double* pairs_M,
              double* pairs_S, double* starts, double* final_state, double* y, int nthreads) {
-    if (dtype != KDAO_BF16 && dtype != KDAO_F32) return -1;
+    if (!dtype_ok(dtype)) return -1;
     if (nseg <= 0 || H <= 0 || dk <= 0 || dv <= 0 || !seg_bounds || !final_state) return -1;
     if (seg_bounds[0] != 0 || seg_bounds[nseg] != T) return -1;
     for (int i = 0; i < nseg; ++i)

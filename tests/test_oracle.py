@@ -388,3 +388,108 @@ def test_oracle_full_acceptance_equals_decode_steps(oracle_mod):
     y_last, _, st = oracle_mod.decode_steps(dec, 3)
     np.testing.assert_allclose(y[:, 2], y_last, rtol=0, atol=1e-13)
     np.testing.assert_allclose(committed.reshape(8, 8, 8), st, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- fused input step
+def _raw_tiny(lens, H=2, dk=8, dv=5, dtype="f32", gated=True, s0_std=0.3, seed=51, gs=0.0, bs=0.0):
+    return kda_inputs.make_raw_prefill(lens, H, dk, dv, dtype, gated, s0_std, seed, gs, bs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_oracle_fused_matches_brute_force(oracle_mod, dtype):
+    """Raw inputs through the fused step (norms, g = g_min sigmoid(a), beta =
+    sigmoid(b)) then the recurrence, against explicit matrices fed by an
+    independently written gate step (sigmoid through tanh, norm through hypot)."""
+    raw = _raw_tiny([9, 1, 23], H=3, dtype=dtype, gs=-1.0)
+    y, st = oracle_mod.recurrence_fused(raw.q, raw.k, raw.v, raw.a, raw.b, raw.cu_seqlens, z=raw.z,
+                                        S_init=raw.S0, scale=0.8)
+    cu = raw.cu_seqlens.tolist()
+    for n in range(3):
+        for h in range(3):
+            sl = slice(cu[n], cu[n + 1])
+            yb, Sb = brute.fused_sequence(raw.q[sl, h], raw.k[sl, h], raw.v[sl, h], raw.a[sl, h],
+                                          raw.b[sl, h], raw.z[sl, h], raw.S0[n, h], 0.8)
+            np.testing.assert_allclose(y[sl, h], yb, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(st[n * 3 + h], Sb, rtol=0, atol=1e-13)
+
+
+def test_oracle_gates_special_values(oracle_mod):
+    """sigmoid(0) = 1/2 gives g = g_min / 2 = -2.5 and beta = 1/2 exactly; the
+    decay stays inside (g_min, 0) and beta inside (0, 1); a unit vector keeps its
+    direction and a zero vector stays zero (no division by zero)."""
+    q = torch.zeros(4, 1, 3)
+    q[0, 0] = torch.tensor([3.0, 0.0, 4.0])
+    q[1, 0, 1] = -2.0
+    a = torch.tensor([[[0.0, 30.0, -30.0]]]).repeat(4, 1, 1)
+    b = torch.tensor([[0.0], [30.0], [-30.0], [1.0]])
+    qh, kh, g, beta = oracle_mod.gates(q, q, a, b)
+    assert g[0, 0, 0].item() == -2.5 and beta[0, 0].item() == 0.5
+    assert -5.0 < g.min().item() and g.max().item() < 0.0
+    assert 0.0 < beta.min().item() and beta.max().item() < 1.0
+    assert abs(g[0, 0, 1].item() + 5.0) < 1e-12 and abs(g[0, 0, 2].item()) < 1e-12
+    eps = oracle_mod.NORM_EPS
+    np.testing.assert_allclose(qh[0, 0].numpy(), np.array([3.0, 0.0, 4.0]) / math.sqrt(25.0 + eps),
+                               rtol=1e-15)
+    assert qh[1, 0, 1].item() == pytest.approx(-2.0 / math.sqrt(4.0 + eps), rel=1e-15)
+    assert torch.equal(qh[2], torch.zeros(1, 3, dtype=torch.float64))
+    assert torch.equal(kh, qh)
+
+
+def test_oracle_gates_match_library_routines(oracle_mod):
+    """Against torch's own normalize (x / max(||x||, eps)) and sigmoid: the two
+    norms differ only by eps / (2 ||x||^2), below 1e-8 relative here."""
+    gen = torch.Generator().manual_seed(52)
+    q = torch.randn(40, 3, 16, generator=gen, dtype=torch.float64) * 3
+    k = torch.randn(40, 3, 16, generator=gen, dtype=torch.float64)
+    a = torch.randn(40, 3, 16, generator=gen, dtype=torch.float64) * 4
+    b = torch.randn(40, 3, generator=gen, dtype=torch.float64) * 4
+    qh, kh, g, beta = oracle_mod.gates(q, k, a, b)
+    eps = oracle_mod.NORM_EPS
+    for x, xh in ((q, qh), (k, kh)):
+        ref = torch.nn.functional.normalize(x, dim=-1)
+        bound = ref.abs() * (eps / (2 * (x * x).sum(-1, keepdim=True))) * 1.001 + 1e-16
+        assert bool(((xh - ref).abs() <= bound).all())
+        assert float(((xh - ref).abs() / bound).max()) > 0.5      # the eps term is really there
+    np.testing.assert_allclose(g, -5.0 * torch.sigmoid(a), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(beta, torch.sigmoid(b), rtol=1e-14, atol=0)
+
+
+def test_oracle_fused_is_invariant_to_the_scale_of_q_and_k(oracle_mod):
+    """Only the directions of q and k matter (up to the eps of the norm)."""
+    raw = _raw_tiny([40], H=2, dk=8, dv=6, s0_std=0.2)
+    y1, s1 = oracle_mod.recurrence_fused(raw.q, raw.k, raw.v, raw.a, raw.b, raw.cu_seqlens,
+                                         z=raw.z, S_init=raw.S0)
+    y2, s2 = oracle_mod.recurrence_fused(raw.q * 8, raw.k * 2, raw.v, raw.a, raw.b,
+                                         raw.cu_seqlens, z=raw.z, S_init=raw.S0)
+    assert oracle_mod.rel_l2(y2, y1) < 1e-6 and oracle_mod.rel_l2(s2, s1) < 1e-6
+    assert oracle_mod.rel_l2(y2, y1) > 0          # eps does enter
+
+
+def test_oracle_fused_zero_keys_leave_only_the_decay(oracle_mod):
+    """k = 0 gives k_hat = 0: nothing is erased or written, so S_t =
+    Diag(exp(g_t)) S_{t-1} in closed form and o_t = scale S_t^T q_hat_t."""
+    raw = _raw_tiny([12], H=1, dk=4, dv=3, s0_std=0.5, gated=False)
+    k0 = torch.zeros_like(raw.k)
+    y, st = oracle_mod.recurrence_fused(raw.q, k0, raw.v, raw.a, raw.b, raw.cu_seqlens,
+                                        S_init=raw.S0, scale=1.5)
+    S = raw.S0[0, 0].double().numpy().copy()
+    for t in range(12):
+        at = raw.a[t, 0].double().numpy()
+        S = np.diag(np.exp(-5.0 / (1.0 + np.exp(-at)))) @ S
+        qt = raw.q[t, 0].double().numpy()
+        qh = qt / math.sqrt(float(qt @ qt) + 1e-6)
+        np.testing.assert_allclose(y[t, 0], 1.5 * S.T @ qh, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(st[0], S, rtol=1e-13, atol=1e-16)
+
+
+def test_raw_generator_shares_the_processed_draws():
+    """make_raw_prefill draws the very numbers make_prefill processes: normalising
+    its q, k and squashing its a, b in fp32 gives make_prefill's inputs."""
+    raw = kda_inputs.make_raw_prefill([30, 7], 2, 16, 8, "f32", True, 0.1, 53, 8.0, 4.0)
+    ref = kda_inputs.make_prefill([30, 7], 2, 16, 8, "f32", True, 0.1, 53, 8.0, 4.0)
+    assert torch.allclose(raw.q / raw.q.norm(dim=-1, keepdim=True), ref.q, atol=1e-6)
+    assert torch.equal(raw.v, ref.v) and torch.equal(raw.z, ref.z) and torch.equal(raw.S0, ref.S0)
+    assert torch.allclose(kda_inputs.G_MIN * torch.sigmoid(raw.a), ref.g, atol=1e-6)
+    assert torch.allclose(torch.sigmoid(raw.b), ref.beta, atol=1e-6)
+    dec = kda_inputs.make_raw_decode(3, 2, 8, 8, "bf16", True, 0.02, 2, 54)
+    assert dec.q.shape == (2, 3, 2, 8) and dec.b.shape == (2, 3, 2) and dec.a.dtype == torch.bfloat16
