@@ -27,7 +27,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
 ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode", "prefill_checkpoints",
-                 "decode_replay")
+                 "decode_replay", "prefill_fused_gates", "decode_fused_gates")
 
 
 def log(msg: str) -> None:
@@ -36,9 +36,11 @@ def log(msg: str) -> None:
 
 # ------------------------------------------------------------------ work model
 def prefill_bytes(tokens: int, H: int, dk: int, dv: int, elt: int, gated: bool,
-                  nseq: int, reads_s0: bool, writes_sT: bool) -> int:
-    """Algorithmic HBM bytes: every input read once, every output written once."""
-    per_th = 2 * dk * elt + dv * elt + (dv * elt if gated else 0) + dv * elt + dk * 4 + 4
+                  nseq: int, reads_s0: bool, writes_sT: bool, gate_elt: int = 4) -> int:
+    """Algorithmic HBM bytes: every input read once, every output written once.
+    gate_elt: bytes of a g / beta element (fp32 4; the fused entry points'
+    pre-activations a / b take the storage dtype)."""
+    per_th = 2 * dk * elt + dv * elt + (dv * elt if gated else 0) + dv * elt + (dk + 1) * gate_elt
     states = nseq * H * dk * dv * 4 * (int(reads_s0) + int(writes_sT))
     return tokens * H * per_th + states
 
@@ -49,9 +51,9 @@ def prefill_flops(tokens: int, H: int, dk: int, dv: int, C: int) -> float:
     return float(tokens) * H * 2 * (3 * dk * dv + C * (3 * dk + 2 * dv) / 2)
 
 
-def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int, gated: bool) -> int:
+def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int, gated: bool, gate_elt: int = 4) -> int:
     state = 2 * N * H * dk * dv * 4
-    inputs = N * H * (2 * dk * elt + dv * elt + (dv * elt if gated else 0) + dk * 4 + 4)
+    inputs = N * H * (2 * dk * elt + dv * elt + (dv * elt if gated else 0) + (dk + 1) * gate_elt)
     return state + inputs + N * H * dv * elt
 
 
@@ -132,11 +134,17 @@ def bench_cpu_baseline(args, inp, gpu_out, torch):
     heads = list(range(0, H, max(1, H // nh)))[:nh]
     threads = oracle.default_threads()
     log(f"cpu baseline: fp64 oracle on {len(heads)} of {H} heads, T={T}, {threads} threads")
-    t0 = time.perf_counter()
-    yo, so = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, z=inp.z,
-                               chains=[(0, h) for h in heads], nthreads=threads)
-    wall = time.perf_counter() - t0
-    log(f"cpu baseline: {wall:.2f} s")
+    # repeat the sample until about args.cpu_seconds of wall time have passed
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        yo, so = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, z=inp.z,
+                                   chains=[(0, h) for h in heads], nthreads=threads)
+        reps += 1
+        total = time.perf_counter() - t0
+        if total >= args.cpu_seconds or total / reps * (reps + 1) > 3 * args.cpu_seconds:
+            break
+    wall = total / reps
+    log(f"cpu baseline: {reps} runs, {wall:.2f} s each")
     y, fs = gpu_out
     yg = y.cpu().double().numpy()[:, heads]
     sg = fs.cpu().double().numpy()[0, heads]
@@ -145,7 +153,8 @@ def bench_cpu_baseline(args, inp, gpu_out, torch):
     cpu = {"value": T / (wall * H / len(heads)), "unit": "tokens/s", "cores": threads,
            "kind": "oracle",
            "sample": (f"{len(heads)} of {H} heads of k3_layer_prefill (T={T}, full chains), fp64 "
-                      f"sequential recurrence in C, {wall:.2f} s wall; value scaled to all {H} heads")}
+                      f"sequential recurrence in C, run {reps} times ({total:.1f} s wall, "
+                      f"{wall:.2f} s per run); value scaled to all {H} heads")}
     parity = {"heads": len(heads), "rel_l2_y": ey, "rel_l2_state": es, "tolerance": 2e-2}
     return cpu, parity
 
@@ -297,6 +306,70 @@ def bench_replay(args, torch, kda, kda_inputs, dev):
     return out
 
 
+def bench_prefill_fused(args, torch, kda, kda_inputs, dev):
+    """The K3 layer prefill from raw inputs (kda_chunk_fwd_fused): unnormalised
+    q, k and the gate pre-activations a, b in bf16; the kernel forms unit q, k,
+    g = -5 sigmoid(a) and beta = sigmoid(b)."""
+    w = kda_inputs.WORKLOADS[1]
+    H, dk, dv, T, C = w["H"], w["dk"], w["dv"], w["lens"][0], w["chunk"]
+    gen = torch.Generator(device=dev).manual_seed(kda_inputs.workload_seed(1))
+    bf = torch.bfloat16
+    d = dict(q=torch.randn(T, H, dk, generator=gen, device=dev).to(bf),
+             k=torch.randn(T, H, dk, generator=gen, device=dev).to(bf),
+             v=torch.randn(T, H, dv, generator=gen, device=dev).to(bf),
+             z=torch.randn(T, H, dv, generator=gen, device=dev).to(bf),
+             b=torch.randn(T, H, generator=gen, device=dev).to(bf),
+             a=torch.randn(T, H, dk, generator=gen, device=dev).to(bf))
+    y = torch.empty(T, H, dv, dtype=bf, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, C, 1, T),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_fwd_fused(d["q"], d["k"], d["v"], d["a"], d["b"], z=d["z"], chunk=C, y=y,
+                            final_state=fs, workspace=ws)
+
+    ms, _ = time_steps(step, args.steps, 2, torch)
+    nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True, gate_elt=2)
+    out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), bytes=nbytes,
+               gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               tflops=prefill_flops(T, H, dk, dv, C) / (ms * 1e-3) / 1e12)
+    del d, y, fs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode_fused(args, torch, kda, kda_inputs, dev):
+    """The decode workload from raw inputs (kda_decode_step_fused)."""
+    w = kda_inputs.WORKLOADS[4]
+    N, H, dk, dv, P = w["N"], w["H"], w["dk"], w["dv"], w["pool"]
+    steps = args.decode_steps
+    gen = torch.Generator(device=dev).manual_seed(kda_inputs.workload_seed(4))
+    bf = torch.bfloat16
+    state = torch.randn(N, H, dk, dv, generator=gen, device=dev) * w["s0_std"]
+    pool = [dict(q=torch.randn(N, H, dk, generator=gen, device=dev).to(bf),
+                 k=torch.randn(N, H, dk, generator=gen, device=dev).to(bf),
+                 v=torch.randn(N, H, dv, generator=gen, device=dev).to(bf),
+                 z=torch.randn(N, H, dv, generator=gen, device=dev).to(bf),
+                 b=torch.randn(N, H, generator=gen, device=dev).to(bf),
+                 a=torch.randn(N, H, dk, generator=gen, device=dev).to(bf)) for _ in range(P)]
+    y = torch.empty(N, H, dv, dtype=bf, device=dev)
+
+    def run_all():
+        for s in range(steps):
+            p = pool[s % P]
+            kda.decode_step_fused(p["q"], p["k"], p["v"], p["a"], p["b"], state, z=p["z"], y=y)
+
+    ms_all, _ = time_steps(run_all, 1, 1, torch)
+    ms = ms_all / steps
+    nbytes = decode_bytes(N, H, dk, dv, 2, True, gate_elt=2)
+    out = dict(ms_per_step=ms, steps=steps, tokens_per_s=N / (ms * 1e-3), bytes_per_step=nbytes,
+               gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del state, pool, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +379,8 @@ def main() -> int:
                     help="comma list of extra workloads (%s), 'all' or 'none'" % ",".join(ALL_WORKLOADS))
     ap.add_argument("--cpu-sample-heads", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time over which the CPU oracle sample is repeated")
     ap.add_argument("--decode-steps", type=int, default=1000,
                     help="decode steps timed as one loop (the workload runs 1000)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -340,7 +415,8 @@ def main() -> int:
     for name in extras:
         fn = {"varlen_prefill": bench_varlen, "kcp_long_sequence": bench_kcp,
               "decode": bench_decode, "prefill_checkpoints": bench_checkpoints,
-              "decode_replay": bench_replay}[name]
+              "decode_replay": bench_replay, "prefill_fused_gates": bench_prefill_fused,
+              "decode_fused_gates": bench_decode_fused}[name]
         workloads[name] = fn(args, torch, kda, kda_inputs, dev)
         log(f"{name}: {json.dumps(workloads[name])}")
     cpu, parity = (None, None)

@@ -33,7 +33,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 # Every symbol include/kda.h declares.
 SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
            "kda_chunk_fwd_checkpointed", "kda_kcp_workspace_size", "kda_kcp_scan",
-           "kda_decode_step", "kda_decode_replay")
+           "kda_decode_step", "kda_decode_replay", "kda_chunk_fwd_fused", "kda_decode_step_fused")
 
 
 class KDAError(RuntimeError):
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
+    L.kda_chunk_fwd_fused.argtypes = L.kda_chunk_fwd.argtypes
+    L.kda_chunk_fwd_fused.restype = i
     L.kda_chunk_fwd_checkpointed.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, i, vp, vp, i64, vp, sz, vp]
     L.kda_chunk_fwd_checkpointed.restype = i
@@ -75,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.kda_kcp_scan.restype = i
     L.kda_decode_step.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_decode_step.restype = i
+    L.kda_decode_step_fused.argtypes = L.kda_decode_step.argtypes
+    L.kda_decode_step_fused.restype = i
     L.kda_decode_replay.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_decode_replay.restype = i
     _lib = L
@@ -126,12 +130,16 @@ def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _check_inputs(q, k, v, g, beta, z):
+def _check_inputs(q, k, v, g, beta, z, fused: bool = False):
+    """fused: g, beta are the pre-activations a, b, in q's dtype."""
     dt = _dt(q)
     for name, t in (("k", k), ("v", v), ("z", z)):
         if t is not None and t.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype {q.dtype}")
-    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+    if fused:
+        if g.dtype != q.dtype or beta.dtype != q.dtype:
+            raise TypeError(f"a and b must have q's dtype {q.dtype}")
+    elif g.dtype != torch.float32 or beta.dtype != torch.float32:
         raise TypeError("g and beta must be float32")
     T, H, dk = q.shape
     dv = v.shape[-1]
@@ -154,7 +162,25 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=Non
               workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Prefill over packed sequences; returns (y, final_state or None).  The
     workspace (uint8 device tensor) is allocated when not given."""
-    dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    return _chunk_fwd(False, q, k, v, g, beta, cu_seqlens, z, initial_state, output_final_state,
+                      chunk, scale, y, final_state, workspace)
+
+
+def chunk_fwd_fused(q, k, v, a, b, cu_seqlens: Optional[torch.Tensor] = None, z=None,
+                    initial_state=None, output_final_state: bool = True, chunk: int = 64,
+                    scale: float = 1.0, y: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """chunk_fwd on raw inputs: q, k unnormalised, a [T, H, dk] and b [T, H] the
+    decay and beta pre-activations in q's dtype (g = -5 sigmoid(a), beta =
+    sigmoid(b), unit q and k formed in the kernel)."""
+    return _chunk_fwd(True, q, k, v, a, b, cu_seqlens, z, initial_state, output_final_state,
+                      chunk, scale, y, final_state, workspace)
+
+
+def _chunk_fwd(fused, q, k, v, g, beta, cu_seqlens, z, initial_state, output_final_state, chunk,
+               scale, y, final_state, workspace):
+    dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z, fused)
     dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state, workspace)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
@@ -174,11 +200,12 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=Non
         if need == 0:
             raise KDAError("kda_chunk_fwd_workspace_size", 2)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = lib().kda_chunk_fwd(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens), _ptr(q),
-                             _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
-                             _ptr(initial_state), _ptr(final_state), _ptr(y), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(dev))
-    _check("kda_chunk_fwd", st)
+    fn = "kda_chunk_fwd_fused" if fused else "kda_chunk_fwd"
+    st = getattr(lib(), fn)(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens), _ptr(q),
+                            _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                            _ptr(initial_state), _ptr(final_state), _ptr(y), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(fn, st)
     return y, final_state
 
 
@@ -241,15 +268,27 @@ def decode_step(q, k, v, g, beta, state, z=None, scale: float = 1.0,
                 y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One token per request; q, k, g: [N, H, dk], v, z: [N, H, dv], beta [N, H],
     state fp32 [N, H, dk, dv] updated in place.  Returns y [N, H, dv]."""
-    dt, N, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    return _decode_step(False, q, k, v, g, beta, state, z, scale, y)
+
+
+def decode_step_fused(q, k, v, a, b, state, z=None, scale: float = 1.0,
+                      y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_step on raw inputs (q, k unnormalised; a [N, H, dk], b [N, H] the
+    gate pre-activations in q's dtype)."""
+    return _decode_step(True, q, k, v, a, b, state, z, scale, y)
+
+
+def _decode_step(fused, q, k, v, g, beta, state, z, scale, y):
+    dt, N, H, dk, dv = _check_inputs(q, k, v, g, beta, z, fused)
     dev = _dev(q, k, v, g, beta, z, state, y)
     if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
         raise ValueError("state must be float32 [N, H, dk, dv]")
     if y is None:
         y = torch.empty(N, H, dv, dtype=q.dtype, device=dev)
-    st = lib().kda_decode_step(dt, N, H, dk, dv, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                               _ptr(beta), _ptr(z), _ptr(state), _ptr(y), _stream(dev))
-    _check("kda_decode_step", st)
+    fn = "kda_decode_step_fused" if fused else "kda_decode_step"
+    st = getattr(lib(), fn)(dt, N, H, dk, dv, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                            _ptr(beta), _ptr(z), _ptr(state), _ptr(y), _stream(dev))
+    _check(fn, st)
     return y
 
 

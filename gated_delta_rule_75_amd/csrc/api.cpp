@@ -112,9 +112,10 @@ size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chu
 namespace {
 
 // kda_chunk_fwd, optionally saving the state every ckpt_interval tokens.
-kda_status chunk_fwd_impl(kda_dtype dt, int H, int dk, int dv, int chunk, float scale, int num_seqs,
+// fused: q, k are raw and g, beta are the pre-activations a, b in dtype dt.
+kda_status chunk_fwd_impl(kda_dtype dt, bool fused, int H, int dk, int dv, int chunk, float scale, int num_seqs,
                           int64_t T_total, const int32_t* cu_seqlens, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, const void* z,
+                          const void* v, const void* g, const void* beta, const void* z,
                           const float* initial_state, float* final_state, void* y, int ckpt_interval,
                           float* checkpoints, int32_t* ckpt_offsets, int64_t ckpt_capacity,
                           void* workspace, size_t workspace_bytes, void* stream) {
@@ -135,8 +136,10 @@ kda_status chunk_fwd_impl(kda_dtype dt, int H, int dk, int dv, int chunk, float 
         if (!aligned(checkpoints, 16) || !aligned(ckpt_offsets, 4)) return KDA_ERR_INVALID_ARGUMENT;
     }
     const size_t ea = vec_align(dt);
+    // g in runs of four fp32 (fused: a in runs of four elements), beta one scalar per (token, head)
+    const size_t ga = fused ? ea : 16, ba = fused ? (dt == KDA_BF16 ? 2 : 4) : 4;
     if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
-        !aligned(y, ea) || !aligned(g, 16) || !aligned(beta, 4) || !aligned(cu_seqlens, 4) ||
+        !aligned(y, ea) || !aligned(g, ga) || !aligned(beta, ba) || !aligned(cu_seqlens, 4) ||
         !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256))
         return KDA_ERR_INVALID_ARGUMENT;
     const int64_t nchunks = cu_seqlens ? varlen_chunks(T_total, chunk, num_seqs)
@@ -159,6 +162,7 @@ kda_status chunk_fwd_impl(kda_dtype dt, int H, int dk, int dv, int chunk, float 
     a.v = v;
     a.g = g;
     a.beta = beta;
+    a.fused = fused;
     a.z = z;
     a.initial_state = initial_state;
     a.final_state = final_state;
@@ -188,6 +192,40 @@ kda_status chunk_fwd_impl(kda_dtype dt, int H, int dk, int dv, int chunk, float 
     return from_hip(kda::launch_chunk_state(a, chunk_off, order));
 }
 
+// kda_decode_step; fused: q, k raw and g, beta the pre-activations a, b in dtype dt.
+kda_status decode_impl(kda_dtype dt, bool fused, int N, int H, int dk, int dv, float scale, const void* q,
+                       const void* k, const void* v, const void* g, const void* beta, const void* z,
+                       float* state, void* y, void* stream) {
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
+    if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)N * H > (int64_t)1 << 30) return KDA_ERR_INVALID_ARGUMENT;
+    if (!head_shape_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (N > 0 && (!q || !k || !v || !g || !beta || !state || !y)) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t ea = elt_align(dt);
+    const size_t ga = fused ? ea : 8, ba = fused ? (dt == KDA_BF16 ? 2 : 4) : 4;
+    if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
+        !aligned(y, ea) || !aligned(g, ga) || !aligned(beta, ba) || !aligned(state, 16))
+        return KDA_ERR_INVALID_ARGUMENT;
+    kda::DecodeArgs a{};
+    a.dtype = (int)dt;
+    a.N = N;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.fused = fused;
+    a.z = z;
+    a.state = state;
+    a.y = y;
+    a.stream = stream;
+    return from_hip(kda::launch_decode(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,7 +236,18 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
                          const float* beta, const void* z, const float* initial_state,
                          float* final_state, void* y, void* workspace, size_t workspace_bytes,
                          void* stream) {
-    return chunk_fwd_impl(dt, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta, z,
+    return chunk_fwd_impl(dt, false, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta,
+                          z, initial_state, final_state, y, 0, nullptr, nullptr, 0, workspace, workspace_bytes,
+                          stream);
+}
+
+kda_status kda_chunk_fwd_fused(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                               int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                               const void* q, const void* k, const void* v, const void* a,
+                               const void* b, const void* z, const float* initial_state,
+                               float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return chunk_fwd_impl(dt, true, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, a, b, z,
                           initial_state, final_state, y, 0, nullptr, nullptr, 0, workspace, workspace_bytes,
                           stream);
 }
@@ -211,7 +260,7 @@ kda_status kda_chunk_fwd_checkpointed(kda_dtype dt, int H, int dk, int dv, int c
                                       int32_t* ckpt_offsets, int64_t ckpt_capacity, void* workspace,
                                       size_t workspace_bytes, void* stream) {
     if (ckpt_interval <= 0) return KDA_ERR_INVALID_ARGUMENT;
-    return chunk_fwd_impl(dt, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta, z,
+    return chunk_fwd_impl(dt, false, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta, z,
                           initial_state, final_state, y, ckpt_interval, checkpoints, ckpt_offsets,
                           ckpt_capacity, workspace, workspace_bytes, stream);
 }
@@ -304,32 +353,14 @@ kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float sca
                            const void* q, const void* k, const void* v, const float* g,
                            const float* beta, const void* z, float* state, void* y,
                            void* stream) {
-    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
-    if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
-    if ((int64_t)N * H > (int64_t)1 << 30) return KDA_ERR_INVALID_ARGUMENT;
-    if (!head_shape_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
-    if (N > 0 && (!q || !k || !v || !g || !beta || !state || !y)) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t ea = elt_align(dt);
-    if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea) || !aligned(z, ea) ||
-        !aligned(y, ea) || !aligned(g, 8) || !aligned(beta, 4) || !aligned(state, 16))
-        return KDA_ERR_INVALID_ARGUMENT;
-    kda::DecodeArgs a{};
-    a.dtype = (int)dt;
-    a.N = N;
-    a.H = H;
-    a.dk = dk;
-    a.dv = dv;
-    a.scale = scale;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.z = z;
-    a.state = state;
-    a.y = y;
-    a.stream = stream;
-    return from_hip(kda::launch_decode(a));
+    return decode_impl(dt, false, N, H, dk, dv, scale, q, k, v, g, beta, z, state, y, stream);
+}
+
+kda_status kda_decode_step_fused(kda_dtype dt, int N, int H, int dk, int dv, float scale,
+                                 const void* q, const void* k, const void* v, const void* a,
+                                 const void* b, const void* z, float* state, void* y,
+                                 void* stream) {
+    return decode_impl(dt, true, N, H, dk, dv, scale, q, k, v, a, b, z, state, y, stream);
 }
 
 kda_status kda_decode_replay(kda_dtype dt, int N, int Td, int H, int dk, int dv, float scale,

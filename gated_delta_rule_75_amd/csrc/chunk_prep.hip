@@ -19,6 +19,15 @@
 //  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA.
 // Qt, Kh and gam leave straight from the decay phase; the tiles of W, U and
 // P leave as they are produced.
+//
+// The FUSED variant takes raw inputs instead: q and k of any length, the
+// decay pre-activation a (in the storage dtype) in place of g, and the beta
+// pre-activation b in place of beta.  Phase 1 then forms g = g_min sigmoid(a)
+// while loading, beta = sigmoid(b), and scales each token's q and k to unit
+// length (unit keys: page "Exercices", Niveau 2 Q9; the low-rank W_alpha and
+// W_beta that produce a and b: page "Retrouver les 2,8 T de paramètres",
+// Bloc 4).  The squared norms are summed over the lanes of a wave by
+// shuffles and across waves through LDS that phase 2 later reuses.
 #include "launch.h"
 #include "twopass.h"
 
@@ -31,12 +40,13 @@ struct PrepParams {
     const int32_t* cu_seqlens;
     const int32_t* chunk_off;  // [num_seqs + 1] chunk offsets of packed sequences, or NULL
     const void *q, *k, *v;
-    const float *g, *beta;
+    const void *g, *beta;   // fp32 g and beta, or (FUSED) the pre-activations a, b in the storage dtype
     TwoPassBufs ws;
 };
 
-template <typename E_, int DK_, int CH_>
+template <typename E_, int DK_, int CH_, bool FUSED_>
 struct PrepCfg {
+    static constexpr bool FUSED = FUSED_;
     using E = E_;
     using K = KBlk<E_>;
     using T = typename E::T;
@@ -70,6 +80,13 @@ struct PrepCfg {
     static constexpr size_t O_BETA = O_D + (size_t)(ND > 0 ? ND : 1) * DK * 4;
     static constexpr size_t BYTES = O_BETA + (size_t)CH * 4;
     static_assert(BYTES <= 160 * 1024, "LDS");
+    // FUSED: per-wave partial squared norms of k and q, [2][NW][CH] fp32, on the L blocks
+    // and the inverse norms, [2][CH], on the L^{-1} blocks
+    static_assert(!FUSED || 2 * NW * CH * 4 <= NPAIR * BLK * 4, "norm scratch");
+    static_assert(!FUSED || (2 * CH * 4 <= NPAIR * BLK * 4 && CH <= 64 && NW >= 2), "inverse norms");
+    // waves per SIMD the LDS allows (2 workgroups of 8 waves per CU at 80 KB
+    // or less): the register budget is held to match
+    static constexpr int WPE = BYTES <= 80 * 1024 ? (2 * NTHR / 64 + 3) / 4 : 1;
 };
 
 __device__ __forceinline__ int pair_index(int a, int b) { return a * (a + 1) / 2 + b; }
@@ -86,9 +103,18 @@ __device__ __forceinline__ void st4(__bf16* p, float a, float b, float c, float 
 __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
 }
+// four elements kept in the storage type between phases (half the registers at bf16)
+template <typename T> struct Vec4;
+template <> struct Vec4<__bf16> { using type = bf16x4_t; };
+template <> struct Vec4<float> { using type = f32x4_t; };
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::type pack4(float a, float b, float c, float d) {
+    return typename Vec4<T>::type{from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
+}
 
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::WPE)))
+void chunk_prep_kernel(PrepParams p) {
     using E = typename C::E;
     using K = typename C::K;
     using T = typename C::T;
@@ -156,23 +182,63 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
     const T* gq = static_cast<const T*>(p.q);
     const T* gk = static_cast<const T*>(p.k);
     const T* gv = static_cast<const T*>(p.v);
-    f32x4_t G[TPT], kx[TPT], qx[TPT], vx[TPT];
+    using T4 = typename Vec4<T>::type;
+    f32x4_t G[TPT], kx[TPT], qx[TPT];
+    T4 vx[TPT];  // v stays in the storage type until phase 3
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
         const int t = tl0 + i;
         const bool ok = t < nvalid;
         const int64_t row = (ts + (ok ? t : 0)) * H + h;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(p.g + row * DK + c0);
+        f32x4_t gg;
+        if constexpr (C::FUSED) {
+            const f32x4_t aa = ld4f(static_cast<const T*>(p.g) + row * DK + c0);
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) gg[ch] = decay_gate(aa[ch]);
+        } else {
+            gg = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + row * DK + c0);
+        }
         const f32x4_t kk = ld4f(gk + row * DK + c0);
         const f32x4_t qq = ld4f(gq + row * DK + c0);
-        const f32x4_t vv = ld4f(gv + row * DV + c0);
+        const T4 vv = *reinterpret_cast<const T4*>(gv + row * DV + c0);
         G[i] = ok ? gg : zero;
         kx[i] = ok ? kk : zero;
         qx[i] = ok ? qq : zero;
-        vx[i] = ok ? vv : zero;
+        vx[i] = ok ? vv : T4{};
     }
-    if (tid < CH) sBeta[tid] = tid < nvalid ? p.beta[(ts + tid) * H + h] : 0.f;
+    if (tid < CH) {
+        float b = 0.f;
+        if (tid < nvalid) {
+            const int64_t at = (ts + tid) * H + h;
+            if constexpr (C::FUSED) b = sigmoid(to_f32(static_cast<const T*>(p.beta)[at]));
+            else b = static_cast<const float*>(p.beta)[at];
+        }
+        sBeta[tid] = b;
+    }
+    float* sNorm = sL;  // FUSED: [2][NW][CH] partial squared norms (k, then q)
+    if constexpr (C::FUSED) {
+        // this thread's 4 channels, then the CGW lanes of a token group, then
+        // one partial per wave in LDS
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                sk += kx[i][ch] * kx[i][ch];
+                sq += qx[i][ch] * qx[i][ch];
+            }
+#pragma unroll
+            for (int d = 1; d < CGW; d <<= 1) {
+                sk += __shfl_xor(sk, d, 64);
+                sq += __shfl_xor(sq, d, 64);
+            }
+            if (cg == 0) {
+                sNorm[wave * CH + tl0 + i] = sk;
+                sNorm[(NW + wave) * CH + tl0 + i] = sq;
+            }
+        }
+    }
 
     // running sum over the thread's tokens, then over the wave's token groups
 #pragma unroll
@@ -220,8 +286,27 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
             }
         st4(gam + c0, __expf(GC[0]), __expf(GC[1]), __expf(GC[2]), __expf(GC[3]));
     }
+    if constexpr (C::FUSED) {
+        // waves 0 and 1 sum the partials of k and q, one token per lane, into
+        // inverse norms (on the L^{-1} blocks, unused until phase 3)
+        float* sInv = sZ;  // [2][CH]
+        __syncthreads();
+        if (wave < 2 && lane < CH) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) s2 += sNorm[(wave * NW + w) * CH + lane];
+            sInv[wave * CH + lane] = rsqrtf(s2 + kNormEps);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            kx[i] *= sInv[tl0 + i];
+            qx[i] *= sInv[CH + tl0 + i];
+        }
+    }
     const float scale = p.scale;
     f32x4_t kh[TPT];
+    T4 kw[TPT];  // K e^G, the W operand, in the storage type until phase 3
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
         const int t = tl0 + i;
@@ -237,8 +322,9 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
             kc[ch] = kx[i][ch] * ec;
             qt[ch] = scale * qx[i][ch] * eg;
             kh[i][ch] = kx[i][ch] * __expf(GC[ch] - Gv);
-            kx[i][ch] *= eg;  // K e^G, the W operand
+            kx[i][ch] *= eg;
         }
+        kw[i] = pack4<T>(kx[i][0], kx[i][1], kx[i][2], kx[i][3]);
         st4(sKr + t * LK + c0, kr[0], kr[1], kr[2], kr[3]);
         st4(sQr + t * LK + c0, qr[0], qr[1], qr[2], qr[3]);
         st4(sKc + t * LK + c0, kc[0], kc[1], kc[2], kc[3]);
@@ -334,14 +420,14 @@ __global__ __launch_bounds__(C::NTHR) void chunk_prep_kernel(PrepParams p) {
         if constexpr (TPT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < TPT; i += 4) {
-                st4(kt + i, kx[i][ch], kx[i + 1][ch], kx[i + 2][ch], kx[i + 3][ch]);
-                st4(vt + i, vx[i][ch], vx[i + 1][ch], vx[i + 2][ch], vx[i + 3][ch]);
+                *reinterpret_cast<T4*>(kt + i) = T4{kw[i][ch], kw[i + 1][ch], kw[i + 2][ch], kw[i + 3][ch]};
+                *reinterpret_cast<T4*>(vt + i) = T4{vx[i][ch], vx[i + 1][ch], vx[i + 2][ch], vx[i + 3][ch]};
             }
         } else {
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
-                kt[i] = from_f32<T>(kx[i][ch]);
-                vt[i] = from_f32<T>(vx[i][ch]);
+                kt[i] = kw[i][ch];
+                vt[i] = vx[i][ch];
             }
         }
     }
@@ -458,10 +544,16 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
     return hipGetLastError();
 }
 
+template <class E, int DK, bool FUSED>
+static hipError_t launch_prep_chunk(const TwoPassArgs& a, const int32_t* co, int64_t nb) {
+    if (a.chunk == 64) return launch_prep_cfg<PrepCfg<E, DK, 64, FUSED>>(a, co, nb);
+    return launch_prep_cfg<PrepCfg<E, DK, 16, FUSED>>(a, co, nb);
+}
+
 template <class E, int DK>
 static hipError_t launch_prep_dk(const TwoPassArgs& a, const int32_t* co, int64_t nb) {
-    if (a.chunk == 64) return launch_prep_cfg<PrepCfg<E, DK, 64>>(a, co, nb);
-    return launch_prep_cfg<PrepCfg<E, DK, 16>>(a, co, nb);
+    if (a.fused) return launch_prep_chunk<E, DK, true>(a, co, nb);
+    return launch_prep_chunk<E, DK, false>(a, co, nb);
 }
 
 hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks) {

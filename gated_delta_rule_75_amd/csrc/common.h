@@ -120,4 +120,10 @@ __device__ __forceinline__ f32x2_t gload2(const float* p) {
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// Fused input step: unit q and k as x / sqrt(sum x^2 + kNormEps), the
+// log-decay g = kGMin * sigmoid(a) in (kGMin, 0), beta = sigmoid(b).
+constexpr float kGMin = -5.0f;
+constexpr float kNormEps = 1e-6f;
+__device__ __forceinline__ float decay_gate(float a) { return kGMin * sigmoid(a); }
+
 }  // namespace kda

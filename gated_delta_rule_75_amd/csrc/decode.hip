@@ -19,12 +19,20 @@
 
 namespace kda {
 
-template <typename T, int DK, int DV>
+//
+// FUSED: q and k arrive unnormalised and the gates as pre-activations a (per
+// key channel) and b (per head), in the storage dtype: alpha = exp(g_min
+// sigmoid(a)), beta = sigmoid(b), and the unit vectors k^ = k / |k|,
+// q^ = q / |q| (|x| = sqrt(sum x^2 + eps)).  The reductions run on the raw
+// k, q and are rescaled afterwards: S^T k^ = (S^T k) / |k|, the write uses
+// k (delta / |k|), and k^.q^ = (k.q) / (|k| |q|); the norms come from the same
+// wave-0 reduction as k.q.
+template <typename T, int DK, int DV, bool FUSED>
 __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
-                                                     const float* __restrict__ g,
-                                                     const float* __restrict__ beta,
+                                                     const void* __restrict__ gp,
+                                                     const void* __restrict__ betap,
                                                      const T* __restrict__ z,
                                                      float* __restrict__ state, T* __restrict__ y) {
     constexpr int CG = DV / 4;      // float4 column groups per row
@@ -35,7 +43,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
     __shared__ float s_u[RG][DV + 4], s_w[RG][DV + 4];
     __shared__ float s_delta[DV];
-    __shared__ float s_kq;
+    __shared__ float s_kq, s_ik, s_iq;
 
     const int nh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -53,15 +61,37 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
     for (int c = tid; c < DK; c += 256) {
         s_k[c] = gload(k + kb + c);
         s_q[c] = gload(q + kb + c);
-        s_a[c] = fast_exp(g[kb + c]);
+        if constexpr (FUSED) s_a[c] = fast_exp(decay_gate(gload(static_cast<const T*>(gp) + kb + c)));
+        else s_a[c] = fast_exp(static_cast<const float*>(gp)[kb + c]);
     }
     __syncthreads();
     if (tid < kWave) {
-        float p = 0.f;
-        for (int c = tid; c < DK; c += kWave) p += s_k[c] * s_q[c];
+        float p = 0.f, pk = 0.f, pq = 0.f;
+        for (int c = tid; c < DK; c += kWave) {
+            p += s_k[c] * s_q[c];
+            if constexpr (FUSED) {
+                pk += s_k[c] * s_k[c];
+                pq += s_q[c] * s_q[c];
+            }
+        }
 #pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
-        if (tid == 0) s_kq = p;
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+            p += __shfl_xor(p, off);
+            if constexpr (FUSED) {
+                pk += __shfl_xor(pk, off);
+                pq += __shfl_xor(pq, off);
+            }
+        }
+        if (tid == 0) {
+            if constexpr (FUSED) {
+                const float ik = rsqrtf(pk + kNormEps), iq = rsqrtf(pq + kNormEps);
+                s_ik = ik;
+                s_iq = iq;
+                s_kq = p * ik * iq;
+            } else {
+                s_kq = p;
+            }
+        }
     }
     f32x4_t u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -85,8 +115,17 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
             U += s_u[r][j];
             W += s_w[r][j];
         }
-        const float d = beta[nh] * (gload(v + vb + j) - U);
-        s_delta[j] = d;
+        float bt, ik = 1.f;
+        if constexpr (FUSED) {
+            bt = sigmoid(gload(static_cast<const T*>(betap) + nh));
+            ik = s_ik;
+            U *= ik;
+            W *= s_iq;
+        } else {
+            bt = static_cast<const float*>(betap)[nh];
+        }
+        const float d = bt * (gload(v + vb + j) - U);
+        s_delta[j] = d * ik;   // the write adds k (d / |k|)^T = k^ d^T
         float o = scale * (W + s_kq * d);
         if (z) o *= sigmoid(gload(z + vb + j));
         gstore(y + vb + j, o);
@@ -210,7 +249,8 @@ static hipError_t launch_replay_t(const DecodeArgs& a, int Td, const int32_t* ac
     if (a.N == 0) return hipSuccess;
     hipLaunchKernelGGL((replay_kernel<T, DK, DV>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
                        (hipStream_t)a.stream, Td, a.scale, a.H, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, a.g, a.beta, (const T*)a.z, accepted, a.state, (T*)a.y);
+                       (const T*)a.v, (const float*)a.g, (const float*)a.beta, (const T*)a.z, accepted,
+                       a.state, (T*)a.y);
     return hipGetLastError();
 }
 
@@ -226,7 +266,13 @@ hipError_t launch_replay(const DecodeArgs& a, int Td, const int32_t* accepted) {
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     if (a.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
+    if (a.fused) {
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
+                           (hipStream_t)a.stream, a.scale, a.H, (const T*)a.q, (const T*)a.k,
+                           (const T*)a.v, a.g, a.beta, (const T*)a.z, a.state, (T*)a.y);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
                        (hipStream_t)a.stream, a.scale, a.H, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, a.g, a.beta, (const T*)a.z, a.state, (T*)a.y);
     return hipGetLastError();

@@ -14,7 +14,8 @@ struct DecodeArgs {
     int N, H, dk, dv;
     float scale;
     const void *q, *k, *v;
-    const float *g, *beta;
+    const void *g, *beta;  // fp32 g, beta; fused: pre-activations a, b in the storage dtype
+    bool fused;            // raw q, k (normalised in the kernel) and gate pre-activations
     const void* z;
     float* state;
     void* y;
@@ -39,7 +40,8 @@ struct TwoPassArgs {
     const int32_t* cu_seqlens;  // device offsets, or NULL: sequence n spans
     int64_t seg_len;            //   [n*seg_len, min((n+1)*seg_len, T_total))
     const void *q, *k, *v;
-    const float *g, *beta;
+    const void *g, *beta;        // fp32 g, beta; fused: pre-activations a, b in the storage dtype
+    bool fused;                  // raw q, k (normalised in the kernel) and gate pre-activations
     const void* z;
     const float* initial_state;  // [num_seqs, H, dk, dv] or NULL
     float* final_state;          // see final_seq_lo; mode 2: [num_seqs, H, dk, dk + dv]

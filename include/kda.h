@@ -33,7 +33,8 @@
  * bytes; kda_decode_step needs 4 bytes (bf16) or 8 bytes (fp32) and g 8.
  * States are 16-byte aligned, workspaces 256-byte aligned.
  *
- * Preconditions (documented, not checked on the hot path):
+ * Preconditions (documented, not checked on the hot path; the *_fused entry
+ * points establish the first three themselves from raw inputs):
  *   - q and k are L2-normalised per (token, head): page "Exercices",
  *     Niveau 2 Q9 -- with unit keys I - beta k k^T does not expand the state;
  *   - g lies in [g_min, 0] with g_min = -5 (page "Exercices", Niveau 2 Q8:
@@ -111,6 +112,34 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
                          const float* beta, const void* z, const float* initial_state,
                          float* final_state, void* y, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * kda_chunk_fwd_fused -- kda_chunk_fwd fed by the layer's raw projections, with
+ * the input-side step fused into the chunk-preparation kernel (page "Ce qui
+ * est public et ce qui ne l'est pas", table "Entièrement publié": the KDA
+ * parametrisation (q, k, v, beta, z) and the bounded decay with g_min = -5;
+ * page "Retrouver les 2,8 T de paramètres", Bloc 4: beta and alpha come from
+ * the low-rank projections W_beta, W_alpha; page "Exercices", Niveau 2 Q9:
+ * unit keys).  Per (token, head) the kernel forms
+ *     k^ = k / sqrt(sum_c k_c^2 + 1e-6)      q^ likewise
+ *     g  = -5 sigmoid(a)  (per key channel, in (-5, 0))
+ *     beta = sigmoid(b)
+ * in fp32 and runs kda_chunk_fwd's recurrence on (q^, k^, v, g, beta, z).
+ *
+ *   q, k             [T_total, H, dk] in dtype dt, any length (a zero vector
+ *                    stays zero).
+ *   a                [T_total, H, dk] in dtype dt: decay pre-activation
+ *                    (aligned like q).  Half the bytes of an fp32 g at bf16.
+ *   b                [T_total, H] in dtype dt: beta pre-activation (aligned to
+ *                    one element).
+ *   all other arguments, the workspace and its size: as kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_fused(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                               int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                               const void* q, const void* k, const void* v, const void* a,
+                               const void* b, const void* z, const float* initial_state,
+                               float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd
@@ -202,6 +231,21 @@ kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float sca
                            const void* q, const void* k, const void* v, const float* g,
                            const float* beta, const void* z, float* state, void* y,
                            void* stream);
+
+/*
+ * kda_decode_step_fused -- kda_decode_step on raw inputs: the fused input step
+ * of kda_chunk_fwd_fused (unit q, k; g = g_min sigmoid(a); beta = sigmoid(b))
+ * inside the decode kernel.
+ *
+ *   q, k             [N, H, dk] in dtype dt, any length (zero gives zero).
+ *   a                [N, H, dk] in dtype dt: decay pre-activation.
+ *   b                [N, H] in dtype dt: beta pre-activation.
+ *   all other arguments: as kda_decode_step (a aligned like q; b to one element).
+ */
+kda_status kda_decode_step_fused(kda_dtype dt, int N, int H, int dk, int dv, float scale,
+                                 const void* q, const void* k, const void* v, const void* a,
+                                 const void* b, const void* z, float* state, void* y,
+                                 void* stream);
 
 /*
  * kda_decode_replay -- speculative decoding: Td draft tokens per request

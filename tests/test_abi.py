@@ -180,3 +180,36 @@ def test_decode_replay_rejects_bad_arguments(L):
     assert rp(acc=ctypes.c_void_p((1 << 20) + 2)) == INVALID
     assert rp(dk=96, dv=96) == UNSUPPORTED
     assert rp(N=0) == OK                          # no requests: nothing launched
+
+
+def test_fused_entry_points_reject_bad_arguments(L):
+    def fw(dt=BF16, a=P, b=P, q=P, dk=128, chunk=64, ws=P):
+        return L.kda_chunk_fwd_fused(dt, 2, dk, dk, chunk, 1.0, 1, 64, None, q, P, P, a, b, None,
+                                     None, None, P, ws, 1 << 40, None)
+    assert fw(dt=9) == INVALID
+    assert fw(a=None) == INVALID
+    assert fw(b=None) == INVALID
+    assert fw(a=ctypes.c_void_p((1 << 20) + 4)) == INVALID            # a in runs of 4 bf16: 8 bytes
+    assert fw(dt=F32, a=ctypes.c_void_p((1 << 20) + 8)) == INVALID    # fp32 runs of 4: 16 bytes
+    assert fw(b=ctypes.c_void_p((1 << 20) + 1)) == INVALID            # b: one element
+    assert fw(dt=F32, b=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert fw(ws=None) == INVALID
+    assert fw(dk=96) == UNSUPPORTED
+    assert fw(chunk=32) == UNSUPPORTED
+
+    def dec(dt=BF16, a=P, b=P, N=4, dk=128):
+        return L.kda_decode_step_fused(dt, N, 2, dk, dk, 1.0, P, P, P, a, b, None, P, P, None)
+    assert dec(a=None) == INVALID
+    assert dec(b=ctypes.c_void_p((1 << 20) + 1)) == INVALID
+    assert dec(dt=F32, a=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert dec(N=-1) == INVALID
+    assert dec(dk=96) == UNSUPPORTED
+    assert dec(N=0) == OK                                              # nothing launched
+
+
+def test_binding_checks_fused_dtypes():
+    import torch
+    q = torch.zeros(4, 1, 64)
+    with pytest.raises(TypeError):    # a must have q's dtype, not fp32 g beside bf16 q
+        kda._check_inputs(q.bfloat16(), q.bfloat16(), q.bfloat16(), q, torch.zeros(4, 1).bfloat16(),
+                          None, fused=True)

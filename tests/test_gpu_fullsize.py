@@ -3,6 +3,8 @@ times, on outputs the oracle can compute one chain at a time.
 
 - K3-layer prefill (H=96, T=8192): every output and final state of 4 heads
   (plus the chunk-scale long-memory variant).
+- The same layer through the fused-input entry point (raw q, k, gate
+  pre-activations): every output and final state of 3 heads.
 - Varlen prefill (16 sequences, lengths in [512, 8192], H=96): 3 sampled
   (sequence, head) chains, including the longest and the shortest sequence.
 - KCP scan (T=2^20, H=4, 256 segments, segment-scale long-memory draw so the
@@ -49,6 +51,26 @@ def test_k3_layer_prefill_full_size(kda, stress):
     ey = rel_l2(y.cpu()[:, heads].double().numpy(), yo[:, heads])
     es = rel_l2(fs.cpu()[0, heads].double().numpy(), so)
     log(f"[fullsize] k3 layer prefill {stress}: y={ey:.3e} state={es:.3e}")
+    assert ey <= BF16_TOL and es <= BF16_TOL
+
+
+def test_k3_layer_prefill_fused_full_size(kda):
+    """kda_chunk_fwd_fused at the K3 layer shape from raw inputs (the draws of
+    the plain workload before normalisation and squashing)."""
+    w = kda_inputs.WORKLOADS[1]
+    raw = kda_inputs.make_raw_prefill(w["lens"], w["H"], w["dk"], w["dv"], w["dtype"], True, 0.0,
+                                      kda_inputs.workload_seed(1))
+    dev = torch.device("cuda")
+    y, fs = kda.chunk_fwd_fused(raw.q.to(dev), raw.k.to(dev), raw.v.to(dev), raw.a.to(dev),
+                                raw.b.to(dev), z=raw.z.to(dev), chunk=64)
+    torch.cuda.synchronize()
+    heads = [0, 50, 95]
+    pick = lambda t: t[:, heads].contiguous()
+    yo, so = oracle.recurrence_fused(pick(raw.q), pick(raw.k), pick(raw.v), pick(raw.a),
+                                     pick(raw.b), raw.cu_seqlens, z=pick(raw.z))
+    ey = rel_l2(y.cpu()[:, heads].double().numpy(), yo)
+    es = rel_l2(fs.cpu()[0, heads].double().numpy(), so)
+    log(f"[fullsize] k3 layer fused prefill: y={ey:.3e} state={es:.3e}")
     assert ey <= BF16_TOL and es <= BF16_TOL
 
 
