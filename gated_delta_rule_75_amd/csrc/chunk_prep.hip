@@ -3,9 +3,13 @@
 // workspace layout are described in twopass.h).
 //
 // One workgroup (8 waves; 4 for dk = 64 with 16-token chunks) per (chunk, head):
-//  1. decay: each thread holds TPT consecutive tokens x 4 consecutive channels
-//     of g, k, q, v; the in-chunk running sum G of g is a per-thread sum plus
-//     a shuffle scan over the wave's token groups.
+//  1. decay: a wave owns 64 channels of a slice of consecutive tokens, so each
+//     load instruction reads whole 128-byte rows (a layout with fewer channels
+//     per wave touched four times the cache lines per byte); a thread holds
+//     TPT consecutive tokens x 4 consecutive channels of g, k, q, v.  The
+//     in-chunk running sum G of g is a per-thread sum, a shuffle scan over
+//     the wave's token groups, and a sum of the earlier slices' totals
+//     exchanged through LDS.
 //  2. gated Gram products A (k.k, strictly lower) and P (q.k, lower) on MFMA.
 //     The factor e^{G_t - G_j} is split at 16-token sub-tile references so no
 //     operand exceeds e^{16 |g_min|}: page "Exercices", Niveau 2 Q8 sizes
@@ -19,6 +23,10 @@
 //  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA.
 // Qt, Kh and gam leave straight from the decay phase; the tiles of W, U and
 // P leave as they are produced.
+//
+// Waves share data only through LDS, so the barriers between phases wait for
+// LDS operations alone; the global stores of each phase (and loads still in
+// flight) drain in the background instead of at every barrier.
 //
 // The FUSED variant takes raw inputs instead: q and k of any length, the
 // decay pre-activation a (in the storage dtype) in place of g, and the beta
@@ -56,10 +64,15 @@ struct PrepCfg {
     static constexpr int NKT = CP / K::KB;                  // k-blocks over tokens
     static constexpr int NPM = pm_frags(NT, NKT, K::KB);    // stored fragments of Pm
     static constexpr int NW = (DK == 64 && CH == 16) ? 4 : 8, NTHR = 64 * NW;
-    // decay-phase mapping: wave w owns channels [w DK/NW, (w+1) DK/NW); lane =
-    // (token group tg, channel group cg) holds TPT tokens x 4 channels
-    static constexpr int CGW = DK / (4 * NW), TGW = 64 / CGW, TPT = CH / TGW;
-    static_assert(TPT >= 1 && TPT * TGW == CH && 16 % TPT == 0, "decay mapping");
+    // decay-phase mapping: wave w owns 64 channels (channel set w % NWC) of
+    // TPW consecutive tokens (token slice w / NWC); lane = (token group tg,
+    // channel group cg) holds TPT consecutive tokens x 4 channels, so one load
+    // instruction reads TGW whole 64-channel rows
+    static constexpr int CGW = 16, TGW = 64 / CGW;
+    static constexpr int NWC = DK / 64, NTS = NW / NWC, TPW = CH / NTS, TPT = TPW / TGW;
+    static constexpr int SPT = 16 / TPW;   // token slices per 16-token sub-tile
+    static_assert(NWC * 64 == DK && NTS * NWC == NW && TPT >= 1 && TPT * TGW == TPW && TPW * SPT == 16,
+                  "decay mapping");
     static constexpr int PADE = 16 / (int)sizeof(T);
     static constexpr int LK = DK + PADE;  // pitch of [token][channel] tables
     static constexpr int LC = CP + PADE;  // pitch of [row][token] tables
@@ -78,11 +91,12 @@ struct PrepCfg {
     static constexpr int ND = NT * (NT - 1) / 2;
     static constexpr size_t O_D = O_Z + (size_t)NPAIR * BLK * 4;   // e^{R_a - R_b}, a > b
     static constexpr size_t O_BETA = O_D + (size_t)(ND > 0 ? ND : 1) * DK * 4;
-    static constexpr size_t BYTES = O_BETA + (size_t)CH * 4;
+    static constexpr size_t O_TOT = O_BETA + (size_t)CH * 4;   // per-slice sums of g, [NTS][DK]
+    static constexpr size_t BYTES = O_TOT + (size_t)NTS * DK * 4;
     static_assert(BYTES <= 160 * 1024, "LDS");
-    // FUSED: per-wave partial squared norms of k and q, [2][NW][CH] fp32, on the L blocks
-    // and the inverse norms, [2][CH], on the L^{-1} blocks
-    static_assert(!FUSED || 2 * NW * CH * 4 <= NPAIR * BLK * 4, "norm scratch");
+    // FUSED: partial squared norms of k and q per channel set, [2][NWC][CH]
+    // fp32, on the L blocks, and the inverse norms, [2][CH], on the L^{-1} blocks
+    static_assert(!FUSED || 2 * NWC * CH * 4 <= NPAIR * BLK * 4, "norm scratch");
     static_assert(!FUSED || (2 * CH * 4 <= NPAIR * BLK * 4 && CH <= 64 && NW >= 2), "inverse norms");
     // waves per SIMD the LDS allows (2 workgroups of 8 waves per CU at 80 KB
     // or less): the register budget is held to match
@@ -176,9 +190,11 @@ void chunk_prep_kernel(PrepParams p) {
     float* gam = p.ws.gam + wsb * DK;
 
     // ---- 1. loads and decay ----------------------------------------------------
+    constexpr int NTS = C::NTS, TPW = C::TPW, SPT = C::SPT;
+    const int cset = wave % C::NWC, tsl = wave / C::NWC;   // wave-uniform
     const int tg = lane / CGW, cg = lane % CGW;
-    const int c0 = wave * (DK / NW) + 4 * cg;
-    const int tl0 = tg * TPT;
+    const int c0 = cset * 64 + 4 * cg;
+    const int tl0 = tsl * TPW + tg * TPT;
     const T* gq = static_cast<const T*>(p.q);
     const T* gk = static_cast<const T*>(p.k);
     const T* gv = static_cast<const T*>(p.v);
@@ -216,10 +232,10 @@ void chunk_prep_kernel(PrepParams p) {
         }
         sBeta[tid] = b;
     }
-    float* sNorm = sL;  // FUSED: [2][NW][CH] partial squared norms (k, then q)
+    float* sNorm = sL;  // FUSED: [2][NWC][CH] partial squared norms (k, then q)
     if constexpr (C::FUSED) {
         // this thread's 4 channels, then the CGW lanes of a token group, then
-        // one partial per wave in LDS
+        // one partial per (channel set, token) in LDS
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             float sk = 0.f, sq = 0.f;
@@ -234,15 +250,17 @@ void chunk_prep_kernel(PrepParams p) {
                 sq += __shfl_xor(sq, d, 64);
             }
             if (cg == 0) {
-                sNorm[wave * CH + tl0 + i] = sk;
-                sNorm[(NW + wave) * CH + tl0 + i] = sq;
+                sNorm[cset * CH + tl0 + i] = sk;
+                sNorm[(C::NWC + cset) * CH + tl0 + i] = sq;
             }
         }
     }
 
-    // running sum over the thread's tokens, then over the wave's token groups
+    // running sum over the thread's tokens, then over the wave's token groups,
+    // then over the token slices before this wave's (slice sums through LDS)
 #pragma unroll
     for (int i = 1; i < TPT; ++i) G[i] += G[i - 1];
+    float* sTot = reinterpret_cast<float*>(smem + C::O_TOT);   // [NTS][DK]
     {
         f32x4_t inc = G[TPT - 1];
 #pragma unroll
@@ -255,27 +273,29 @@ void chunk_prep_kernel(PrepParams p) {
         const f32x4_t ex = inc - G[TPT - 1];
 #pragma unroll
         for (int i = 0; i < TPT; ++i) G[i] += ex;
+        if (tg == TGW - 1) *reinterpret_cast<f32x4_t*>(sTot + tsl * DK + c0) = inc;
     }
-    // sub-tile references R_b = G at token 16 b - 1 (R_0 = 0) and G_C
+    barrier_keep_loads();
+    // sub-tile references R_b = G at token 16 b - 1 (R_0 = 0), the sum over
+    // the slices before this one, and G_C
     f32x4_t Rb[NT], Ro, GC;
-#pragma unroll
-    for (int b = 0; b < NT; ++b) {
-        const int src = (b == 0 ? 0 : (16 * b) / TPT - 1) * CGW + cg;
-#pragma unroll
-        for (int ch = 0; ch < 4; ++ch) Rb[b][ch] = __shfl(G[TPT - 1][ch], src, 64);
-        if (b == 0) Rb[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
     {
-        const int a = tl0 / 16;
-        const int src = (a == 0 ? 0 : (16 * a) / TPT - 1) * CGW + cg;
+        f32x4_t run = {0.f, 0.f, 0.f, 0.f}, pre = run;
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-            Ro[ch] = __shfl(G[TPT - 1][ch], src, 64);
-            GC[ch] = __shfl(G[TPT - 1][ch], (TGW - 1) * CGW + cg, 64);
+        for (int sl = 0; sl < NTS; ++sl) {
+            if (sl % SPT == 0) Rb[sl / SPT] = run;
+            if (sl == tsl) pre = run;
+            run += *reinterpret_cast<const f32x4_t*>(sTot + sl * DK + c0);
         }
-        if (a == 0) Ro = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        GC = run;
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) G[i] += pre;
+        Ro = Rb[0];
+#pragma unroll
+        for (int a = 1; a < NT; ++a)
+            if (tsl / SPT == a) Ro = Rb[a];
     }
-    if (tg == 0) {
+    if (tsl == 0 && tg == 0) {
 #pragma unroll
         for (int a = 1; a < NT; ++a)
 #pragma unroll
@@ -290,14 +310,13 @@ void chunk_prep_kernel(PrepParams p) {
         // waves 0 and 1 sum the partials of k and q, one token per lane, into
         // inverse norms (on the L^{-1} blocks, unused until phase 3)
         float* sInv = sZ;  // [2][CH]
-        __syncthreads();
         if (wave < 2 && lane < CH) {
             float s2 = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) s2 += sNorm[(wave * NW + w) * CH + lane];
+            for (int w = 0; w < C::NWC; ++w) s2 += sNorm[(wave * C::NWC + w) * CH + lane];
             sInv[wave * CH + lane] = rsqrtf(s2 + kNormEps);
         }
-        __syncthreads();
+        barrier_keep_loads();
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             kx[i] *= sInv[tl0 + i];
@@ -368,7 +387,7 @@ void chunk_prep_kernel(PrepParams p) {
             Pm[frag_elem<K>(pm_frag_index(a, j / K::KB, C::NKT, K::KB), t, j)] = from_f32<T>(0.f);
         }
     }
-    __syncthreads();
+    barrier_keep_loads();
 
     // ---- 2. gated Gram products -------------------------------------------------
     for (int task = wave; task < C::NPAIR; task += NW) {
@@ -410,7 +429,7 @@ void chunk_prep_kernel(PrepParams p) {
         const int j0 = 16 * b + 4 * g4;
         st4(Pm + frag_elem<K>(pm_frag_index(a, j0 / K::KB, C::NKT, K::KB), l16, j0), pv[0], pv[1], pv[2], pv[3]);
     }
-    __syncthreads();
+    barrier_keep_loads();
 
     // ---- 3. operands of W and U; inverse of L ----------------------------------
 #pragma unroll
@@ -454,7 +473,7 @@ void chunk_prep_kernel(PrepParams p) {
             for (int t = 0; t < 16; ++t) Zb[t * 17 + l16] = x[t];
         }
     }
-    __syncthreads();
+    barrier_keep_loads();
     // off-diagonal blocks, level l = a - b: wave b forms M = sum_{b<=c<a} L_ac X_cb
     // and X_ab = -X_aa M with fp32 MFMAs (16x16x4, four per 16-wide reduction);
     // M stays in the accumulator and feeds the second product directly, MFMA i
@@ -480,7 +499,7 @@ void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) Zab[(4 * g4 + i) * 17 + l16] = -x[i];
         }
-        __syncthreads();
+        barrier_keep_loads();
     }
     // L^{-1} diag(beta), zero above the diagonal blocks and past C
     for (int idx = tid; idx < CH * CP; idx += NTHR) {
@@ -490,7 +509,7 @@ void chunk_prep_kernel(PrepParams p) {
         if (j < CH && b <= a) x = sZ[pair_index(a, b) * BLK + (t & 15) * 17 + (j & 15)] * sBeta[j];
         sLB[t * LC + j] = from_f32<T>(x);
     }
-    __syncthreads();
+    barrier_keep_loads();
 
     // ---- 4. W^T = (K e^G)^T (L^{-1} diag(beta))^T and U = L^{-1} diag(beta) V ----
     for (int task = wave; task < NCT * NT; task += NW) {

@@ -24,6 +24,14 @@
 //
 // The workgroups of one chain take ids with equal residue mod 8, which places
 // them on one XCD, so they share the chunk operands through its L2.
+//
+// Loader waves.  When two buffers of the chunk operands plus the workgroup's
+// U^T tiles fit in LDS (one value tile per wave), two extra waves do all the
+// staging: they issue the global-to-LDS copies of chunk c+1 right after the
+// barrier that opens chunk c, wait for them, and meet the compute waves at
+// the next barrier.  A wave that issues a 1 KiB copy stalls until the memory
+// pipeline takes it, so the compute waves, which now issue only their 8-byte
+// z loads and the y stores, no longer lose those cycles.
 #include <type_traits>
 
 #include "launch.h"
@@ -56,7 +64,7 @@ struct StCfg {
     using T = typename K::T;
     static constexpr int DK = DK_, DV = DV_, CH = CH_, NVT = NVT_, MODE = MODE_;
     static constexpr bool AUG = MODE_ == kModePairs;
-    static constexpr int NW = 4, NTHR = 64 * NW;
+    static constexpr int NW = 4;
     static constexpr int CW = 16 * NVT * NW;            // state columns per workgroup
     static constexpr int NTT = CH / 16, NCT = DK / 16;
     static constexpr int KB = K::KB, TPB = K::TPB;
@@ -73,9 +81,22 @@ struct StCfg {
     static constexpr int F_G = F_P + N_P;               // gam: dk fp32, repeated to fill 1 KiB
     static constexpr int NF = F_G + 1;
     static constexpr int FPW = (NF + NW - 1) / NW;      // fragment loads per wave
-    static constexpr int BUF = NF * 1024;
-    static constexpr int NBUF = 2 * BUF <= 150 * 1024 ? 2 : 1;
+    // U^T of the workgroup's columns: NW NVT value tiles x NTT token tiles in
+    // accumulator layout (64 lanes x 4 elements each), after the fragments
+    static constexpr int UTT = 64 * 4 * (int)sizeof(T);  // bytes of one U^T tile
+    static constexpr int UTB = NW * NVT * NTT * UTT;
+    static_assert(UTB % 1024 == 0, "U^T in whole 1 KiB copies");
+    // loader wave (with two value tiles per wave the compute waves' registers
+    // are at the 256 limit already; they keep staging their own operands)
+    static constexpr bool LW = NVT == 1 && 2 * (NF * 1024 + UTB) <= 150 * 1024;
+    static constexpr int BUF = NF * 1024 + (LW ? UTB : 0);
+    static constexpr int NBUF = LW || 2 * BUF <= 150 * 1024 ? 2 : 1;
     static constexpr int BYTES = NBUF * BUF;
+    // loader waves: two (one to four measure alike; the copy rate of one wave
+    // alone is about half that of two)
+    static constexpr int NLW = LW ? 2 : 0;
+    static constexpr int NCOPY = NF + UTB / 1024;            // 1 KiB copies per chunk
+    static constexpr int NTHR = 64 * (NW + NLW);
 };
 
 template <typename T> struct VecT4;
@@ -103,19 +124,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that leaves global loads in flight.  __syncthreads()
-// waits for every outstanding vector-memory operation (its fence covers the
-// direct-to-LDS prefetch too); here the caller waits for exactly the loads it
-// needs.  Pending LDS reads finish first, so no wave still reads a buffer
-// that another wave's prefetch overwrites after the barrier; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_keep_loads() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 template <class C>
@@ -155,6 +163,65 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     int nch = len > 0 ? (int)((len + CH - 1) / CH) : 0;
     if (cbase + nch > p.chunk_cap) nch = cbase < p.chunk_cap ? p.chunk_cap - cbase : 0;
     const int dvt = p.dvt;
+    // first value tile (16 columns of v / U) of the workgroup; negative for
+    // the transition columns of mode 2, whose waves take no values
+    const int vt_wg = (vg * C::CW - (C::AUG ? DK : 0)) / 16;
+
+    if constexpr (C::LW) {
+        if (wave >= NW) {
+            // ---- loader waves: chunk c+1 into buffer (c+1) % 2 during chunk c ----
+            constexpr int FB = 64 * KPL * (int)sizeof(T);   // bytes of one fragment (1 KiB)
+            static_assert(FB == 1024, "fragment size");
+            const char* wn = static_cast<const char*>(p.ws.wn) + 16 * lane;
+            const char* qt = static_cast<const char*>(p.ws.qt) + 16 * lane;
+            const char* kh = static_cast<const char*>(p.ws.kht) + 16 * lane;
+            const char* pm = static_cast<const char*>(p.ws.pm) + 16 * lane;
+            const char* gm = reinterpret_cast<const char*>(p.ws.gam) + 16 * (lane % (DK / 4));
+            const char* ut = static_cast<const char*>(p.ws.ut) + 16 * lane;
+            // copy k of a chunk: fragment k (k < NF) or U^T copy k - NF; loader
+            // li takes copies [li NCOPY / NLW, (li + 1) NCOPY / NLW)
+            const int li = wave - NW;
+            const int k0 = li * C::NCOPY / C::NLW, k1 = (li + 1) * C::NCOPY / C::NLW;
+            auto stage_all = [&](int c, int b) {
+                const int64_t wsb = (int64_t)(cbase + c) * H + h;
+                char* buf = smem + b * C::BUF;
+                const char* aw = wn + wsb * (int64_t)(CH * DK * sizeof(T));
+                const char* aq = qt + wsb * (int64_t)(CH * DK * sizeof(T));
+                const char* ak = kh + wsb * (int64_t)(DK * CP * sizeof(T));
+                const char* ap = pm + wsb * (int64_t)(C::NPM * FB);
+                const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
+                const char* au = ut + wsb * (int64_t)(DV * CH * sizeof(T));
+                constexpr int TPC = 1024 / C::UTT;   // U^T tiles per copy
+#pragma unroll
+                for (int k = 0; k < C::NCOPY; ++k) {
+                    if (k < k0 || k >= k1) continue;
+                    const char* src;
+                    if (k < C::F_Q) src = aw + (k - C::F_W) * FB;
+                    else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
+                    else if (k < C::F_P) src = ak + (k - C::F_K) * FB;
+                    else if (k < C::F_G) src = ap + (k - C::F_P) * FB;
+                    else if (k == C::F_G) src = ag;
+                    else {
+                        // U^T tiles [vt_wg, vt_wg + NW NVT) x all token tiles, contiguous;
+                        // transition tiles (vt < 0) copy a valid tile nobody reads
+                        const int lt = (k - C::NF) * TPC;   // first (wave tile, token tile)
+                        int g = vt_wg + lt / NTT;
+                        g = g < 0 ? 0 : g;
+                        src = au + (int64_t)(g * NTT + lt % NTT) * C::UTT;
+                    }
+                    lds_dma16(src, buf + k * 1024);
+                }
+            };
+            if (nch > 0) stage_all(0, 0);
+            for (int c = 0; c < nch; ++c) {
+                wait_vmcnt<0>();            // chunk c has landed
+                barrier_keep_loads();       // ... and the compute waves are done with chunk c-1
+                if (c + 1 < nch) stage_all(c + 1, (c + 1) % 2);
+            }
+            return;
+        }
+    }
+
     const int colw = vg * C::CW + wave * 16 * NVT;  // first state column of the wave
     const bool ident = C::AUG && colw < DK;         // transition columns: start I, values 0
     const int vcol0 = C::AUG ? colw - DK : colw;    // its first column of v / z / y
@@ -241,13 +308,15 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     auto load_uz = [&](int c) {
         const int64_t wsb = (int64_t)(cbase + c) * H + h;
         const T* UT = static_cast<const T*>(p.ws.ut) + wsb * (DV * CH);
+        if constexpr (!C::LW) {
 #pragma unroll
-        for (int ta = 0; ta < NTT; ++ta)
+            for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) {
-                const int vtg = ident ? 0 : vcol0 / 16 + vt;   // value tile of the U^T block
-                ut[ta][vt] = *reinterpret_cast<const T4*>(UT + ((vtg * NTT + ta) * 64 + lane) * 4);
-            }
+                for (int vt = 0; vt < NVT; ++vt) {
+                    const int vtg = ident ? 0 : vcol0 / 16 + vt;   // value tile of the U^T block
+                    ut[ta][vt] = *reinterpret_cast<const T4*>(UT + ((vtg * NTT + ta) * 64 + lane) * 4);
+                }
+        }
         if (!C::AUG && gz) {
             const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
 #pragma unroll
@@ -281,7 +350,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     };
 
     if (nch > 0) {
-        stage(0, 0, J_0{}, J_E{});
+        if constexpr (!C::LW) stage(0, 0, J_0{}, J_E{});
         load_uz(0);
     }
     for (int c = 0; c < nch; ++c) {
@@ -294,13 +363,22 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
-                utc[ta][vt] = ut[ta][vt];
+                if constexpr (!C::LW) utc[ta][vt] = ut[ta][vt];
                 zzc[ta][vt] = zz[ta][vt];
             }
         const int nvalid = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
         // every wave's part of chunk c has landed, and every wave is done with
         // the buffer the next chunk goes to
         barrier_keep_loads();
+        if constexpr (C::LW) {
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+                    utc[ta][vt] = *reinterpret_cast<const T4*>(buf + C::NF * 1024 +
+                                                               ((wave * NVT + vt) * NTT + ta) * C::UTT +
+                                                               lane * 4 * (int)sizeof(T));
+        }
 
         // Delta = U + Wn S
         Frag sf[NKC][NVT];
@@ -325,7 +403,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         if constexpr (!C::AUG) {
             if (yd_nvalid > 0) store_y();
         }
-        if constexpr (C::NBUF == 2) stage(cn, nb, J_0{}, J_H{});
+        if constexpr (C::NBUF == 2 && !C::LW) stage(cn, nb, J_0{}, J_H{});
         Frag df[NKT][NVT];
 #pragma unroll
         for (int u = 0; u < NKT; ++u)
@@ -351,7 +429,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             }
         }
         if constexpr (C::NBUF == 2) {
-            stage(cn, nb, J_H{}, J_E{});
+            if constexpr (!C::LW) stage(cn, nb, J_H{}, J_E{});
             load_uz(cn);
         }
         if constexpr (!C::AUG) {

@@ -120,6 +120,21 @@ __device__ __forceinline__ f32x2_t gload2(const float* p) {
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// Workgroup barrier that leaves global loads and stores in flight.
+// __syncthreads() waits for every outstanding vector-memory operation (its
+// fence covers global stores and direct-to-LDS copies too); kernels whose
+// waves share data only through LDS need just their LDS operations finished.
+// Pending LDS reads finish first, so no wave still reads a buffer that
+// another wave overwrites after the barrier; the empty asm statements keep
+// the compiler from moving memory accesses across it.  A caller that needs a
+// global-to-LDS copy to have landed waits for it (s_waitcnt vmcnt) first.
+__device__ __forceinline__ void barrier_keep_loads() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Fused input step: unit q and k as x / sqrt(sum x^2 + kNormEps), the
 // log-decay g = kGMin * sigmoid(a) in (kGMin, 0), beta = sigmoid(b).
 constexpr float kGMin = -5.0f;
