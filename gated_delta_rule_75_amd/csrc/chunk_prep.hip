@@ -207,13 +207,13 @@ void chunk_prep_kernel(PrepParams p) {
         const bool ok = t < nvalid;
         const int64_t row = (ts + (ok ? t : 0)) * H + h;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t gg;
+        f32x4_t gg;   // log-decay in base 2: every exponential below is one v_exp_f32
         if constexpr (C::FUSED) {
             const f32x4_t aa = ld4f(static_cast<const T*>(p.g) + row * DK + c0);
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) gg[ch] = decay_gate(aa[ch]);
+            for (int ch = 0; ch < 4; ++ch) gg[ch] = decay_gate(aa[ch]) * kLog2e;
         } else {
-            gg = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + row * DK + c0);
+            gg = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + row * DK + c0) * kLog2e;
         }
         const f32x4_t kk = ld4f(gk + row * DK + c0);
         const f32x4_t qq = ld4f(gq + row * DK + c0);
@@ -302,9 +302,9 @@ void chunk_prep_kernel(PrepParams p) {
             for (int b = 0; b < a; ++b) {
                 float* d = sD + (a * (a - 1) / 2 + b) * DK + c0;
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) d[ch] = __expf(Rb[a][ch] - Rb[b][ch]);
+                for (int ch = 0; ch < 4; ++ch) d[ch] = exp2_fast(Rb[a][ch] - Rb[b][ch]);
             }
-        st4(gam + c0, __expf(GC[0]), __expf(GC[1]), __expf(GC[2]), __expf(GC[3]));
+        st4(gam + c0, exp2_fast(GC[0]), exp2_fast(GC[1]), exp2_fast(GC[2]), exp2_fast(GC[3]));
     }
     if constexpr (C::FUSED) {
         // waves 0 and 1 sum the partials of k and q, one token per lane, into
@@ -323,7 +323,17 @@ void chunk_prep_kernel(PrepParams p) {
             qx[i] *= sInv[CH + tl0 + i];
         }
     }
+    // two exponentials per element, e^{G - R} <= 1 and e^{R - G} <= e^80 (R the
+    // sub-tile reference); e^G and e^{G_C - G} follow by per-channel factors
+    // e^R <= 1 and e^{G_C - R} <= 1
     const float scale = p.scale;
+    f32x4_t eR, eCR, sR;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+        eR[ch] = exp2_fast(Ro[ch]);
+        eCR[ch] = exp2_fast(GC[ch] - Ro[ch]);
+        sR[ch] = scale * eR[ch];
+    }
     f32x4_t kh[TPT];
     T4 kw[TPT];  // K e^G, the W operand, in the storage type until phase 3
 #pragma unroll
@@ -332,16 +342,15 @@ void chunk_prep_kernel(PrepParams p) {
         f32x4_t kr, qr, kc, qt;
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
-            const float Gv = G[i][ch];
-            const float er = __expf(Gv - Ro[ch]);   // <= 1
-            const float ec = __expf(Ro[ch] - Gv);   // <= e^80
-            const float eg = __expf(Gv);
+            const float d = G[i][ch] - Ro[ch];
+            const float er = exp2_fast(d);    // e^{G - R}
+            const float ec = exp2_fast(-d);   // e^{R - G}
             kr[ch] = kx[i][ch] * er;
             qr[ch] = qx[i][ch] * er;
             kc[ch] = kx[i][ch] * ec;
-            qt[ch] = scale * qx[i][ch] * eg;
-            kh[i][ch] = kx[i][ch] * __expf(GC[ch] - Gv);
-            kx[i][ch] *= eg;
+            qt[ch] = qr[ch] * sR[ch];         // scale q e^G
+            kh[i][ch] = kc[ch] * eCR[ch];     // k e^{G_C - G}
+            kx[i][ch] = kr[ch] * eR[ch];      // k e^G
         }
         kw[i] = pack4<T>(kx[i][0], kx[i][1], kx[i][2], kx[i][3]);
         st4(sKr + t * LK + c0, kr[0], kr[1], kr[2], kr[3]);

@@ -118,6 +118,9 @@ __device__ __forceinline__ f32x2_t gload2(const float* p) {
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+// 2^x in one v_exp_f32
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Workgroup barrier that leaves global loads and stores in flight.
