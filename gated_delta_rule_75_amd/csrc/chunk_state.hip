@@ -30,8 +30,13 @@
 // staging: they issue the global-to-LDS copies of chunk c+1 right after the
 // barrier that opens chunk c, wait for them, and meet the compute waves at
 // the next barrier.  A wave that issues a 1 KiB copy stalls until the memory
-// pipeline takes it, so the compute waves, which now issue only their 8-byte
-// z loads and the y stores, no longer lose those cycles.
+// pipeline takes it, so the compute waves, which now issue only their z
+// loads and y stores, no longer lose those cycles.  Those move as whole
+// 128-byte rows: each compute wave loads its share of the next chunk's z rows
+// into registers and writes them into a z tile in LDS at the top of that
+// chunk; outputs go into a y tile and leave as whole rows after the next
+// barrier.  (Per-lane accesses in the accumulator layout touched 16 lines
+// for 32 bytes each.)
 #include <type_traits>
 
 #include "launch.h"
@@ -86,12 +91,21 @@ struct StCfg {
     static constexpr int UTT = 64 * 4 * (int)sizeof(T);  // bytes of one U^T tile
     static constexpr int UTB = NW * NVT * NTT * UTT;
     static_assert(UTB % 1024 == 0, "U^T in whole 1 KiB copies");
-    // loader wave (with two value tiles per wave the compute waves' registers
-    // are at the 256 limit already; they keep staging their own operands)
-    static constexpr bool LW = NVT == 1 && 2 * (NF * 1024 + UTB) <= 150 * 1024;
+    // z and y tiles of the workgroup's columns, [CH][CW] row-major in LDS with
+    // the 16-byte units of row t stored at unit x ^ (t % ZXR), which spreads
+    // the 16 rows a wave's fragment access touches over the banks
+    static constexpr int ZRB = CW * (int)sizeof(T);        // bytes of one token row
+    static constexpr int ZXR = ZRB / 16;                   // 16-byte units per row
+    static constexpr int ZT = AUG ? 0 : CH * ZRB;          // bytes of a z or y tile
+    // loader waves (with two value tiles per wave the compute waves' registers
+    // are at the 256 limit already; they keep staging their own operands);
+    // the z and y rows go in whole 1 KiB copies per compute wave
+    static constexpr bool LW = NVT == 1 && ZT % (1024 * NW) == 0 && 2 * (NF * 1024 + UTB) + 4 * ZT <= 160 * 1024;
     static constexpr int BUF = NF * 1024 + (LW ? UTB : 0);
     static constexpr int NBUF = LW || 2 * BUF <= 150 * 1024 ? 2 : 1;
-    static constexpr int BYTES = NBUF * BUF;
+    static constexpr int O_Z = NBUF * BUF;                 // with LW: two z tiles, then two y tiles
+    static constexpr int O_Y = O_Z + 2 * ZT;
+    static constexpr int BYTES = NBUF * BUF + (LW ? 4 * ZT : 0);
     // loader waves: two (one to four measure alike; the copy rate of one wave
     // alone is about half that of two)
     static constexpr int NLW = LW ? 2 : 0;
@@ -218,6 +232,9 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 barrier_keep_loads();       // ... and the compute waves are done with chunk c-1
                 if (c + 1 < nch) stage_all(c + 1, (c + 1) % 2);
             }
+            if constexpr (!C::AUG) {
+                if (nch > 0) barrier_keep_loads();   // matches the compute waves' last y hand-off
+            }
             return;
         }
     }
@@ -303,6 +320,50 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     auto frag = [&](const char* buf, int f) -> Frag {
         return *reinterpret_cast<const Frag*>(buf + f * 1024 + 16 * lane);
     };
+    // With loader waves, z and y move as whole rows: copy j (1 KiB) of a tile
+    // belongs to compute wave j % NW; lane l of the copy holds token row t,
+    // logical 16-byte unit x
+    constexpr int ZJW = C::ZT / 1024 / NW;   // row copies per wave
+    auto zpos = [&](int j, int& t, int& x) {
+        const int pbyte = j * 1024 + 16 * lane;
+        t = pbyte / C::ZRB;
+        x = ((pbyte % C::ZRB) / 16) ^ (t % C::ZXR);
+    };
+    // byte offset, in a z or y tile, of this lane's 4 columns of token 16 ta + l16
+    auto zy_off = [&](int ta, int vt) -> int {
+        const int t = 16 * ta + l16;
+        const int cb = (wave * 16 * NVT + 16 * vt + 4 * g4) * (int)sizeof(T);
+        return t * C::ZRB + (((cb / 16) ^ (t % C::ZXR)) * 16) + cb % 16;
+    };
+    const int vcw = vcol0 - wave * 16 * NVT;   // first value column of the workgroup
+    static_assert(!C::LW || ZJW <= 2, "z rows per wave");
+    uint4 zrow0 = {0, 0, 0, 0}, zrow1 = {0, 0, 0, 0};   // rows in flight (copies wave, wave + NW)
+    auto zrow_src = [&](int c, int jj) -> const uint4* {
+        const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+        int t, x;
+        zpos(jj * NW + wave, t, x);
+        t = t < nv ? t : nv - 1;
+        return reinterpret_cast<const uint4*>(
+            reinterpret_cast<const char*>(gz + ((t0 + (int64_t)c * CH + t) * H + h) * DV + vcw) + 16 * x);
+    };
+    auto load_zrows = [&](int c) {
+        if constexpr (ZJW >= 1) zrow0 = *zrow_src(c, 0);
+        if constexpr (ZJW >= 2) zrow1 = *zrow_src(c, 1);
+    };
+    auto store_yrows = [&](int c) {
+        const char* yt = smem + C::O_Y + (c % 2) * C::ZT;
+        const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+#pragma unroll
+        for (int jj = 0; jj < ZJW; ++jj) {
+            const int j = jj * NW + wave;
+            int t, x;
+            zpos(j, t, x);
+            const uint4 v = *reinterpret_cast<const uint4*>(yt + j * 1024 + 16 * lane);
+            if (t < nv)
+                *reinterpret_cast<uint4*>(reinterpret_cast<char*>(
+                    gy + ((t0 + (int64_t)c * CH + t) * H + h) * DV + vcw) + 16 * x) = v;
+        }
+    };
     // U^T and z of the wave's columns, one chunk ahead in registers
     T4 ut[NTT][NVT], zz[NTT][NVT];
     auto load_uz = [&](int c) {
@@ -317,7 +378,9 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                     ut[ta][vt] = *reinterpret_cast<const T4*>(UT + ((vtg * NTT + ta) * 64 + lane) * 4);
                 }
         }
-        if (!C::AUG && gz) {
+        if constexpr (C::LW && !C::AUG) {
+            if (gz) load_zrows(c);
+        } else if (!C::AUG && gz) {
             const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
 #pragma unroll
             for (int ta = 0; ta < NTT; ++ta) {
@@ -363,9 +426,18 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
-                if constexpr (!C::LW) utc[ta][vt] = ut[ta][vt];
-                zzc[ta][vt] = zz[ta][vt];
+                if constexpr (!C::LW) {
+                    utc[ta][vt] = ut[ta][vt];
+                    zzc[ta][vt] = zz[ta][vt];
+                }
             }
+        if constexpr (C::LW && !C::AUG) {
+            if (gz) {   // this wave's z rows of chunk c into the z tile
+                char* zt = smem + C::O_Z + (c % 2) * C::ZT;
+                if constexpr (ZJW >= 1) *reinterpret_cast<uint4*>(zt + wave * 1024 + 16 * lane) = zrow0;
+                if constexpr (ZJW >= 2) *reinterpret_cast<uint4*>(zt + (NW + wave) * 1024 + 16 * lane) = zrow1;
+            }
+        }
         const int nvalid = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
         // every wave's part of chunk c has landed, and every wave is done with
         // the buffer the next chunk goes to
@@ -378,6 +450,14 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                     utc[ta][vt] = *reinterpret_cast<const T4*>(buf + C::NF * 1024 +
                                                                ((wave * NVT + vt) * NTT + ta) * C::UTT +
                                                                lane * 4 * (int)sizeof(T));
+            if (!C::AUG && gz) {
+                const char* zt = smem + C::O_Z + (c % 2) * C::ZT;
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt)
+                        zzc[ta][vt] = *reinterpret_cast<const T4*>(zt + zy_off(ta, vt));
+            }
         }
 
         // Delta = U + Wn S
@@ -401,7 +481,11 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(wf, sf[s][vt], D[ta][vt]);
             }
         if constexpr (!C::AUG) {
-            if (yd_nvalid > 0) store_y();
+            if constexpr (C::LW) {
+                if (c > 0) store_yrows(c - 1);   // rows of the previous chunk's outputs
+            } else if (yd_nvalid > 0) {
+                store_y();
+            }
         }
         if constexpr (C::NBUF == 2 && !C::LW) stage(cn, nb, J_0{}, J_H{});
         Frag df[NKT][NVT];
@@ -483,7 +567,10 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) o[i] *= sigmoid(zf[i]);
                     }
-                    yd[ta][vt] = from_f32x4<T>(o);
+                    if constexpr (C::LW)
+                        *reinterpret_cast<T4*>(smem + C::O_Y + (c % 2) * C::ZT + zy_off(ta, vt)) = from_f32x4<T>(o);
+                    else
+                        yd[ta][vt] = from_f32x4<T>(o);
                 }
             yd_row0 = (t0 + (int64_t)c * CH) * H + h;
             yd_nvalid = nvalid;
@@ -496,8 +583,14 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             }
         }
     }
-    if constexpr (!C::AUG) {
+    if constexpr (!C::AUG && !C::LW) {
         if (yd_nvalid > 0) store_y();             // outputs of the last chunk
+    }
+    if constexpr (!C::AUG && C::LW) {
+        if (nch > 0) {
+            barrier_keep_loads();                 // every wave's outputs of the last chunk are in LDS
+            store_yrows(nch - 1);
+        }
     }
 
     // ---- final state ---------------------------------------------------------
