@@ -27,7 +27,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
 ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode", "prefill_checkpoints",
-                 "decode_replay", "prefill_fused_gates", "decode_fused_gates")
+                 "decode_replay", "prefill_fused_gates", "decode_fused_gates", "prefill_chunk32")
 
 
 def log(msg: str) -> None:
@@ -306,6 +306,27 @@ def bench_replay(args, torch, kda, kda_inputs, dev):
     return out
 
 
+def bench_prefill_chunk32(args, torch, kda, kda_inputs, dev):
+    """The K3 layer prefill with 32-token chunks (the headline fixes 64): the
+    same result up to rounding, a smaller per-chunk triangular block."""
+    w = kda_inputs.WORKLOADS[1]
+    H, dk, dv, T = w["H"], w["dk"], w["dv"], w["lens"][0]
+    C = 32
+    d = gpu_inputs(torch, [T], H, dk, dv, True, 0.0, kda_inputs.workload_seed(1), dev)
+    y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, C, 1, T), dtype=torch.uint8,
+                     device=dev)
+    ms, _ = time_steps(lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C,
+                                             y=y, final_state=fs, workspace=ws), args.steps, 2, torch)
+    nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True)
+    out = dict(ms=ms, chunk=C, tokens_per_s=T / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
+               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del d, y, fs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_prefill_fused(args, torch, kda, kda_inputs, dev):
     """The K3 layer prefill from raw inputs (kda_chunk_fwd_fused): unnormalised
     q, k and the gate pre-activations a, b in bf16; the kernel forms unit q, k,
@@ -416,7 +437,7 @@ def main() -> int:
         fn = {"varlen_prefill": bench_varlen, "kcp_long_sequence": bench_kcp,
               "decode": bench_decode, "prefill_checkpoints": bench_checkpoints,
               "decode_replay": bench_replay, "prefill_fused_gates": bench_prefill_fused,
-              "decode_fused_gates": bench_decode_fused}[name]
+              "decode_fused_gates": bench_decode_fused, "prefill_chunk32": bench_prefill_chunk32}[name]
         workloads[name] = fn(args, torch, kda, kda_inputs, dev)
         log(f"{name}: {json.dumps(workloads[name])}")
     cpu, parity = (None, None)

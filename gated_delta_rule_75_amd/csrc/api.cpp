@@ -404,7 +404,7 @@ namespace kda {
 
 bool prefill_supported(int dtype, int dk, int dv, int chunk) {
     if (!((dk == 64 && dv == 64) || (dk == 128 && dv == 128))) return false;
-    if (chunk != 16 && chunk != 64) return false;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return false;
     return dtype == 0 || dtype == 1;
 }
 

@@ -575,6 +575,7 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
 template <class E, int DK, bool FUSED>
 static hipError_t launch_prep_chunk(const TwoPassArgs& a, const int32_t* co, int64_t nb) {
     if (a.chunk == 64) return launch_prep_cfg<PrepCfg<E, DK, 64, FUSED>>(a, co, nb);
+    if (a.chunk == 32) return launch_prep_cfg<PrepCfg<E, DK, 32, FUSED>>(a, co, nb);
     return launch_prep_cfg<PrepCfg<E, DK, 16, FUSED>>(a, co, nb);
 }
 

@@ -725,6 +725,7 @@ static hipError_t launch_state_mode(const TwoPassArgs& a, const int32_t* co, con
 template <class E, int DK>
 static hipError_t launch_state_dk(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
     if (a.chunk == 64) return launch_state_mode<E, DK, 64>(a, co, ord);
+    if (a.chunk == 32) return launch_state_mode<E, DK, 32>(a, co, ord);
     return launch_state_mode<E, DK, 16>(a, co, ord);
 }
 

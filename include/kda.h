@@ -44,7 +44,7 @@
  *   - cu_seqlens is non-decreasing, cu_seqlens[0] = 0,
  *     cu_seqlens[num_seqs] = T_total.
  *
- * Supported sizes: (dk, dv) in {(64, 64), (128, 128)}; chunk in {16, 64}.
+ * Supported sizes: (dk, dv) in {(64, 64), (128, 128)}; chunk in {16, 32, 64}.
  * Anything else returns KDA_ERR_UNSUPPORTED.
  */
 #ifndef LIBKDA_KDA_H
@@ -82,7 +82,7 @@ const char* kda_status_string(kda_status status);
  * whole input in parallel and is compute-limited).
  *
  *   dt, H, dk, dv   dtype and head shape.
- *   chunk           tokens per chunk of the blocked algorithm (16 or 64); it
+ *   chunk           tokens per chunk of the blocked algorithm (16, 32 or 64); it
  *                   changes rounding only, never the result's definition.
  *   scale           factor on the output o_t (1.0 for the plain recurrence).
  *   num_seqs        number of packed sequences (>= 1).

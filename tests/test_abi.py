@@ -79,7 +79,8 @@ def test_chunk_fwd_checkpointed_rejects_bad_arguments(L):
 def test_chunk_fwd_rejects_unsupported_shapes(L):
     assert _fwd(L, dk=96, dv=96) == UNSUPPORTED
     assert _fwd(L, dk=128, dv=64) == UNSUPPORTED
-    assert _fwd(L, chunk=32) == UNSUPPORTED
+    assert _fwd(L, chunk=48) == UNSUPPORTED
+    assert _fwd(L, chunk=128) == UNSUPPORTED
 
 
 def _pm_frags(C, kb):
@@ -116,7 +117,7 @@ def test_chunk_fwd_workspace_size(L):
     assert small >= 2 * _chunk_block_bytes(2, 64, 64, 16, 32)
     assert L.kda_chunk_fwd_workspace_size(BF16, H, 96, 96, C, N, T) == 0
     assert L.kda_chunk_fwd_workspace_size(BF16, 0, dk, dv, C, N, T) == 0
-    assert L.kda_chunk_fwd_workspace_size(BF16, H, dk, dv, 32, N, T) == 0
+    assert L.kda_chunk_fwd_workspace_size(BF16, H, dk, dv, 48, N, T) == 0
 
 
 def test_kcp_workspace_size(L):
@@ -195,7 +196,7 @@ def test_fused_entry_points_reject_bad_arguments(L):
     assert fw(dt=F32, b=ctypes.c_void_p((1 << 20) + 2)) == INVALID
     assert fw(ws=None) == INVALID
     assert fw(dk=96) == UNSUPPORTED
-    assert fw(chunk=32) == UNSUPPORTED
+    assert fw(chunk=48) == UNSUPPORTED
 
     def dec(dt=BF16, a=P, b=P, N=4, dk=128):
         return L.kda_decode_step_fused(dt, N, 2, dk, dk, 1.0, P, P, P, a, b, None, P, P, None)

@@ -8,7 +8,7 @@ import kda_inputs
 from tests.chunk_model import chunk_forward
 
 
-@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("C", [16, 32, 64])
 @pytest.mark.parametrize("stress", [None, "chunk"])
 def test_chunk_model_equals_sequential_oracle(oracle_mod, C, stress):
     gs, bs = kda_inputs.STRESS[stress]
@@ -35,7 +35,7 @@ def test_chunk_model_at_the_decay_bound(oracle_mod):
     np.testing.assert_allclose(Sm, st[0], rtol=0, atol=1e-11)
 
 
-@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("C", [16, 32, 64])
 @pytest.mark.parametrize("stress", [None, "chunk"])
 def test_two_pass_model_equals_sequential_oracle(oracle_mod, C, stress):
     from tests.chunk_model import chunk_prep, state_scan

@@ -57,7 +57,8 @@ def check(name, y, fs, yo, so, tol):
 
 @pytest.mark.parametrize("dtype,d,chunk,stress", [
     ("bf16", 128, 64, None), ("bf16", 128, 16, "chunk"), ("bf16", 64, 64, "chunk"),
-    ("f32", 64, 16, None), ("f32", 128, 64, "chunk"), ("f32", 64, 64, None),
+    ("f32", 64, 16, None), ("f32", 128, 64, "chunk"), ("f32", 64, 64, None), ("bf16", 128, 32, None),
+    ("f32", 128, 32, "chunk"),
 ])
 def test_fused_prefill_matches_oracle(kda, dtype, d, chunk, stress):
     gs, bs = kda_inputs.STRESS[stress]
