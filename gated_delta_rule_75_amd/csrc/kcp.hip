@@ -12,7 +12,9 @@
 // is a dk x dk times dk x CW product: thread (row r, column half) reads row r
 // of M_s from LDS once and the state block by broadcast, and M_{s+1} and the
 // thread's row of Sloc_{s+1} are in flight meanwhile (the head's column blocks
-// share M in L2), so a step waits on LDS and the barriers, not on memory.
+// share M in L2).  The barriers wait for LDS operations only, so those loads
+// stay in flight across them; a step waits on memory only where it writes
+// M_{s+1} into LDS, after its own product.
 #include "common.h"
 #include "launch.h"
 
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void kcp_scan_kernel(int H, int nseg,
             stage_m(s + 1, buf ^ 1, tmp);
             stage_l(s + 1);
         }
-        __syncthreads();                           // M_s and S_s visible
+        barrier_keep_loads();                      // M_s and S_s visible; M_{s+1} stays in flight
         const float* mrow = sM + (buf * DK + r) * LM;
         const float* sblk = sS + buf * DK * CW + cj;
 #pragma unroll 4
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void kcp_scan_kernel(int H, int nseg,
         buf ^= 1;
         // the next iteration's writes to buffer buf (= the one read two steps
         // later) are ordered by its own barrier; buffer buf^1 was last read here
-        __syncthreads();
+        barrier_keep_loads();
     }
 }
 
