@@ -77,10 +77,15 @@ int pick_nvt(int64_t chains, int dvt) {
     return chains * (dvt / 128) >= 1024 ? 2 : 1;
 }
 
-// Byte sizes of the KCP workspace parts.
-void kcp_parts(int H, int dk, int dv, int nseg, size_t* pairs, size_t* starts) {
+// Byte sizes of the KCP workspace parts: segment pairs and entering states,
+// then the group pairs and group entering states of the two-level scan.
+void kcp_parts(int H, int dk, int dv, int nseg, size_t* pairs, size_t* starts, size_t* gpairs,
+               size_t* gstarts) {
+    const int L = kda::kcp_group_len(nseg), G = (nseg + L - 1) / L;
     *pairs = round_up((size_t)nseg * H * dk * (size_t)(dk + dv) * sizeof(float), 256);
     *starts = round_up((size_t)nseg * H * dk * (size_t)dv * sizeof(float), 256);
+    *gpairs = round_up((size_t)G * H * dk * (size_t)(dk + dv) * sizeof(float), 256);
+    *gstarts = round_up((size_t)G * H * dk * (size_t)dv * sizeof(float), 256);
 }
 
 }  // namespace
@@ -269,10 +274,10 @@ size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, in
                               int num_segments) {
     if ((dt != KDA_BF16 && dt != KDA_F32) || H <= 0 || num_segments <= 0 || T < num_segments) return 0;
     if (!kda::prefill_supported((int)dt, dk, dv, chunk)) return 0;
-    size_t pairs, starts;
-    kcp_parts(H, dk, dv, num_segments, &pairs, &starts);
+    size_t pairs, starts, gpairs, gstarts;
+    kcp_parts(H, dk, dv, num_segments, &pairs, &starts, &gpairs, &gstarts);
     const int64_t seg_len = (T + num_segments - 1) / num_segments;
-    return pairs + starts +
+    return pairs + starts + gpairs + gstarts +
            twopass_layout(dt, H, dk, dv, chunk, num_segments, seg_chunks(seg_len, chunk, num_segments)).total;
 }
 
@@ -294,11 +299,13 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
         return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < kda_kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments))
         return KDA_ERR_WORKSPACE_TOO_SMALL;
-    size_t pbytes, sbytes;
-    kcp_parts(H, dk, dv, num_segments, &pbytes, &sbytes);
+    size_t pbytes, sbytes, gpbytes, gsbytes;
+    kcp_parts(H, dk, dv, num_segments, &pbytes, &sbytes, &gpbytes, &gsbytes);
     float* pairs = static_cast<float*>(workspace);
     float* starts = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes);
-    void* tp = static_cast<char*>(workspace) + pbytes + sbytes;
+    float* gpairs = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes + sbytes);
+    float* gstarts = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes + sbytes + gpbytes);
+    void* tp = static_cast<char*>(workspace) + pbytes + sbytes + gpbytes + gsbytes;
     // segments hold seg_len tokens each; with T not a multiple, trailing ones may be empty
     const int64_t seg_len = (T + num_segments - 1) / num_segments;
     const int64_t nchunks = seg_chunks(seg_len, chunk, num_segments);
@@ -335,7 +342,7 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.y = nullptr;
     if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
     // phase 2: entering state of every segment
-    if (kda::launch_kcp_scan(H, dk, dv, num_segments, pairs, initial_state, starts, final_state,
+    if (kda::launch_kcp_scan(H, dk, dv, num_segments, pairs, initial_state, starts, gpairs, gstarts,
                              (hipStream_t)stream) != hipSuccess)
         return KDA_ERR_HIP;
     // phase 3: outputs of every segment from its entering state; the last

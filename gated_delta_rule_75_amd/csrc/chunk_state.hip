@@ -126,20 +126,6 @@ template <> __device__ __forceinline__ bf16x4_t from_f32x4<__bf16>(f32x4_t x) {
 }
 template <> __device__ __forceinline__ f32x4_t from_f32x4<float>(f32x4_t x) { return x; }
 
-// 16 bytes per lane from global memory straight into LDS: lane i writes
-// lds + 16 i.  (A __device__ wrapper: the builtin written directly in a
-// kernel template hides the kernel from the host compilation pass.)
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
-    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) (n < 64), other counters left alone
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     using K = typename C::K;

@@ -123,6 +123,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds + 16 i.  (A __device__ wrapper: the builtin written directly in a
+// kernel template hides the kernel from the host compilation pass.)
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n < 64), other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier that leaves global loads and stores in flight.
 // __syncthreads() waits for every outstanding vector-memory operation (its
 // fence covers global stores and direct-to-LDS copies too); kernels whose

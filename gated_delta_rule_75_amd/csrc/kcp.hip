@@ -1,150 +1,201 @@
-// KCP phase 2: fold the segment pairs in order to give every segment its
-// entering state (page "Exercices", Niveau 3 Q21-Q22: a segment acts on the
-// state entering it as S_end = M S_start + Sloc, and pairs compose
-// associatively, (M2, S2) o (M1, S1) = (M2 M1, M2 S1 + S2)).
+// KCP phase 2: the state entering every segment (page "Exercices", Niveau 3
+// Q21-Q22: a segment acts on the state entering it as S_end = M S_start +
+// Sloc, and pairs compose associatively, (M2, S2) o (M1, S1) =
+// (M2 M1, M2 S1 + S2)).  Phase 1 (the pairs) and phase 3 (every segment's
+// outputs from its entering state) are the prefill kernels; see kda_kcp_scan
+// in api.cpp.
 //
-// Phase 1 (the pairs) and phase 3 (every segment's outputs from its entering
-// state) are the prefill kernel; see kda_kcp_scan in api.cpp.
-//
-// This kernel applies the pairs to the state directly: starts[0] = S0 and
-// starts[s+1] = M_s starts[s] + Sloc_s.  State columns are independent, so a
-// workgroup owns CW columns of one head and walks the segments.  Each step
-// is a dk x dk times dk x CW product: thread (row r, column half) reads row r
-// of M_s from LDS once and the state block by broadcast, and M_{s+1} and the
-// thread's row of Sloc_{s+1} are in flight meanwhile (the head's column blocks
-// share M in L2).  The barriers wait for LDS operations only, so those loads
-// stay in flight across them; a step waits on memory only where it writes
-// M_{s+1} into LDS, after its own product.
+// The segments are cut into G groups of L ~ sqrt(nseg).  Three launches of
+// one chain kernel: (1) each group's pairs composed into one pair, all groups
+// side by side; (2) one chain over the G group pairs from S0, giving the
+// state entering each group; (3) each group's segments replayed from its
+// entering state, all groups side by side, writing every segment's entering
+// state.  The dependent depth is about 3 sqrt(nseg) steps instead of nseg.
 #include "common.h"
 #include "launch.h"
 
 namespace kda {
 
-template <int DK, int DV, int CW>
-__global__ __launch_bounds__(256) void kcp_scan_kernel(int H, int nseg,
-                                                       const float* __restrict__ pairs,
-                                                       const float* __restrict__ s0,
-                                                       float* __restrict__ starts) {
-    constexpr int NT = 256;
-    constexpr int TPR = NT / DK;          // threads per state row
-    constexpr int CPT = CW / TPR;         // columns per thread
-    constexpr int W = DK + DV;            // row width of a pair [M | Sloc]
-    constexpr int LM = DK + 4;            // padded LDS pitch of M
-    constexpr int MV4 = DK * DK / 4;      // float4s of M
-    static_assert(TPR * DK == NT && CPT * TPR == CW && CPT % 4 == 0, "scan tiling");
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    float* sM = sm;                        // [2][DK][LM]
-    float* sS = sm + 2 * DK * LM;          // [2][DK][CW]
+// One chain of pairs applied to a 64-column slice of a DK-row state X:
+//     for j = 0 .. L-1:  [out_each[s0 + j] = X;]  X <- M_{s0+j} X + A_{s0+j}
+//     [out_final[g] = X]
+// with (M_s, A_s) from the pair rows [M | Sloc] of `pairs` (row width W).
+// Plain chains carry a state of dv columns (A = Sloc, X starts at `init`);
+// augmented chains carry [M | S] (dk + dv columns: the first dk start at the
+// identity and take no additive term, A = Sloc on the rest), which composes
+// the chain's pairs into one pair (page "Exercices", Niveau 3 Q21-Q22).
+//
+// Four waves, one 16-column tile each; X stays in MFMA accumulator tiles
+// (lane: rows 4 (l/16) + i, column l%16) and enters the next product as the B
+// operand, MFMA i taking row 4 (l/16) + i (fp32 16x16x4).  M_{s+1} streams
+// into the other half of a double buffer in LDS by global-to-LDS copies
+// while step s computes; the barrier between steps waits for LDS only.
+struct ChainParams {
+    int H, nseg, L;          // pairs entries, steps per chain (chain g starts at g L)
+    int W;                   // row width of a pair: dk + dv
+    int aug;                 // augmented [M | S] state
+    int ncol;                // state columns: dv, or dk + dv when augmented
+    const float* pairs;      // [nseg][H][dk][W]
+    const float* init;       // plain chains: [G][H][dk][dv] or NULL (zeros)
+    float* out_each;         // plain chains: [nseg][H][dk][dv] or NULL
+    float* out_final;        // [G][H][dk][ncol] or NULL
+};
 
-    const int nblk_h = DV / CW;
-    const int h = blockIdx.x / nblk_h;
-    const int col0 = (blockIdx.x % nblk_h) * CW;
-    const int tid = threadIdx.x;
-    const int r = tid / TPR;
-    const int cj = (tid % TPR) * CPT;
+template <int DK>
+__global__ __launch_bounds__(256) void kcp_chain_kernel(ChainParams p) {
+    constexpr int NRT = DK / 16;                 // 16-row tiles of the state
+    constexpr int RPC = 1024 / (DK * 4);         // M rows per 1 KiB copy
+    constexpr int NCP = DK / RPC;                // copies per M
+    constexpr int MP = 1024 + 16;                // LDS pitch of a copy (bank spread)
+    constexpr int MBUF = NCP * MP;
+    static_assert(NCP % 4 == 0, "copies per wave");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int col = blockIdx.z * 64 + wave * 16 + l16;   // this lane's state column
+    const int s0 = g * p.L;
+    const int L = p.nseg - s0 < p.L ? p.nseg - s0 : p.L;
+    if (L <= 0) return;
+    const int dv = p.W - DK;
+    auto prow = [&](int s, int r) { return p.pairs + (((int64_t)s * p.H + h) * DK + r) * p.W; };
 
-    auto pair_row = [&](int s, int row) { return pairs + (((int64_t)s * H + h) * DK + row) * W; };
-    // M of segment s into LDS buffer b (vector loads, then LDS writes)
-    auto stage_m = [&](int s, int b, f32x4_t* tmp) {
+    // copies [4 j + wave] of M_s into buffer b: rows RPC c .. RPC c + RPC - 1
+    auto stage = [&](int s, int b) {
+        char* buf = smem + b * MBUF;
 #pragma unroll
-        for (int i = 0; i < MV4 / NT; ++i) {
-            const int e = (i * NT + tid) * 4, row = e / DK, c = e % DK;
-            tmp[i] = *reinterpret_cast<const f32x4_t*>(pair_row(s, row) + c);
+        for (int jj = 0; jj < NCP / 4; ++jj) {
+            const int c = jj * 4 + wave;
+            const int r = RPC * c + lane / (64 / RPC), k = (lane % (64 / RPC)) * 4;
+            lds_dma16(prow(s, r) + k, buf + c * MP);
         }
     };
-    auto put_m = [&](int b, const f32x4_t* tmp) {
+    auto mread = [&](const char* buf, int r, int k) -> f32x4_t {
+        return *reinterpret_cast<const f32x4_t*>(buf + (r / RPC) * MP + (r % RPC) * DK * 4 + k * 4);
+    };
+    // additive column of step s for this lane's rows
+    const bool ident = p.aug && col < DK;
+    const int acol = p.aug ? col : DK + col;
+    auto load_a = [&](int s, f32x4_t* a) {
 #pragma unroll
-        for (int i = 0; i < MV4 / NT; ++i) {
-            const int e = (i * NT + tid) * 4, row = e / DK, c = e % DK;
-            *reinterpret_cast<f32x4_t*>(sM + (b * DK + row) * LM + c) = tmp[i];
-        }
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[rt][i] = ident ? 0.f : prow(s, 16 * rt + 4 * g4 + i)[acol];
     };
 
-    float cur[CPT];
+    f32x4_t X[NRT], A[NRT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j)
-        cur[j] = s0 ? s0[((int64_t)h * DK + r) * DV + col0 + cj + j] : 0.f;
-    f32x4_t tmp[MV4 / NT];
-    f32x4_t lnext[CPT / 4];   // Sloc row r of the next step, prefetched
-    auto stage_l = [&](int s) {
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int j = 0; j < CPT; j += 4)
-            lnext[j / 4] = *reinterpret_cast<const f32x4_t*>(pair_row(s, r) + DK + col0 + cj + j);
-    };
-    if (nseg > 1) {
-        stage_m(0, 0, tmp);
-        stage_l(0);
-        put_m(0, tmp);
-    }
-    int buf = 0;
-    for (int s = 0; s < nseg; ++s) {
-        float* st = starts + (((int64_t)s * H + h) * DK + r) * DV + col0 + cj;
-#pragma unroll
-        for (int j = 0; j < CPT; j += 4) {
-            const f32x4_t v = f32x4_t{cur[j], cur[j + 1], cur[j + 2], cur[j + 3]};
-            *reinterpret_cast<f32x4_t*>(st + j) = v;
-            *reinterpret_cast<f32x4_t*>(sS + (buf * DK + r) * CW + cj + j) = v;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * g4 + i;
+            float x = 0.f;
+            if (p.aug) x = (col == r) ? 1.f : 0.f;
+            else if (p.init) x = p.init[(((int64_t)g * p.H + h) * DK + r) * dv + col];
+            X[rt][i] = x;
         }
-        if (s + 1 == nseg) break;
-        const bool more = s + 2 < nseg;
-        float acc[CPT];
+    stage(s0, 0);
+    load_a(s0, A);
+    for (int j = 0; j < L; ++j) {
+        const int s = s0 + j;
+        const char* buf = smem + (j & 1) * MBUF;
+        if (p.out_each) {
+            float* o = p.out_each + ((int64_t)s * p.H + h) * DK * dv;
 #pragma unroll
-        for (int j = 0; j < CPT; j += 4) {
-            acc[j] = lnext[j / 4][0];
-            acc[j + 1] = lnext[j / 4][1];
-            acc[j + 2] = lnext[j / 4][2];
-            acc[j + 3] = lnext[j / 4][3];
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[(16 * rt + 4 * g4 + i) * dv + col] = X[rt][i];
         }
-        if (more) {   // M and Sloc of the next step, in flight during this one
-            stage_m(s + 1, buf ^ 1, tmp);
-            stage_l(s + 1);
+        f32x4_t acc[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) acc[rt] = A[rt];
+        wait_vmcnt<0>();           // M_s (and A_s) have landed
+        barrier_keep_loads();      // ... for every wave; buffer (j+1)&1 is free
+        if (j + 1 < L) {
+            stage(s + 1, (j + 1) & 1);
+            load_a(s + 1, A);
         }
-        barrier_keep_loads();                      // M_s and S_s visible; M_{s+1} stays in flight
-        const float* mrow = sM + (buf * DK + r) * LM;
-        const float* sblk = sS + buf * DK * CW + cj;
-#pragma unroll 4
-        for (int c = 0; c < DK; c += 4) {
-            const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(mrow + c);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+        for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
-                for (int j = 0; j < CPT; j += 4) {
-                    const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(sblk + (c + e) * CW + j);
-                    acc[j] += m4[e] * s4[0];
-                    acc[j + 1] += m4[e] * s4[1];
-                    acc[j + 2] += m4[e] * s4[2];
-                    acc[j + 3] += m4[e] * s4[3];
-                }
+            for (int rt = 0; rt < NRT; ++rt) {
+                const f32x4_t m4 = mread(buf, 16 * rt + l16, 16 * kt + 4 * g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(m4[i], X[kt][i], acc[rt], 0, 0, 0);
             }
-        }
-        if (more) put_m(buf ^ 1, tmp);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) cur[j] = acc[j];
-        buf ^= 1;
-        // the next iteration's writes to buffer buf (= the one read two steps
-        // later) are ordered by its own barrier; buffer buf^1 was last read here
-        barrier_keep_loads();
+        for (int rt = 0; rt < NRT; ++rt) X[rt] = acc[rt];
+    }
+    if (p.out_final) {
+        float* o = p.out_final + ((int64_t)g * p.H + h) * DK * p.ncol;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[(16 * rt + 4 * g4 + i) * p.ncol + col] = X[rt][i];
     }
 }
 
-template <int DK, int DV, int CW>
-static hipError_t launch_scan_t(int H, int nseg, const float* pairs, const float* s0,
-                                float* starts, hipStream_t stream) {
-    const size_t lds = (size_t)(2 * DK * (DK + 4) + 2 * DK * CW) * sizeof(float);
-    auto kern = kcp_scan_kernel<DK, DV, CW>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+template <int DK>
+static hipError_t launch_chain_t(const ChainParams& p, int nchain, int ncol, hipStream_t stream) {
+    constexpr int MBUF = (DK / (1024 / (DK * 4))) * (1024 + 16);
+    auto kern = kcp_chain_kernel<DK>;
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             2 * MBUF);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(H * (DV / CW)), dim3(256), lds, stream, H, nseg, pairs, s0,
-                       starts);
+    hipLaunchKernelGGL(kern, dim3(nchain, p.H, ncol / 64), dim3(256), 2 * MBUF, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_kcp_scan(int H, int dk, int dv, int nseg, const float* pairs,
-                           const float* initial_state, float* starts, float* /*final_state*/,
-                           hipStream_t stream) {
-    if (dk == 128) return launch_scan_t<128, 128, 8>(H, nseg, pairs, initial_state, starts, stream);
-    return launch_scan_t<64, 64, 16>(H, nseg, pairs, initial_state, starts, stream);
+static hipError_t launch_chain(int dk, const ChainParams& p, int nchain, hipStream_t stream) {
+    return dk == 128 ? launch_chain_t<128>(p, nchain, p.ncol, stream) : launch_chain_t<64>(p, nchain, p.ncol, stream);
+}
+
+int kcp_group_len(int nseg) {
+    int L = 1;
+    while (L * L < nseg) ++L;
+    return L;
+}
+
+hipError_t launch_kcp_scan(int H, int dk, int dv, int nseg, const float* pairs, const float* initial_state,
+                           float* starts, float* group_pairs, float* group_starts, hipStream_t stream) {
+    const int L = kcp_group_len(nseg), G = (nseg + L - 1) / L;
+    ChainParams p{};
+    p.H = H;
+    p.W = dk + dv;
+    // 1. every group's pairs composed into one pair, groups side by side
+    p.nseg = nseg;
+    p.L = L;
+    p.aug = 1;
+    p.ncol = dk + dv;
+    p.pairs = pairs;
+    p.out_final = group_pairs;
+    hipError_t e = launch_chain(dk, p, G, stream);
+    if (e != hipSuccess) return e;
+    // 2. the state entering every group: one chain over the group pairs
+    p = ChainParams{};
+    p.H = H;
+    p.W = dk + dv;
+    p.nseg = G;
+    p.L = G;
+    p.ncol = dv;
+    p.pairs = group_pairs;
+    p.init = initial_state;
+    p.out_each = group_starts;
+    e = launch_chain(dk, p, 1, stream);
+    if (e != hipSuccess) return e;
+    // 3. the state entering every segment, groups side by side from their starts
+    p = ChainParams{};
+    p.H = H;
+    p.W = dk + dv;
+    p.nseg = nseg;
+    p.L = L;
+    p.ncol = dv;
+    p.pairs = pairs;
+    p.init = group_starts;
+    p.out_each = starts;
+    return launch_chain(dk, p, G, stream);
 }
 
 }  // namespace kda

@@ -81,9 +81,12 @@ hipError_t launch_decode(const DecodeArgs& a);
 // accepted[n] written back (accepted optional).
 hipError_t launch_replay(const DecodeArgs& a, int Td, const int32_t* accepted);
 
-// KCP phase 2: starts[s] = M_{s-1} starts[s-1] + Sloc_{s-1}, starts[0] = S0.
+// KCP phase 2: starts[s] = M_{s-1} starts[s-1] + Sloc_{s-1}, starts[0] = S0,
+// through kcp_group_len(nseg)-segment groups: group_pairs [G][H][dk][dk+dv]
+// and group_starts [G][H][dk][dv] are scratch (G = ceil(nseg / L)).
+int kcp_group_len(int nseg);
 hipError_t launch_kcp_scan(int H, int dk, int dv, int nseg, const float* pairs,
-                           const float* initial_state, float* starts, float* final_state,
-                           hipStream_t stream);
+                           const float* initial_state, float* starts, float* group_pairs,
+                           float* group_starts, hipStream_t stream);
 
 }  // namespace kda

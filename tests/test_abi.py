@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every symbol the header
 declares, and rejects bad arguments before launching anything."""
 import ctypes
+import math
 import os
 import re
 
@@ -124,10 +125,15 @@ def test_kcp_workspace_size(L):
     H, dk, dv, S, T, C = 4, 128, 128, 256, 1 << 20, 64
     pairs = S * H * dk * (dk + dv) * 4
     starts = S * H * dk * dv * 4
+    # the scan of the pairs goes through G groups of ceil(sqrt(S)) segments
+    Lg = math.isqrt(S - 1) + 1
+    G = -(-S // Lg)
+    assert (Lg, G) == (16, 16)
+    groups = G * H * dk * (dk + dv) * 4 + G * H * dk * dv * 4
     need = L.kda_kcp_workspace_size(BF16, H, dk, dv, C, T, S)
     nb = S * (T // S // C) * H
-    assert need >= pairs + starts + nb * _chunk_block_bytes(2, dk, dv, C, C)
-    assert need <= pairs + starts + nb * _chunk_block_bytes(2, dk, dv, C, C) + 16 * 256 + 8 * S
+    base = pairs + starts + groups + nb * _chunk_block_bytes(2, dk, dv, C, C)
+    assert base <= need <= base + 16 * 256 + 8 * S
     assert L.kda_kcp_workspace_size(BF16, H, 96, 96, C, T, S) == 0
     assert L.kda_kcp_workspace_size(BF16, 0, dk, dv, C, T, S) == 0
     assert L.kda_kcp_workspace_size(BF16, H, dk, dv, C, T, 0) == 0
