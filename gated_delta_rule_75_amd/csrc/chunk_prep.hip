@@ -117,6 +117,8 @@ __device__ __forceinline__ void st4(__bf16* p, float a, float b, float c, float 
 __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
 }
+__device__ __forceinline__ f32x4_t cvt4(bf16x4_t v) { return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
+__device__ __forceinline__ f32x4_t cvt4(f32x4_t v) { return v; }
 // four elements kept in the storage type between phases (half the registers at bf16)
 template <typename T> struct Vec4;
 template <> struct Vec4<__bf16> { using type = bf16x4_t; };
@@ -147,10 +149,17 @@ void chunk_prep_kernel(PrepParams p) {
     float* sD = reinterpret_cast<float*>(smem + C::O_D);
     float* sBeta = reinterpret_cast<float*>(smem + C::O_BETA);
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform
     const int H = p.H;
+    constexpr int NTS = C::NTS, TPW = C::TPW, SPT = C::SPT;
+    const int cset = wave % C::NWC, tsl = wave / C::NWC;   // wave-uniform
+    const T* gq = static_cast<const T*>(p.q);
+    const T* gk = static_cast<const T*>(p.k);
+    const T* gv = static_cast<const T*>(p.v);
+    using T4 = typename Vec4<T>::type;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t wsb = blockIdx.x;  // (chunk, head) block of the workspace
     const int h = (int)(wsb % H);
     const int gc = (int)(wsb / H);
@@ -170,9 +179,9 @@ void chunk_prep_kernel(PrepParams p) {
         const int64_t rem = p.cu_seqlens[lo + 1] - ts;
         nvalid = (int)(rem < CH ? rem : CH);
     } else {
-        const int n = gc / p.cps;
-        if (n >= p.num_seqs) return;
-        const int64_t s0 = (int64_t)n * p.seg_len;
+        const int sq = gc / p.cps;
+        if (sq >= p.num_seqs) return;
+        const int64_t s0 = (int64_t)sq * p.seg_len;
         const int64_t s1 = s0 + p.seg_len < p.T_total ? s0 + p.seg_len : p.T_total;
         ts = s0 + (int64_t)(gc % p.cps) * CH;
         if (ts >= s1) return;  // past the end of a short last segment
@@ -182,46 +191,24 @@ void chunk_prep_kernel(PrepParams p) {
     if (ts >= p.T_total) return;
     if (ts + nvalid > p.T_total) nvalid = (int)(p.T_total - ts);
 
-    T* Wn = static_cast<T*>(p.ws.wn) + wsb * (CH * DK);
-    T* Qt = static_cast<T*>(p.ws.qt) + wsb * (CH * DK);
-    T* KhT = static_cast<T*>(p.ws.kht) + wsb * (DK * CP);
-    T* Pm = static_cast<T*>(p.ws.pm) + wsb * (C::NPM * 64 * (K::KB / 4));
-    T* UT = static_cast<T*>(p.ws.ut) + wsb * (DV * CH);
-    float* gam = p.ws.gam + wsb * DK;
-
-    // ---- 1. loads and decay ----------------------------------------------------
-    constexpr int NTS = C::NTS, TPW = C::TPW, SPT = C::SPT;
-    const int cset = wave % C::NWC, tsl = wave / C::NWC;   // wave-uniform
+    // phase-1 mapping (see below): this thread's channels and first token
     const int tg = lane / CGW, cg = lane % CGW;
     const int c0 = cset * 64 + 4 * cg;
     const int tl0 = tsl * TPW + tg * TPT;
-    const T* gq = static_cast<const T*>(p.q);
-    const T* gk = static_cast<const T*>(p.k);
-    const T* gv = static_cast<const T*>(p.v);
-    using T4 = typename Vec4<T>::type;
-    f32x4_t G[TPT], kx[TPT], qx[TPT];
-    T4 vx[TPT];  // v stays in the storage type until phase 3
+    // the block's inputs as stored, converted where they are used: g (fp32)
+    // or the pre-activation a, k, q, v, and one beta (or b) per thread below C
+    using GRaw = typename std::conditional<C::FUSED, T4, f32x4_t>::type;
+    GRaw rg[TPT];
+    T4 rk[TPT], rq[TPT], rv[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
         const int t = tl0 + i;
-        const bool ok = t < nvalid;
-        const int64_t row = (ts + (ok ? t : 0)) * H + h;
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t gg;   // log-decay in base 2: every exponential below is one v_exp_f32
-        if constexpr (C::FUSED) {
-            const f32x4_t aa = ld4f(static_cast<const T*>(p.g) + row * DK + c0);
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) gg[ch] = decay_gate(aa[ch]) * kLog2e;
-        } else {
-            gg = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + row * DK + c0) * kLog2e;
-        }
-        const f32x4_t kk = ld4f(gk + row * DK + c0);
-        const f32x4_t qq = ld4f(gq + row * DK + c0);
-        const T4 vv = *reinterpret_cast<const T4*>(gv + row * DV + c0);
-        G[i] = ok ? gg : zero;
-        kx[i] = ok ? kk : zero;
-        qx[i] = ok ? qq : zero;
-        vx[i] = ok ? vv : T4{};
+        const int64_t row = (ts + (t < nvalid ? t : 0)) * H + h;
+        if constexpr (C::FUSED) rg[i] = *reinterpret_cast<const T4*>(static_cast<const T*>(p.g) + row * DK + c0);
+        else rg[i] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + row * DK + c0);
+        rk[i] = *reinterpret_cast<const T4*>(gk + row * DK + c0);
+        rq[i] = *reinterpret_cast<const T4*>(gq + row * DK + c0);
+        rv[i] = *reinterpret_cast<const T4*>(gv + row * DV + c0);
     }
     if (tid < CH) {
         float b = 0.f;
@@ -232,6 +219,38 @@ void chunk_prep_kernel(PrepParams p) {
         }
         sBeta[tid] = b;
     }
+
+    T* Wn = static_cast<T*>(p.ws.wn) + wsb * (CH * DK);
+    T* Qt = static_cast<T*>(p.ws.qt) + wsb * (CH * DK);
+    T* KhT = static_cast<T*>(p.ws.kht) + wsb * (DK * CP);
+    T* Pm = static_cast<T*>(p.ws.pm) + wsb * (C::NPM * 64 * (K::KB / 4));
+    T* UT = static_cast<T*>(p.ws.ut) + wsb * (DV * CH);
+    float* gam = p.ws.gam + wsb * DK;
+
+    // ---- 1. loads and decay ----------------------------------------------------
+    // k, q and v stay in the storage type (rk, rq, rv) until they are used
+    f32x4_t G[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        // log-decay in base 2: every exponential below is one v_exp_f32
+        if constexpr (C::FUSED) {
+            const f32x4_t aa = cvt4(rg[i]);
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) G[i][ch] = decay_gate(aa[ch]) * kLog2e;
+        } else {
+            G[i] = rg[i] * kLog2e;
+        }
+    }
+    if (nvalid < CH) {  // tokens past the end of a ragged chunk take no part
+#pragma unroll
+        for (int i = 0; i < TPT; ++i)
+            if (tl0 + i >= nvalid) {
+                G[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                rk[i] = T4{};
+                rq[i] = T4{};
+                rv[i] = T4{};
+            }
+    }
     float* sNorm = sL;  // FUSED: [2][NWC][CH] partial squared norms (k, then q)
     if constexpr (C::FUSED) {
         // this thread's 4 channels, then the CGW lanes of a token group, then
@@ -239,10 +258,11 @@ void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             float sk = 0.f, sq = 0.f;
+            const f32x4_t kk = cvt4(rk[i]), qq = cvt4(rq[i]);
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
-                sk += kx[i][ch] * kx[i][ch];
-                sq += qx[i][ch] * qx[i][ch];
+                sk += kk[ch] * kk[ch];
+                sq += qq[ch] * qq[ch];
             }
 #pragma unroll
             for (int d = 1; d < CGW; d <<= 1) {
@@ -261,6 +281,7 @@ void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
     for (int i = 1; i < TPT; ++i) G[i] += G[i - 1];
     float* sTot = reinterpret_cast<float*>(smem + C::O_TOT);   // [NTS][DK]
+    f32x4_t ex;   // sum over the wave's earlier token groups
     {
         f32x4_t inc = G[TPT - 1];
 #pragma unroll
@@ -270,15 +291,13 @@ void chunk_prep_kernel(PrepParams p) {
             for (int ch = 0; ch < 4; ++ch) y[ch] = __shfl_up(inc[ch], d * CGW, 64);
             if (tg >= d) inc += y;
         }
-        const f32x4_t ex = inc - G[TPT - 1];
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) G[i] += ex;
+        ex = inc - G[TPT - 1];
         if (tg == TGW - 1) *reinterpret_cast<f32x4_t*>(sTot + tsl * DK + c0) = inc;
     }
     barrier_keep_loads();
     // sub-tile references R_b = G at token 16 b - 1 (R_0 = 0), the sum over
     // the slices before this one, and G_C
-    f32x4_t Rb[NT], Ro, GC;
+    f32x4_t Rb[NT], Ro, RoL, GC;
     {
         f32x4_t run = {0.f, 0.f, 0.f, 0.f}, pre = run;
 #pragma unroll
@@ -288,12 +307,11 @@ void chunk_prep_kernel(PrepParams p) {
             run += *reinterpret_cast<const f32x4_t*>(sTot + sl * DK + c0);
         }
         GC = run;
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) G[i] += pre;
         Ro = Rb[0];
 #pragma unroll
         for (int a = 1; a < NT; ++a)
             if (tsl / SPT == a) Ro = Rb[a];
+        RoL = Ro - pre - ex;   // the reference relative to the thread's own running sums
     }
     if (tsl == 0 && tg == 0) {
 #pragma unroll
@@ -306,10 +324,9 @@ void chunk_prep_kernel(PrepParams p) {
             }
         st4(gam + c0, exp2_fast(GC[0]), exp2_fast(GC[1]), exp2_fast(GC[2]), exp2_fast(GC[3]));
     }
+    float* sInv = sZ;  // FUSED: [2][CH] inverse norms (on the L^{-1} blocks, unused until phase 3)
     if constexpr (C::FUSED) {
-        // waves 0 and 1 sum the partials of k and q, one token per lane, into
-        // inverse norms (on the L^{-1} blocks, unused until phase 3)
-        float* sInv = sZ;  // [2][CH]
+        // waves 0 and 1 sum the partials of k and q, one token per lane
         if (wave < 2 && lane < CH) {
             float s2 = 0.f;
 #pragma unroll
@@ -317,11 +334,6 @@ void chunk_prep_kernel(PrepParams p) {
             sInv[wave * CH + lane] = rsqrtf(s2 + kNormEps);
         }
         barrier_keep_loads();
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            kx[i] *= sInv[tl0 + i];
-            qx[i] *= sInv[CH + tl0 + i];
-        }
     }
     // two exponentials per element, e^{G - R} <= 1 and e^{R - G} <= e^80 (R the
     // sub-tile reference); e^G and e^{G_C - G} follow by per-channel factors
@@ -339,20 +351,25 @@ void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
         const int t = tl0 + i;
-        f32x4_t kr, qr, kc, qt;
+        f32x4_t kx = cvt4(rk[i]), qx = cvt4(rq[i]);
+        if constexpr (C::FUSED) {
+            kx *= sInv[t];
+            qx *= sInv[CH + t];
+        }
+        f32x4_t kr, qr, kc, qt, kg;
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
-            const float d = G[i][ch] - Ro[ch];
+            const float d = G[i][ch] - RoL[ch];
             const float er = exp2_fast(d);    // e^{G - R}
             const float ec = exp2_fast(-d);   // e^{R - G}
-            kr[ch] = kx[i][ch] * er;
-            qr[ch] = qx[i][ch] * er;
-            kc[ch] = kx[i][ch] * ec;
+            kr[ch] = kx[ch] * er;
+            qr[ch] = qx[ch] * er;
+            kc[ch] = kx[ch] * ec;
             qt[ch] = qr[ch] * sR[ch];         // scale q e^G
             kh[i][ch] = kc[ch] * eCR[ch];     // k e^{G_C - G}
-            kx[i][ch] = kr[ch] * eR[ch];      // k e^G
+            kg[ch] = kr[ch] * eR[ch];         // k e^G
         }
-        kw[i] = pack4<T>(kx[i][0], kx[i][1], kx[i][2], kx[i][3]);
+        kw[i] = pack4<T>(kg[0], kg[1], kg[2], kg[3]);
         st4(sKr + t * LK + c0, kr[0], kr[1], kr[2], kr[3]);
         st4(sQr + t * LK + c0, qr[0], qr[1], qr[2], qr[3]);
         st4(sKc + t * LK + c0, kc[0], kc[1], kc[2], kc[3]);
@@ -377,23 +394,11 @@ void chunk_prep_kernel(PrepParams p) {
             }
         }
     }
-    // zero padding past C (k-blocks over tokens) and the P tiles above the
-    // diagonal that share a k-block with a diagonal tile
+    // zero padding of Kh^T past C (k-blocks over tokens)
     if constexpr (CP > CH) {
         for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
             const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
             KhT[frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t)] = from_f32<T>(0.f);
-        }
-        for (int idx = tid; idx < CH * (CP - CH); idx += NTHR) {
-            const int t = idx / (CP - CH), j = CH + idx % (CP - CH);
-            Pm[frag_elem<K>(pm_frag_index(t / 16, j / K::KB, C::NKT, K::KB), t, j)] = from_f32<T>(0.f);
-        }
-    }
-    if constexpr (K::TPB == 2 && NT > 1) {
-        for (int idx = tid; idx < (NT / 2) * 256; idx += NTHR) {
-            const int a = 2 * (idx >> 8), e = idx & 255;
-            const int t = 16 * a + (e >> 4), j = 16 * (a + 1) + (e & 15);
-            Pm[frag_elem<K>(pm_frag_index(a, j / K::KB, C::NKT, K::KB), t, j)] = from_f32<T>(0.f);
         }
     }
     barrier_keep_loads();
@@ -437,6 +442,12 @@ void chunk_prep_kernel(PrepParams p) {
         for (int i = 0; i < 4; ++i) pv[i] = (a > b || 4 * g4 + i <= l16) ? scale * accP[i] : 0.f;
         const int j0 = 16 * b + 4 * g4;
         st4(Pm + frag_elem<K>(pm_frag_index(a, j0 / K::KB, C::NKT, K::KB), l16, j0), pv[0], pv[1], pv[2], pv[3]);
+        // a two-tile k-block holds tile a + 1 beside an even diagonal tile a
+        // (past C when a + 1 = NT): zeros there
+        if (K::TPB == 2 && a == b && a % 2 == 0) {
+            const int jz = j0 + 16;
+            st4(Pm + frag_elem<K>(pm_frag_index(a, jz / K::KB, C::NKT, K::KB), l16, jz), 0.f, 0.f, 0.f, 0.f);
+        }
     }
     barrier_keep_loads();
 
@@ -449,13 +460,13 @@ void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
             for (int i = 0; i < TPT; i += 4) {
                 *reinterpret_cast<T4*>(kt + i) = T4{kw[i][ch], kw[i + 1][ch], kw[i + 2][ch], kw[i + 3][ch]};
-                *reinterpret_cast<T4*>(vt + i) = T4{vx[i][ch], vx[i + 1][ch], vx[i + 2][ch], vx[i + 3][ch]};
+                *reinterpret_cast<T4*>(vt + i) = T4{rv[i][ch], rv[i + 1][ch], rv[i + 2][ch], rv[i + 3][ch]};
             }
         } else {
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
                 kt[i] = kw[i][ch];
-                vt[i] = vx[i][ch];
+                vt[i] = rv[i][ch];
             }
         }
     }
@@ -476,10 +487,27 @@ void chunk_prep_kernel(PrepParams p) {
             for (int m = 0; m < t; ++m) s -= Lb[t * 17 + m] * x[m];
             x[t] = s;
         }
+        // the block of L^{-1} and of L^{-1} diag(beta), the operand of phase 4;
+        // with two-tile k-blocks phase 4 also reads tile (a, a + 1) for even a:
+        // zeros there
+        const int a = wave;
         if (lane < 16) {
-            float* Zb = sZ + pair_index(wave, wave) * BLK;
+            float* Zb = sZ + pair_index(a, a) * BLK;
+            const float bj = sBeta[16 * a + l16];
+            T* lb = sLB + (16 * a) * LC + 16 * a + l16;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Zb[t * 17 + l16] = x[t];
+            for (int t = 0; t < 16; ++t) {
+                Zb[t * 17 + l16] = x[t];
+                lb[t * LC] = from_f32<T>(x[t] * bj);
+            }
+        } else if (K::TPB == 2 && a % 2 == 0) {
+            T* lb = sLB + (16 * a) * LC + 16 * (a + 1) + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lb[(4 * (g4 - 1) + i) * LC] = from_f32<T>(0.f);
+            if (g4 == 3) {
+#pragma unroll
+                for (int i = 12; i < 16; ++i) lb[i * LC] = from_f32<T>(0.f);
+            }
         }
     }
     barrier_keep_loads();
@@ -505,40 +533,52 @@ void chunk_prep_kernel(PrepParams p) {
             for (int i = 0; i < 4; ++i)
                 x = __builtin_amdgcn_mfma_f32_16x16x4f32(Za[l16 * 17 + 4 * g4 + i], m[i], x, 0, 0, 0);
             float* Zab = sZ + pair_index(a, b) * BLK;
+            const float bj = sBeta[16 * b + l16];
+            T* lb = sLB + (16 * a + 4 * g4) * LC + 16 * b + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Zab[(4 * g4 + i) * 17 + l16] = -x[i];
+            for (int i = 0; i < 4; ++i) {
+                Zab[(4 * g4 + i) * 17 + l16] = -x[i];
+                lb[i * LC] = from_f32<T>(-x[i] * bj);
+            }
         }
         barrier_keep_loads();
     }
-    // L^{-1} diag(beta), zero above the diagonal blocks and past C
-    for (int idx = tid; idx < CH * CP; idx += NTHR) {
-        const int t = idx / CP, j = idx % CP;
-        const int a = t >> 4, b = j >> 4;
-        float x = 0.f;
-        if (j < CH && b <= a) x = sZ[pair_index(a, b) * BLK + (t & 15) * 17 + (j & 15)] * sBeta[j];
-        sLB[t * LC + j] = from_f32<T>(x);
-    }
-    barrier_keep_loads();
 
     // ---- 4. W^T = (K e^G)^T (L^{-1} diag(beta))^T and U = L^{-1} diag(beta) V ----
-    for (int task = wave; task < NCT * NT; task += NW) {
-        const int ct = task / NT, ta = task % NT;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < 16 * (ta + 1); kk += E::KSTEP)
-            acc = E::mma(lds_frag<E>(sKtT, LC, 16 * ct, kk, lane), lds_frag<E>(sLB, LC, 16 * ta, kk, lane),
-                         acc);
-        // lane holds W[16ta+l16][16ct+4g4+i]; stored negated
-        const int c = 16 * ct + 4 * g4;
-        st4(Wn + frag_elem<K>((c / K::KB) * NT + ta, l16, c), -acc[0], -acc[1], -acc[2], -acc[3]);
-    }
-    for (int task = wave; task < NT * (DV / 16); task += NW) {
-        const int ta = task % NT, vt = task / NT;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < 16 * (ta + 1); kk += E::KSTEP)
-            acc = E::mma(lds_frag<E>(sLB, LC, 16 * ta, kk, lane), lds_frag<E>(sVtT, LC, 16 * vt, kk, lane),
-                         acc);
-        // lane holds U[16ta+4g4+i][16vt+l16]: the accumulator-layout tile (vt, ta)
-        st4(UT + ((vt * NT + ta) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
+    // A wave owns channel tile ct of W and value tile ct of U: their operands
+    // along the tokens are loaded once, and each fragment of L^{-1} diag(beta)
+    // feeds both products (as the B operand of W^T, the A operand of U).  With
+    // fewer tiles than waves, one set of waves takes W and the other U.
+    {
+        constexpr int NKK = (16 * NT + E::KSTEP - 1) / E::KSTEP;  // k-steps of the last token tile
+        constexpr bool SPLIT = NCT < NW;
+        static_assert(!SPLIT || 2 * NCT <= NW, "tiles per wave");
+        for (int j = wave; j < (SPLIT ? 2 * NCT : NCT); j += NW) {
+            const int ct = SPLIT ? j % NCT : j;
+            const bool dw = !SPLIT || j < NCT, du = !SPLIT || j >= NCT;   // wave-uniform
+            typename E::Frag fk[NKK], fv[NKK];
+#pragma unroll
+            for (int s = 0; s < NKK; ++s) {
+                if (dw) fk[s] = lds_frag<E>(sKtT, LC, 16 * ct, s * E::KSTEP, lane);
+                if (du) fv[s] = lds_frag<E>(sVtT, LC, 16 * ct, s * E::KSTEP, lane);
+            }
+#pragma unroll
+            for (int ta = 0; ta < NT; ++ta) {
+                f32x4_t aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
+#pragma unroll
+                for (int s = 0; s * E::KSTEP < 16 * (ta + 1); ++s) {
+                    const typename E::Frag fl = lds_frag<E>(sLB, LC, 16 * ta, s * E::KSTEP, lane);
+                    if (dw) aw = E::mma(fk[s], fl, aw);
+                    if (du) au = E::mma(fl, fv[s], au);
+                }
+                if (dw) {  // lane holds W[16ta+l16][16ct+4g4+i]; stored negated
+                    const int c = 16 * ct + 4 * g4;
+                    st4(Wn + frag_elem<K>((c / K::KB) * NT + ta, l16, c), -aw[0], -aw[1], -aw[2], -aw[3]);
+                }
+                if (du)    // lane holds U[16ta+4g4+i][16ct+l16]: the accumulator-layout tile (ct, ta)
+                    st4(UT + ((ct * NT + ta) * 64 + lane) * 4, au[0], au[1], au[2], au[3]);
+            }
+        }
     }
 }
 

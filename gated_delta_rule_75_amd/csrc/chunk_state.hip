@@ -26,7 +26,7 @@
 // them on one XCD, so they share the chunk operands through its L2.
 //
 // Loader waves.  When two buffers of the chunk operands plus the workgroup's
-// U^T tiles fit in LDS (one value tile per wave), two extra waves do all the
+// U^T tiles fit in LDS (one value tile per wave), four extra waves do all the
 // staging: they issue the global-to-LDS copies of chunk c+1 right after the
 // barrier that opens chunk c, wait for them, and meet the compute waves at
 // the next barrier.  A wave that issues a 1 KiB copy stalls until the memory
@@ -106,9 +106,10 @@ struct StCfg {
     static constexpr int O_Z = NBUF * BUF;                 // with LW: two z tiles, then two y tiles
     static constexpr int O_Y = O_Z + 2 * ZT;
     static constexpr int BYTES = NBUF * BUF + (LW ? 4 * ZT : 0);
-    // loader waves: two (one to four measure alike; the copy rate of one wave
-    // alone is about half that of two)
-    static constexpr int NLW = LW ? 2 : 0;
+    // loader waves: four (a wave issues a 1 KiB copy about every 170 cycles
+    // on its own; with the copies dealt round-robin, two, three and four
+    // loaders reach 324, 317 and 314 us on the 96-head layer)
+    static constexpr int NLW = LW ? 4 : 0;
     static constexpr int NCOPY = NF + UTB / 1024;            // 1 KiB copies per chunk
     static constexpr int NTHR = 64 * (NW + NLW);
 };
@@ -178,10 +179,10 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             const char* pm = static_cast<const char*>(p.ws.pm) + 16 * lane;
             const char* gm = reinterpret_cast<const char*>(p.ws.gam) + 16 * (lane % (DK / 4));
             const char* ut = static_cast<const char*>(p.ws.ut) + 16 * lane;
-            // copy k of a chunk: fragment k (k < NF) or U^T copy k - NF; loader
-            // li takes copies [li NCOPY / NLW, (li + 1) NCOPY / NLW)
+            // copy k of a chunk: fragment k (k < NF) or U^T copy k - NF.  The
+            // U^T copies, private to the workgroup and so never in L2 already,
+            // go out first; the copies are dealt to the loaders in turn
             const int li = wave - NW;
-            const int k0 = li * C::NCOPY / C::NLW, k1 = (li + 1) * C::NCOPY / C::NLW;
             auto stage_all = [&](int c, int b) {
                 const int64_t wsb = (int64_t)(cbase + c) * H + h;
                 char* buf = smem + b * C::BUF;
@@ -192,9 +193,11 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
                 const char* au = ut + wsb * (int64_t)(DV * CH * sizeof(T));
                 constexpr int TPC = 1024 / C::UTT;   // U^T tiles per copy
+                constexpr int NU = C::NCOPY - C::NF;
 #pragma unroll
-                for (int k = 0; k < C::NCOPY; ++k) {
-                    if (k < k0 || k >= k1) continue;
+                for (int j = 0; j < C::NCOPY; ++j) {
+                    if (j % C::NLW != li) continue;
+                    const int k = j < NU ? C::NF + j : j - NU;
                     const char* src;
                     if (k < C::F_Q) src = aw + (k - C::F_W) * FB;
                     else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
