@@ -179,11 +179,16 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             const char* pm = static_cast<const char*>(p.ws.pm) + 16 * lane;
             const char* gm = reinterpret_cast<const char*>(p.ws.gam) + 16 * (lane % (DK / 4));
             const char* ut = static_cast<const char*>(p.ws.ut) + 16 * lane;
-            // copy k of a chunk: fragment k (k < NF) or U^T copy k - NF.  The
-            // U^T copies, private to the workgroup and so never in L2 already,
-            // go out first; the copies are dealt to the loaders in turn
+            // copy k of a chunk: fragment k (k < NF) or U^T copy k - NF.  Two
+            // groups, each with a barrier of its own: group 1 (U^T and Wn, the
+            // operands of Delta) and group 2 (gam, Kh^T, Qt, Pm), whose last
+            // copies land while Delta is formed.  The U^T copies, private to
+            // the workgroup and so never in L2 already, go out first; the
+            // copies of a group are dealt to the loaders in turn.
             const int li = wave - NW;
-            auto stage_all = [&](int c, int b) {
+            constexpr int NU = C::NCOPY - C::NF;
+            constexpr int NG1 = NU + C::N_W, NG2 = C::NCOPY - NG1;
+            auto stage_group = [&](int c, int b, auto G) {
                 const int64_t wsb = (int64_t)(cbase + c) * H + h;
                 char* buf = smem + b * C::BUF;
                 const char* aw = wn + wsb * (int64_t)(CH * DK * sizeof(T));
@@ -193,11 +198,14 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
                 const char* au = ut + wsb * (int64_t)(DV * CH * sizeof(T));
                 constexpr int TPC = 1024 / C::UTT;   // U^T tiles per copy
-                constexpr int NU = C::NCOPY - C::NF;
+                constexpr int NJ = decltype(G)::value == 1 ? NG1 : NG2;
 #pragma unroll
-                for (int j = 0; j < C::NCOPY; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     if (j % C::NLW != li) continue;
-                    const int k = j < NU ? C::NF + j : j - NU;
+                    int k;
+                    if constexpr (decltype(G)::value == 1) k = j < NU ? C::NF + j : C::F_W + j - NU;
+                    else k = j == 0 ? C::F_G : j <= C::N_K ? C::F_K + j - 1 : j <= C::N_K + C::N_Q ? C::F_Q + j - 1 - C::N_K
+                                                                                            : C::F_P + j - 1 - C::N_K - C::N_Q;
                     const char* src;
                     if (k < C::F_Q) src = aw + (k - C::F_W) * FB;
                     else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
@@ -215,11 +223,26 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                     lds_dma16(src, buf + k * 1024);
                 }
             };
-            if (nch > 0) stage_all(0, 0);
+            using G1 = std::integral_constant<int, 1>;
+            using G2 = std::integral_constant<int, 2>;
+            // copies of a group that every loader issues at least
+            constexpr int M1 = NG1 / C::NLW, M2 = NG2 / C::NLW;
+            static_assert(M1 <= 63 && M2 <= 63, "vmcnt range");
+            if (nch > 0) {
+                stage_group(0, 0, G1{});
+                stage_group(0, 0, G2{});
+            }
             for (int c = 0; c < nch; ++c) {
-                wait_vmcnt<0>();            // chunk c has landed
+                wait_vmcnt<M2>();           // group 1 of chunk c has landed (group 2 may be in flight)
                 barrier_keep_loads();       // ... and the compute waves are done with chunk c-1
-                if (c + 1 < nch) stage_all(c + 1, (c + 1) % 2);
+                if (c + 1 < nch) {
+                    stage_group(c + 1, (c + 1) % 2, G1{});
+                    wait_vmcnt<M1>();       // group 2 of chunk c (group 1 of c+1 may be in flight)
+                } else {
+                    wait_vmcnt<0>();
+                }
+                barrier_keep_loads();       // group 2 of chunk c is in LDS
+                if (c + 1 < nch) stage_group(c + 1, (c + 1) % 2, G2{});
             }
             if constexpr (!C::AUG) {
                 if (nch > 0) barrier_keep_loads();   // matches the compute waves' last y hand-off
@@ -487,6 +510,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                                                                  : f32x4_t{0.f, 0.f, 0.f, 0.f});
             }
 
+        if constexpr (C::LW) barrier_keep_loads();   // group 2 of chunk c (gam, Kh^T, Qt, Pm) has landed
         // S <- gam * S + Kh^T Delta
         const float* gbuf = reinterpret_cast<const float*>(buf + C::F_G * 1024);
 #pragma unroll
