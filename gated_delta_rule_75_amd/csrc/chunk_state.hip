@@ -27,11 +27,12 @@
 //
 // Loader waves.  When two buffers of the chunk operands plus the workgroup's
 // U^T tiles fit in LDS (one value tile per wave), four extra waves do all the
-// staging: they issue the global-to-LDS copies of chunk c+1 right after the
-// barrier that opens chunk c, wait for them, and meet the compute waves at
-// the next barrier.  A wave that issues a 1 KiB copy stalls until the memory
-// pipeline takes it, so the compute waves, which now issue only their z
-// loads and y stores, no longer lose those cycles.  Those move as whole
+// staging: they issue the global-to-LDS copies of chunk c+1 while chunk c is
+// computed and meet the compute waves at its barriers (two per chunk: one
+// once U^T and Wn, the operands of Delta, are in; one before the state
+// update, once the rest is).  A wave that issues a 1 KiB copy stalls until
+// the memory pipeline takes it, so the compute waves, which now issue only
+// their z loads and y stores, no longer lose those cycles.  Those move as whole
 // 128-byte rows: each compute wave loads its share of the next chunk's z rows
 // into registers and writes them into a z tile in LDS at the top of that
 // chunk; outputs go into a y tile and leave as whole rows after the next
@@ -721,7 +722,13 @@ static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_of
 
 template <class E, int DK, int CH, int MODE>
 static hipError_t launch_state_nvt(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
-    if (a.nvt == 1) return launch_state_cfg<StCfg<E, DK, DK, CH, 1, MODE>>(a, co, ord);
+    // One value tile per wave wherever loader waves apply, whatever the
+    // number of chains (on the 16-sequence varlen layer 2.84 ms against 3.04
+    // with two tiles); the transition pairs, with dk + dv columns a chain,
+    // keep the choice made from the chain count (two tiles: 0.74 ms against
+    // 1.07 for 1024 chains).
+    using C1 = StCfg<E, DK, DK, CH, 1, MODE>;
+    if (a.nvt == 1 || (C1::LW && MODE != kModePairs)) return launch_state_cfg<C1>(a, co, ord);
     return launch_state_cfg<StCfg<E, DK, DK, CH, 2, MODE>>(a, co, ord);
 }
 
