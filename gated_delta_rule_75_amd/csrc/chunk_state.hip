@@ -485,14 +485,32 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = ident ? f32x4_t{0.f, 0.f, 0.f, 0.f} : to_f32x4(utc[ta][vt]);
+        // With one value tile per wave, each phase reads all its fragments
+        // before its first product, so that the reads overlap one another
+        // instead of each product waiting for its own (two tiles have no
+        // registers for that).
+        constexpr bool PRE = NVT == 1;
+        if constexpr (PRE) {
+            Frag wf[NKC][NTT];
 #pragma unroll
-        for (int s = 0; s < NKC; ++s)
+            for (int s = 0; s < NKC; ++s)
 #pragma unroll
-            for (int ta = 0; ta < NTT; ++ta) {
-                const Frag wf = frag(buf, C::F_W + s * NTT + ta);
+                for (int ta = 0; ta < NTT; ++ta) wf[s][ta] = frag(buf, C::F_W + s * NTT + ta);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(wf, sf[s][vt], D[ta][vt]);
-            }
+            for (int s = 0; s < NKC; ++s)
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta) D[ta][0] = K::mma(wf[s][ta], sf[s][0], D[ta][0]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < NKC; ++s)
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta) {
+                    const Frag wf = frag(buf, C::F_W + s * NTT + ta);
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(wf, sf[s][vt], D[ta][vt]);
+                }
+        }
         if constexpr (!C::AUG) {
             if constexpr (C::LW) {
                 if (c > 0) store_yrows(c - 1);   // rows of the previous chunk's outputs
@@ -514,16 +532,34 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         if constexpr (C::LW) barrier_keep_loads();   // group 2 of chunk c (gam, Kh^T, Qt, Pm) has landed
         // S <- gam * S + Kh^T Delta
         const float* gbuf = reinterpret_cast<const float*>(buf + C::F_G * 1024);
+        if constexpr (PRE) {
+            Frag kf[NCT][NKT];
+            f32x4_t gm[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(gbuf + 16 * ct + 4 * g4);
+            for (int ct = 0; ct < NCT; ++ct) {
+                gm[ct] = *reinterpret_cast<const f32x4_t*>(gbuf + 16 * ct + 4 * g4);
 #pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) S[ct][vt] *= gm;
+                for (int u = 0; u < NKT; ++u) kf[ct][u] = frag(buf, C::F_K + ct * NKT + u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < NKT; ++u) {
-                const Frag kf = frag(buf, C::F_K + ct * NKT + u);
+            for (int ct = 0; ct < NCT; ++ct) {
+                S[ct][0] *= gm[ct];
 #pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) S[ct][vt] = K::mma(kf, df[u][vt], S[ct][vt]);
+                for (int u = 0; u < NKT; ++u) S[ct][0] = K::mma(kf[ct][u], df[u][0], S[ct][0]);
+            }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(gbuf + 16 * ct + 4 * g4);
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) S[ct][vt] *= gm;
+#pragma unroll
+                for (int u = 0; u < NKT; ++u) {
+                    const Frag kf = frag(buf, C::F_K + ct * NKT + u);
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) S[ct][vt] = K::mma(kf, df[u][vt], S[ct][vt]);
+                }
             }
         }
         if constexpr (C::NBUF == 2) {
@@ -554,23 +590,46 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
                 for (int ta = 0; ta < NTT; ++ta) O[vt][ta] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (PRE) {
+                Frag qf[NKC][NTT], pf[NTT][NKT];
 #pragma unroll
-            for (int s = 0; s < NKC; ++s)
+                for (int s = 0; s < NKC; ++s)
 #pragma unroll
-                for (int ta = 0; ta < NTT; ++ta) {
-                    const Frag qf = frag(buf, C::F_Q + s * NTT + ta);
+                    for (int ta = 0; ta < NTT; ++ta) qf[s][ta] = frag(buf, C::F_Q + s * NTT + ta);
 #pragma unroll
-                    for (int vt = 0; vt < NVT; ++vt) O[vt][ta] = K::mma(sf[s][vt], qf, O[vt][ta]);
-                }
+                for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
-            for (int ta = 0; ta < NTT; ++ta)
+                    for (int u = 0; u < NKT; ++u)
+                        if (u * KB <= 16 * ta + 15) pf[ta][u] = frag(buf, C::F_P + pm_frag_index(ta, u, NKT, KB));
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < NKT; ++u)
-                    if (u * KB <= 16 * ta + 15) {
-                        const Frag pf = frag(buf, C::F_P + pm_frag_index(ta, u, NKT, KB));
+                for (int s = 0; s < NKC; ++s)
 #pragma unroll
-                        for (int vt = 0; vt < NVT; ++vt) O[vt][ta] = K::mma(df[u][vt], pf, O[vt][ta]);
+                    for (int ta = 0; ta < NTT; ++ta) O[0][ta] = K::mma(sf[s][0], qf[s][ta], O[0][ta]);
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                    for (int u = 0; u < NKT; ++u)
+                        if (u * KB <= 16 * ta + 15) O[0][ta] = K::mma(df[u][0], pf[ta][u], O[0][ta]);
+            } else {
+#pragma unroll
+                for (int s = 0; s < NKC; ++s)
+#pragma unroll
+                    for (int ta = 0; ta < NTT; ++ta) {
+                        const Frag qf = frag(buf, C::F_Q + s * NTT + ta);
+#pragma unroll
+                        for (int vt = 0; vt < NVT; ++vt) O[vt][ta] = K::mma(sf[s][vt], qf, O[vt][ta]);
                     }
+#pragma unroll
+                for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                    for (int u = 0; u < NKT; ++u)
+                        if (u * KB <= 16 * ta + 15) {
+                            const Frag pf = frag(buf, C::F_P + pm_frag_index(ta, u, NKT, KB));
+#pragma unroll
+                            for (int vt = 0; vt < NVT; ++vt) O[vt][ta] = K::mma(df[u][vt], pf, O[vt][ta]);
+                        }
+            }
 #pragma unroll
             for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
