@@ -392,7 +392,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 }
         }
         if constexpr (C::LW && !C::AUG) {
-            if (gz) load_zrows(c);
+            if (gz && c == 0) load_zrows(c);   // later chunks' rows go out right after the first barrier
         } else if (!C::AUG && gz) {
             const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
 #pragma unroll
@@ -425,6 +425,13 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
     };
 
+    // checkpoint parameters, read once: kernel-argument loads inside the loop
+    // would share the LDS wait counter and make every fragment read wait for
+    // all the others
+    float* ckpt = p.ckpt;
+    int ck_every = p.ckpt_every > 0 ? p.ckpt_every : 1;
+    int64_t ck_cap = p.ckpt_cap, ck_base = ckpt ? (int64_t)p.ckpt_off[n] : 0;
+    asm volatile("" : "+s"(ckpt), "+s"(ck_every), "+s"(ck_cap), "+s"(ck_base));
     if (nch > 0) {
         if constexpr (!C::LW) stage(0, 0, J_0{}, J_E{});
         load_uz(0);
@@ -470,6 +477,8 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
                     for (int vt = 0; vt < NVT; ++vt)
                         zzc[ta][vt] = *reinterpret_cast<const T4*>(zt + zy_off(ta, vt));
+                // the next chunk's z rows: in flight for the whole of this chunk
+                if constexpr (!C::AUG) load_zrows(cn);
             }
         }
 
@@ -564,14 +573,14 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
         if constexpr (C::NBUF == 2) {
             if constexpr (!C::LW) stage(cn, nb, J_H{}, J_E{});
-            load_uz(cn);
+            if constexpr (!C::LW) load_uz(cn);
         }
         if constexpr (!C::AUG) {
             // prefix-cache checkpoint: the state after this chunk
-            if (p.ckpt && (c + 1) % p.ckpt_every == 0 && (int64_t)(c + 1) * CH <= len) {
-                const int64_t row = p.ckpt_off[n] + (c + 1) / p.ckpt_every - 1;
-                if (row < p.ckpt_cap) {
-                    float* dst = p.ckpt + (row * H + h) * DK * (int64_t)DV;
+            if (ckpt && (c + 1) % ck_every == 0 && (int64_t)(c + 1) * CH <= len) {
+                const int64_t row = ck_base + (c + 1) / ck_every - 1;
+                if (row < ck_cap) {
+                    float* dst = ckpt + (row * H + h) * DK * (int64_t)DV;
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
