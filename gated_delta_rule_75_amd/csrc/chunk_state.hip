@@ -580,7 +580,10 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             if (ckpt && (c + 1) % ck_every == 0 && (int64_t)(c + 1) * CH <= len) {
                 const int64_t row = ck_base + (c + 1) / ck_every - 1;
                 if (row < ck_cap) {
-                    float* dst = ckpt + (row * H + h) * DK * (int64_t)DV;
+                    // global address space: a generic store would also count on the
+                    // LDS wait counter
+                    __attribute__((address_space(1))) float* dst =
+                        (__attribute__((address_space(1))) float*)(ckpt + (row * H + h) * DK * (int64_t)DV);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll

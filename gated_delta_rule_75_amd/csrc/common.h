@@ -146,10 +146,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the compiler from moving memory accesses across it.  A caller that needs a
 // global-to-LDS copy to have landed waits for it (s_waitcnt vmcnt) first.
 __device__ __forceinline__ void barrier_keep_loads() {
+    // no instruction is scheduled across it either (work placed after a
+    // barrier in the source stays after it, and the reverse)
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fused input step: unit q and k as x / sqrt(sum x^2 + kNormEps), the
