@@ -200,24 +200,31 @@ void chunk_prep_kernel(PrepParams p) {
     using GRaw = typename std::conditional<C::FUSED, T4, f32x4_t>::type;
     GRaw rg[TPT];
     T4 rk[TPT], rq[TPT], rv[TPT];
+    // beta, then g: vector loads complete in issue order, so the running
+    // sums below wait for these alone while k, q and v are still on their way
+    using BRaw = typename std::conditional<C::FUSED, T, float>::type;
+    BRaw braw = BRaw(0.f);
+    if (tid < CH && tid < nvalid) {
+        const int64_t at = (ts + tid) * H + h;
+        braw = static_cast<const BRaw*>(p.beta)[at];
+    }
+    int64_t rows[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) rows[i] = (ts + (tl0 + i < nvalid ? tl0 + i : 0)) * H + h;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-        const int t = tl0 + i;
-        const int64_t row = (ts + (t < nvalid ? t : 0)) * H + h;
-        if constexpr (C::FUSED) rg[i] = *reinterpret_cast<const T4*>(static_cast<const T*>(p.g) + row * DK + c0);
-        else rg[i] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + row * DK + c0);
-        rk[i] = *reinterpret_cast<const T4*>(gk + row * DK + c0);
-        rq[i] = *reinterpret_cast<const T4*>(gq + row * DK + c0);
-        rv[i] = *reinterpret_cast<const T4*>(gv + row * DV + c0);
+        if constexpr (C::FUSED) rg[i] = *reinterpret_cast<const T4*>(static_cast<const T*>(p.g) + rows[i] * DK + c0);
+        else rg[i] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.g) + rows[i] * DK + c0);
     }
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) rk[i] = *reinterpret_cast<const T4*>(gk + rows[i] * DK + c0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) rq[i] = *reinterpret_cast<const T4*>(gq + rows[i] * DK + c0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) rv[i] = *reinterpret_cast<const T4*>(gv + rows[i] * DV + c0);
     if (tid < CH) {
-        float b = 0.f;
-        if (tid < nvalid) {
-            const int64_t at = (ts + tid) * H + h;
-            if constexpr (C::FUSED) b = sigmoid(to_f32(static_cast<const T*>(p.beta)[at]));
-            else b = static_cast<const float*>(p.beta)[at];
-        }
-        sBeta[tid] = b;
+        if constexpr (C::FUSED) sBeta[tid] = tid < nvalid ? sigmoid(to_f32(braw)) : 0.f;
+        else sBeta[tid] = braw;
     }
 
     T* Wn = static_cast<T*>(p.ws.wn) + wsb * (CH * DK);
