@@ -168,6 +168,18 @@ def test_prefill_many_chains_wide_scan_waves(kda):
     assert_parity("varlen 1024 chains", inp, y, fs, yo, so, TOL["bf16"])
 
 
+def test_prefill_many_chains_two_value_tiles(kda):
+    """fp32, dk = dv = 128 and 1024 (sequence, head) chains: each scan wave takes
+    two 16-column value tiles and stages its own share of the chunk operands
+    (the operands of one chunk do not fit twice in LDS beside loader waves)."""
+    rng = np.random.default_rng(8)
+    lens = rng.integers(1, 61, 16).tolist()
+    inp = kda_inputs.make_prefill(lens, 64, 128, 128, "f32", True, 0.05, 80, 8.0, 4.0)
+    y, fs = run_prefill(kda, inp, chunk=64)
+    yo, so = oracle_prefill(inp)
+    assert_parity("fp32 1024 chains", inp, y, fs, yo, so, TOL["f32"])
+
+
 def test_prefill_varlen_workload_shape_reduced(kda):
     """Varlen workload recipe (16 sequences, lengths uniform) at reduced lengths and heads."""
     inp = kda_inputs.make_workload(2, H=6, lmin=20, lmax=700)
