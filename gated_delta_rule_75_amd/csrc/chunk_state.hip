@@ -12,8 +12,8 @@
 // loads, double-buffered so chunk c+1 streams in while chunk c is computed.
 // In LDS each operand fragment (16 rows x one k-block) is stored in lane
 // order, 16 bytes per lane, so that every wave reads a fragment with one
-// conflict-free 16-byte access per lane.  U^T and z, private to a wave, go
-// straight to registers one chunk ahead.
+// conflict-free 16-byte access per lane.  Without loader waves (below), U^T
+// and z, private to a wave, go straight to registers one chunk ahead.
 // Products (lane layout: rows 4*(l/16)+i, column l%16 of a 16x16 tile):
 //     Delta [t][v]  += Wn[t][c] . S[c][v]            A = Wn rows,   B = S
 //     O^T  [v][t]   += S^T[v][c] . Qt^T[c][t]        A = S,         B = Qt rows
@@ -33,11 +33,13 @@
 // update, once the rest is).  A wave that issues a 1 KiB copy stalls until
 // the memory pipeline takes it, so the compute waves, which now issue only
 // their z loads and y stores, no longer lose those cycles.  Those move as whole
-// 128-byte rows: each compute wave loads its share of the next chunk's z rows
-// into registers and writes them into a z tile in LDS at the top of that
-// chunk; outputs go into a y tile and leave as whole rows after the next
-// barrier.  (Per-lane accesses in the accumulator layout touched 16 lines
-// for 32 bytes each.)
+// 128-byte rows: right after the first barrier of chunk c each compute wave
+// loads its share of chunk c+1's z rows into registers, and writes them into
+// a z tile in LDS at the top of chunk c+1; outputs go into a y tile and leave
+// as whole rows after the next chunk's first barrier.  (Per-lane accesses in
+// the accumulator layout touched 16 lines for 32 bytes each.)  With one value
+// tile per wave, each phase also reads all of its fragments from LDS before
+// its first product.
 #include <type_traits>
 
 #include "launch.h"
