@@ -6,7 +6,8 @@
 //  1. decay: a wave owns 64 channels of a slice of consecutive tokens, so each
 //     load instruction reads whole 128-byte rows (a layout with fewer channels
 //     per wave touched four times the cache lines per byte); a thread holds
-//     TPT consecutive tokens x 4 consecutive channels of g, k, q, v.  The
+//     TPT consecutive tokens x 4 consecutive channels of g, k, q, v (beta and
+//     g are loaded first, so that the sums below wait for them alone).  The
 //     in-chunk running sum G of g is a per-thread sum, a shuffle scan over
 //     the wave's token groups, and a sum of the earlier slices' totals
 //     exchanged through LDS.
@@ -20,7 +21,11 @@
 //  3. L = I + diag(beta) A is unit lower triangular; its inverse is blocked:
 //     16 x 16 diagonal blocks by forward substitution, then off-diagonal
 //     blocks level by level, X_ab = -X_aa sum_{b<=c<a} L_ac X_cb (fp32 MFMA).
-//  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA.
+//     Each block is also written, times beta_j, in bf16 into the table of
+//     L^{-1} diag(beta) that phase 4 reads.
+//  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA, a
+//     wave taking one channel tile of W and one value tile of U, so that
+//     every fragment of L^{-1} diag(beta) feeds both products.
 // Qt, Kh and gam leave straight from the decay phase; the tiles of W, U and
 // P leave as they are produced.
 //
