@@ -6,7 +6,7 @@
 // in api.cpp.
 //
 // The segments are cut into G groups of L ~ sqrt(nseg).  Three launches of
-// one chain kernel: (1) each group's pairs composed into one pair, all groups
+// the chain kernel (in a narrow or a wide form, below): (1) each group's pairs composed into one pair, all groups
 // side by side; (2) one chain over the G group pairs from S0, giving the
 // state entering each group; (3) each group's segments replayed from its
 // entering state, all groups side by side, writing every segment's entering
@@ -16,7 +16,7 @@
 
 namespace kda {
 
-// One chain of pairs applied to a 64-column slice of a DK-row state X:
+// One chain of pairs applied to a slice of the columns of a DK-row state X:
 //     for j = 0 .. L-1:  [out_each[s0 + j] = X;]  X <- M_{s0+j} X + A_{s0+j}
 //     [out_final[g] = X]
 // with (M_s, A_s) from the pair rows [M | Sloc] of `pairs` (row width W).
@@ -25,11 +25,19 @@ namespace kda {
 // identity and take no additive term, A = Sloc on the rest), which composes
 // the chain's pairs into one pair (page "Exercices", Niveau 3 Q21-Q22).
 //
-// Four waves, one 16-column tile each; X stays in MFMA accumulator tiles
-// (lane: rows 4 (l/16) + i, column l%16) and enters the next product as the B
-// operand, MFMA i taking row 4 (l/16) + i (fp32 16x16x4).  M_{s+1} streams
-// into the other half of a double buffer in LDS by global-to-LDS copies
-// while step s computes; the barrier between steps waits for LDS only.
+// Narrow form, for launches with few chains (one round of workgroups): a
+// step is a DK x DK by DK x 16 product on fp32 MFMA 16x16x4.  Sixteen
+// columns a workgroup spread a chain over many CUs (the steps of a chain
+// are sequential, and a 64-column slice kept one CU busy for ~8k cycles a
+// step: the one chain over the group pairs takes 55 us against 104).  Four
+// waves split the rows: wave w forms rows [w DK/4, (w+1) DK/4) of the new X
+// in accumulator tiles (lane: rows 4 (l/16) + i, column l%16).
+// The state crosses between waves through LDS, stored transposed (X^T, a
+// column per row) so that a lane reads the four k values of its MFMA
+// operands with one 16-byte access; two buffers alternate, one barrier a
+// step.  Each wave reads its rows of M_s straight from memory as 16-byte
+// runs, one step ahead, into registers: lane (l%16, l/16) of k-block kb
+// holds M[row][16 kb + 4 (l/16) + i], MFMA i of the k-block taking that k.
 struct ChainParams {
     int H, nseg, L;          // pairs entries, steps per chain (chain g starts at g L)
     int W;                   // row width of a pair: dk + dv
@@ -42,7 +50,110 @@ struct ChainParams {
 };
 
 template <int DK>
-__global__ __launch_bounds__(256) void kcp_chain_kernel(ChainParams p) {
+__global__ __launch_bounds__(256) void kcp_chain_narrow_kernel(ChainParams p) {
+    constexpr int RW = DK / 4;          // rows per wave
+    constexpr int NRT = RW / 16;        // 16-row tiles per wave
+    constexpr int NKB = DK / 16;        // 16-wide k-blocks
+    constexpr int XP = DK + 4;          // LDS pitch of a column of X^T (floats)
+    __shared__ __attribute__((aligned(16))) float sX[2][16 * XP];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int col = blockIdx.z * 16 + l16;   // this lane's state column
+    const int s0 = g * p.L;
+    const int L = p.nseg - s0 < p.L ? p.nseg - s0 : p.L;
+    if (L <= 0) return;
+    const int dv = p.W - DK;
+    const int r0 = wave * RW;                // first row of the wave
+    auto prow = [&](int s, int r) { return p.pairs + (((int64_t)s * p.H + h) * DK + r) * p.W; };
+    const bool ident = p.aug && col < DK;    // transition columns: start I, no additive term
+    const int acol = p.aug ? col : DK + col;
+
+    // M rows of the wave and the additive terms of its accumulator rows, step s
+    auto load = [&](int s, f32x4_t (*M)[NKB], f32x4_t* A) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const float* pr = prow(s, r0 + 16 * rt + l16);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) M[rt][kb] = *reinterpret_cast<const f32x4_t*>(pr + 16 * kb + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) A[rt][i] = ident ? 0.f : prow(s, r0 + 16 * rt + 4 * g4 + i)[acol];
+        }
+    };
+
+    // the initial state: this wave's rows in registers and X^T in LDS buffer 0
+    f32x4_t X[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 16 * rt + 4 * g4 + i;
+            float x = 0.f;
+            if (p.aug) x = (col == r) ? 1.f : 0.f;
+            else if (p.init) x = p.init[(((int64_t)g * p.H + h) * DK + r) * dv + col];
+            X[rt][i] = x;
+        }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+        *reinterpret_cast<f32x4_t*>(&sX[0][l16 * XP + r0 + 16 * rt + 4 * g4]) = X[rt];
+    f32x4_t M[NRT][NKB], A[NRT];
+    load(s0, M, A);
+    __syncthreads();
+    for (int j = 0; j < L; ++j) {
+        const int s = s0 + j;
+        if (p.out_each) {
+            float* o = p.out_each + ((int64_t)s * p.H + h) * DK * dv;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[(int64_t)(r0 + 16 * rt + 4 * g4 + i) * dv + col] = X[rt][i];
+        }
+        f32x4_t Mn[NRT][NKB], An[NRT];
+        if (j + 1 < L) load(s + 1, Mn, An);
+        const float* xb = sX[j & 1];
+        f32x4_t xo[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) xo[kb] = *reinterpret_cast<const f32x4_t*>(xb + l16 * XP + 16 * kb + 4 * g4);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            f32x4_t acc = A[rt];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M[rt][kb][i], xo[kb][i], acc, 0, 0, 0);
+            X[rt] = acc;
+            *reinterpret_cast<f32x4_t*>(&sX[(j + 1) & 1][l16 * XP + r0 + 16 * rt + 4 * g4]) = acc;
+        }
+        __syncthreads();   // the new X^T is complete; the old buffer is free for the step after
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            A[rt] = An[rt];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) M[rt][kb] = Mn[rt][kb];
+        }
+    }
+    if (p.out_final) {
+        float* o = p.out_final + ((int64_t)g * p.H + h) * DK * p.ncol;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[(int64_t)(r0 + 16 * rt + 4 * g4 + i) * p.ncol + col] = X[rt][i];
+    }
+}
+
+// Wide form, for launches with many chains side by side: a 64-column slice
+// a workgroup, four waves of 16 columns, each forming all DK rows of its
+// columns; X stays in accumulator tiles and enters the next product as the B
+// operand, MFMA i taking row 4 (l/16) + i (fp32 16x16x4); M_{s+1} streams into
+// the other half of a double buffer in LDS by global-to-LDS copies while
+// step s computes, and the barrier between steps waits for LDS only.  It
+// reads each M once for 64 columns, where the narrow form reads it once for
+// 16: with more than one round of workgroups the narrow form is bound by
+// those reads (152 us against 103 for 1024 narrow workgroups).
+template <int DK>
+__global__ __launch_bounds__(256) void kcp_chain_wide_kernel(ChainParams p) {
     constexpr int NRT = DK / 16;                 // 16-row tiles of the state
     constexpr int RPC = 1024 / (DK * 4);         // M rows per 1 KiB copy
     constexpr int NCP = DK / RPC;                // copies per M
@@ -138,18 +249,27 @@ __global__ __launch_bounds__(256) void kcp_chain_kernel(ChainParams p) {
 }
 
 template <int DK>
-static hipError_t launch_chain_t(const ChainParams& p, int nchain, int ncol, hipStream_t stream) {
-    constexpr int MBUF = (DK / (1024 / (DK * 4))) * (1024 + 16);
-    auto kern = kcp_chain_kernel<DK>;
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             2 * MBUF);
+static hipError_t launch_chain_t(const ChainParams& p, int nchain, hipStream_t stream) {
+    // narrow form while its workgroups fit in one round at two per CU
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nchain, p.H, ncol / 64), dim3(256), 2 * MBUF, stream, p);
+    const int64_t narrow_wgs = (int64_t)nchain * p.H * (p.ncol / 16);
+    if (narrow_wgs <= 2 * (int64_t)cus) {
+        hipLaunchKernelGGL(kcp_chain_narrow_kernel<DK>, dim3(nchain, p.H, p.ncol / 16), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
+    constexpr int MBUF = (DK / (1024 / (DK * 4))) * (1024 + 16);
+    auto kern = kcp_chain_wide_kernel<DK>;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * MBUF);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(nchain, p.H, p.ncol / 64), dim3(256), 2 * MBUF, stream, p);
     return hipGetLastError();
 }
 
 static hipError_t launch_chain(int dk, const ChainParams& p, int nchain, hipStream_t stream) {
-    return dk == 128 ? launch_chain_t<128>(p, nchain, p.ncol, stream) : launch_chain_t<64>(p, nchain, p.ncol, stream);
+    return dk == 128 ? launch_chain_t<128>(p, nchain, stream) : launch_chain_t<64>(p, nchain, stream);
 }
 
 int kcp_group_len(int nseg) {
