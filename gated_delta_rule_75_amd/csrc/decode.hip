@@ -181,14 +181,34 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
     f32x4_t S[RPT], Sc[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = *reinterpret_cast<const f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg);
+    // a draft token's inputs, one element per thread (k, q, g below dk; v, z,
+    // beta below dv), loaded while the token before it is computed
+    static_assert(DK <= 256 && DV <= 256, "one input element per thread");
+    float xk = 0.f, xq = 0.f, xg = 0.f, xv = 0.f, xz = 0.f, xb = 0.f;
+    auto fetch = [&](int t, float& fk, float& fq, float& fg, float& fv, float& fz, float& fb) {
+        const int64_t tok = ((int64_t)n * Td + t) * H + h;
+        if (tid < DK) {
+            fk = gload(k + tok * DK + tid);
+            fq = gload(q + tok * DK + tid);
+            fg = g[tok * DK + tid];
+        }
+        if (tid < DV) {
+            fv = gload(v + tok * DV + tid);
+            fz = z ? gload(z + tok * DV + tid) : 0.f;
+            fb = beta[tok];
+        }
+    };
+    fetch(0, xk, xq, xg, xv, xz, xb);
     for (int t = 0; t < steps; ++t) {
         const int64_t tok = ((int64_t)n * Td + t) * H + h;
-        const int64_t kb = tok * DK, vb = tok * DV;
-        for (int c = tid; c < DK; c += 256) {
-            s_k[c] = gload(k + kb + c);
-            s_q[c] = gload(q + kb + c);
-            s_a[c] = fast_exp(g[kb + c]);
+        const int64_t vb = tok * DV;
+        if (tid < DK) {
+            s_k[tid] = xk;
+            s_q[tid] = xq;
+            s_a[tid] = fast_exp(xg);
         }
+        float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nz = 0.f, nb = 0.f;
+        if (t + 1 < steps) fetch(t + 1, nk, nq, ng, nv, nz, nb);
         __syncthreads();
         if (tid < kWave) {
             float pk = 0.f;
@@ -219,11 +239,11 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
                 U += s_u[r][j];
                 W += s_w[r][j];
             }
-            const float d = beta[tok] * (gload(v + vb + j) - U);
+            const float d = xb * (xv - U);
             s_delta[j] = d;
             if (y) {
                 float o = scale * (W + s_kq * d);
-                if (z) o *= sigmoid(gload(z + vb + j));
+                if (z) o *= sigmoid(xz);
                 gstore(y + vb + j, o);
             }
         }
@@ -236,6 +256,7 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
             for (int r = 0; r < RPT; ++r) Sc[r] = S[r];
         }
         __syncthreads();  // s_k, s_delta are rewritten by the next token
+        xk = nk; xq = nq; xg = ng; xv = nv; xz = nz; xb = nb;
     }
     if (acc > 0) {
 #pragma unroll
