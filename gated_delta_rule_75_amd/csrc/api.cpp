@@ -68,7 +68,8 @@ int64_t seg_chunks(int64_t seg_len, int chunk, int num_seqs) {
 
 // Value tiles per scan wave: two (half the operand traffic per column) when
 // that still leaves many workgroups; a scan workgroup covers 64 NVT state
-// columns (4 waves of 16 NVT).
+// columns (4 waves of 16 NVT).  The scan launcher keeps one tile wherever its
+// loader waves apply (all but the KCP pairs), which measured faster there.
 int pick_nvt(int64_t chains, int dvt) {
     if (dvt % 128 != 0) return 1;
 #ifdef KDA_SCAN_NVT
