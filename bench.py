@@ -24,6 +24,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+WARM_MS = 50.0                   # untimed GPU work before each extra workload's timed calls
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
 ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode", "prefill_checkpoints",
@@ -76,11 +77,22 @@ def counter_traffic(kernel: str):
     return rec["traffic_bytes"] if h.hexdigest() == rec["src_sha256"] else None
 
 
-def time_steps(fn, steps: int, warmup: int, torch):
-    """Average ms per call of fn over `steps` calls, HIP events on the current stream."""
+def time_steps(fn, steps: int, warmup: int, torch, warm_ms: float = 0.0):
+    """Average ms per call of fn over `steps` calls, HIP events on the current stream.
+    Untimed first: `warmup` calls, then (warm_ms > 0) more calls until about
+    warm_ms of GPU time has run, so that the clocks have settled (a cold GPU
+    runs the K3 layer ~10 % slower for the first few dozen calls)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if warm_ms > 0:
+        t = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        one = max((time.perf_counter() - t) * 1e3, 1e-3)
+        for _ in range(int(warm_ms / one)):
+            fn()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -175,7 +187,7 @@ def bench_varlen(args, torch, kda, kda_inputs, dev):
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], z=d["z"],
                       initial_state=d["s0"], chunk=w["chunk"], y=y, final_state=fs, workspace=ws)
 
-    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch)
+    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch, WARM_MS)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, len(lens), True, True)
     out = dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3),
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -199,7 +211,7 @@ def bench_kcp(args, torch, kda, kda_inputs, dev):
         kda.kcp_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], S, chunk=w["chunk"],
                      workspace=ws, y=y, final_state=fs)
 
-    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch)
+    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch, WARM_MS)
     nbytes = prefill_bytes(T, H, dk, dv, 2, False, 1, False, True)
     out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), segments=S,
                gbs_single_pass=nbytes / (ms * 1e-3) / 1e9,
@@ -257,7 +269,7 @@ def bench_checkpoints(args, torch, kda, kda_inputs, dev):
     d = gpu_inputs(torch, [T], H, dk, dv, True, 0.0, kda_inputs.workload_seed(1), dev)
     ms, _ = time_steps(lambda: kda.chunk_fwd_checkpointed(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                           interval, z=d["z"], chunk=C),
-                       max(1, args.steps // 2), 2, torch)
+                       max(1, args.steps // 2), 2, torch, WARM_MS)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True) + (T // interval) * H * dk * dv * 4
     out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), interval=interval, checkpoints=T // interval,
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -287,9 +299,9 @@ def bench_replay(args, torch, kda, kda_inputs, dev):
     acc = torch.randint(0, Td + 1, (N,), generator=gen, device=dev).to(torch.int32)
     y = torch.empty(N, Td, H, dv, dtype=torch.bfloat16, device=dev)
     ms_v, _ = time_steps(lambda: kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
-                                                   z=x["z"], y=y), 20, 2, torch)
+                                                   z=x["z"], y=y), 20, 2, torch, WARM_MS)
     ms_c, _ = time_steps(lambda: kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
-                                                   accepted=acc, z=x["z"], want_y=False), 20, 2, torch)
+                                                   accepted=acc, z=x["z"], want_y=False), 20, 2, torch, WARM_MS)
     st = H * dk * dv * 4                              # one request's states
     tok = H * (2 * dk * 2 + dv * 2 * 2 + dk * 4 + 4)   # one draft token's inputs
     a = [int(t) for t in acc.cpu().tolist()]
@@ -318,7 +330,7 @@ def bench_prefill_chunk32(args, torch, kda, kda_inputs, dev):
     ws = torch.empty(kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, C, 1, T), dtype=torch.uint8,
                      device=dev)
     ms, _ = time_steps(lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C,
-                                             y=y, final_state=fs, workspace=ws), args.steps, 2, torch)
+                                             y=y, final_state=fs, workspace=ws), args.steps, 2, torch, WARM_MS)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True)
     out = dict(ms=ms, chunk=C, tokens_per_s=T / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -350,7 +362,7 @@ def bench_prefill_fused(args, torch, kda, kda_inputs, dev):
         kda.chunk_fwd_fused(d["q"], d["k"], d["v"], d["a"], d["b"], z=d["z"], chunk=C, y=y,
                             final_state=fs, workspace=ws)
 
-    ms, _ = time_steps(step, args.steps, 2, torch)
+    ms, _ = time_steps(step, args.steps, 2, torch, WARM_MS)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True, gate_elt=2)
     out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), bytes=nbytes,
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -395,7 +407,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads (%s), 'all' or 'none'" % ",".join(ALL_WORKLOADS))
     ap.add_argument("--cpu-sample-heads", type=int, default=96)
