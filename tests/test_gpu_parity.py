@@ -148,6 +148,15 @@ def test_prefill_varlen_with_ragged_and_empty_sequences(kda):
     np.testing.assert_array_equal(fs[4].numpy(), inp.S0[4].numpy())
 
 
+@pytest.mark.parametrize("lens", [[0], [0, 0, 0]])
+def test_prefill_zero_tokens(kda, lens):
+    """No tokens at all: y is empty and every final state is its initial state."""
+    inp = kda_inputs.make_prefill(lens, 3, 64, 64, "bf16", True, 0.05, 79, 0.0, 0.0)
+    y, fs = run_prefill(kda, inp, chunk=64)
+    assert y.shape == (0, 3, 64)
+    np.testing.assert_array_equal(fs.numpy(), inp.S0.numpy())
+
+
 def test_prefill_varlen_many_short_sequences(kda):
     """More than 1024 packed sequences (no longest-first reordering), lengths 0..40."""
     rng = np.random.default_rng(5)
@@ -377,6 +386,19 @@ def test_kcp_ragged_segments(kda):
     torch.cuda.synchronize()
     yo, so = oracle_prefill(inp)
     assert_parity("kcp ragged", inp, y.cpu(), fs.cpu(), yo, so, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,d,T,nseg", [("f32", 64, 512, 1), ("f32", 64, 130, 130), ("bf16", 128, 1000, 64)])
+def test_kcp_degenerate_segment_counts(kda, dtype, d, T, nseg):
+    """One segment (no scan at all), one token a segment, and segments shorter
+    than a chunk with the trailing ones empty."""
+    inp = kda_inputs.make_workload(3, "segment", lens=[T], H=2, dk=d, dv=d, dtype=dtype,
+                                   s0_std=0.05, gated=True)
+    y, fs = kda.kcp_scan(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(),
+                         inp.beta.cuda(), nseg, z=inp.z.cuda(), initial_state=inp.S0.cuda())
+    torch.cuda.synchronize()
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"kcp T={T} nseg={nseg}", inp, y.cpu(), fs.cpu(), yo, so, TOL[dtype])
 
 
 def test_kcp_equals_chunk_fwd(kda):
