@@ -19,6 +19,18 @@
 
 namespace kda {
 
+// Request-head of hardware workgroup i.  Workgroups i, i + 8, i + 16, ... run
+// on one XCD; handing each XCD its heads in runs of two consecutive ones
+// (64 KiB states, so 128 KiB runs) instead of one made the 128 x 96 step
+// 6 % faster (5.35 against 5.72 ms per 20 steps, alternating runs, three
+// boxes); other run lengths, from 3 to 1536 heads, moved it by -7 % to +4 %
+// from box to box.  Applied when the grid is a multiple of 16.
+__device__ __forceinline__ int decode_head(int i, int nb) {
+    if (nb % 16 != 0) return i;
+    const int x = i % 8, j = i / 8;
+    return (j / 2) * 16 + x * 2 + j % 2;
+}
+
 //
 // FUSED: q and k arrive unnormalised and the gates as pre-activations a (per
 // key channel) and b (per head), in the storage dtype: alpha = exp(g_min
@@ -45,7 +57,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
     __shared__ float s_delta[DV];
     __shared__ float s_kq, s_ik, s_iq;
 
-    const int nh = blockIdx.x;
+    const int nh = decode_head(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
     const int64_t kb = (int64_t)nh * DK, vb = (int64_t)nh * DV;
