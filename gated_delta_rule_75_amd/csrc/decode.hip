@@ -160,7 +160,10 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
 // the request's draft tokens with the state in registers, emits every draft
 // token's output (when y is given), keeps a copy of the state after the
 // accepted prefix, and writes that copy back (when accepted is given).
-template <typename T, int DK, int DV>
+// KEEP: both at once, so the copy is a second register set; otherwise the
+// state in hand after the loop is the one to write (without outputs the loop
+// stops at the accepted prefix), and a third workgroup fits on each SIMD.
+template <typename T, int DK, int DV, bool KEEP>
 __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H, const T* __restrict__ q,
                                                      const T* __restrict__ k, const T* __restrict__ v,
                                                      const float* __restrict__ g,
@@ -178,7 +181,8 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
     __shared__ float s_delta[DV];
     __shared__ float s_kq;
 
-    const int nh = blockIdx.x, n = nh / H, h = nh % H;
+    // placement as in the decode step (the commit, which writes the state, 3 % faster)
+    const int nh = decode_head(blockIdx.x, gridDim.x), n = nh / H, h = nh % H;
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
     int acc = 0;
@@ -190,11 +194,13 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
     if (steps == 0) return;
     float* st = state + (int64_t)nh * DK * DV;
 
-    f32x4_t S[RPT], Sc[RPT];
+    f32x4_t S[RPT], Sc[KEEP ? RPT : 1];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = *reinterpret_cast<const f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg);
     // a draft token's inputs, one element per thread (k, q, g below dk; v, z,
-    // beta below dv), loaded while the token before it is computed
+    // beta below dv), loaded while the token before it is computed: the
+    // barriers in the loop wait for LDS operations only, so those loads stay
+    // in flight across them
     static_assert(DK <= 256 && DV <= 256, "one input element per thread");
     float xk = 0.f, xq = 0.f, xg = 0.f, xv = 0.f, xz = 0.f, xb = 0.f;
     auto fetch = [&](int t, float& fk, float& fq, float& fg, float& fv, float& fz, float& fb) {
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
         }
         float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nz = 0.f, nb = 0.f;
         if (t + 1 < steps) fetch(t + 1, nk, nq, ng, nv, nz, nb);
-        __syncthreads();
+        barrier_keep_loads();
         if (tid < kWave) {
             float pk = 0.f;
             for (int c = tid; c < DK; c += kWave) pk += s_k[c] * s_q[c];
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
             s_u[rg][4 * cg + i] = u[i];
             s_w[rg][4 * cg + i] = w[i];
         }
-        __syncthreads();
+        barrier_keep_loads();
         if (tid < DV) {
             const int j = tid;
             float U = 0.f, W = 0.f;
@@ -259,31 +265,32 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
                 gstore(y + vb + j, o);
             }
         }
-        __syncthreads();
+        barrier_keep_loads();
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&s_delta[4 * cg]);
 #pragma unroll
         for (int r = 0; r < RPT; ++r) S[r] += s_k[r * RG + rg] * d4;
-        if (t + 1 == acc) {
+        if (KEEP && t + 1 == acc) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) Sc[r] = S[r];
+            for (int r = 0; r < RPT; ++r) Sc[KEEP ? r : 0] = S[r];
         }
-        __syncthreads();  // s_k, s_delta are rewritten by the next token
+        barrier_keep_loads();  // s_k, s_delta are rewritten by the next token
         xk = nk; xq = nq; xg = ng; xv = nv; xz = nz; xb = nb;
     }
     if (acc > 0) {
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
-            __builtin_nontemporal_store(Sc[r], reinterpret_cast<f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg));
+            __builtin_nontemporal_store(KEEP ? Sc[KEEP ? r : 0] : S[r],
+                                        reinterpret_cast<f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg));
     }
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_replay_t(const DecodeArgs& a, int Td, const int32_t* accepted) {
     if (a.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((replay_kernel<T, DK, DV>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
-                       (hipStream_t)a.stream, Td, a.scale, a.H, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const float*)a.g, (const float*)a.beta, (const T*)a.z, accepted,
-                       a.state, (T*)a.y);
+    auto kern = a.y && accepted ? replay_kernel<T, DK, DV, true> : replay_kernel<T, DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.N * a.H)), dim3(256), 0, (hipStream_t)a.stream, Td, a.scale,
+                       a.H, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.g,
+                       (const float*)a.beta, (const T*)a.z, accepted, a.state, (T*)a.y);
     return hipGetLastError();
 }
 
