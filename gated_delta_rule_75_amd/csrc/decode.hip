@@ -158,12 +158,13 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
 // kept and the recurrence is replayed on chip).  One workgroup per
 // (request, head) loads the state once, runs the decode step above for each of
 // the request's draft tokens with the state in registers, emits every draft
-// token's output (when y is given), keeps a copy of the state after the
-// accepted prefix, and writes that copy back (when accepted is given).
-// KEEP: both at once, so the copy is a second register set; otherwise the
-// state in hand after the loop is the one to write (without outputs the loop
-// stops at the accepted prefix), and a third workgroup fits on each SIMD.
-template <typename T, int DK, int DV, bool KEEP>
+// token's output (when y is given), and writes the state back as it stands
+// after the accepted prefix (when accepted is given), in the middle of the
+// loop when outputs of later draft tokens are still to come.  The state is
+// read only before the loop, so writing it there is safe, and no second
+// register copy is needed (154 VGPRs: three workgroups per SIMD, against two
+// with a copy).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H, const T* __restrict__ q,
                                                      const T* __restrict__ k, const T* __restrict__ v,
                                                      const float* __restrict__ g,
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
     if (steps == 0) return;
     float* st = state + (int64_t)nh * DK * DV;
 
-    f32x4_t S[RPT], Sc[KEEP ? RPT : 1];
+    f32x4_t S[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = *reinterpret_cast<const f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg);
     // a draft token's inputs, one element per thread (k, q, g below dk; v, z,
@@ -269,28 +270,23 @@ __global__ __launch_bounds__(256) void replay_kernel(int Td, float scale, int H,
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&s_delta[4 * cg]);
 #pragma unroll
         for (int r = 0; r < RPT; ++r) S[r] += s_k[r * RG + rg] * d4;
-        if (KEEP && t + 1 == acc) {
+        if (t + 1 == acc) {   // the state after the accepted prefix
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) Sc[KEEP ? r : 0] = S[r];
+            for (int r = 0; r < RPT; ++r)
+                __builtin_nontemporal_store(S[r], reinterpret_cast<f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg));
         }
         barrier_keep_loads();  // s_k, s_delta are rewritten by the next token
         xk = nk; xq = nq; xg = ng; xv = nv; xz = nz; xb = nb;
-    }
-    if (acc > 0) {
-#pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            __builtin_nontemporal_store(KEEP ? Sc[KEEP ? r : 0] : S[r],
-                                        reinterpret_cast<f32x4_t*>(st + (int64_t)(r * RG + rg) * DV + 4 * cg));
     }
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_replay_t(const DecodeArgs& a, int Td, const int32_t* accepted) {
     if (a.N == 0) return hipSuccess;
-    auto kern = a.y && accepted ? replay_kernel<T, DK, DV, true> : replay_kernel<T, DK, DV, false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.N * a.H)), dim3(256), 0, (hipStream_t)a.stream, Td, a.scale,
-                       a.H, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.g,
-                       (const float*)a.beta, (const T*)a.z, accepted, a.state, (T*)a.y);
+    hipLaunchKernelGGL((replay_kernel<T, DK, DV>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
+                       (hipStream_t)a.stream, Td, a.scale, a.H, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const float*)a.g, (const float*)a.beta, (const T*)a.z, accepted,
+                       a.state, (T*)a.y);
     return hipGetLastError();
 }
 
