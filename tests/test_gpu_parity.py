@@ -308,6 +308,32 @@ def test_replay_outputs_and_commit_in_one_call(kda):
     assert rel_l2(state.cpu().double().numpy(), so) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_replay_long_drafts_across_input_groups(kda, dtype, d):
+    """Nine draft tokens: the inputs are staged a few tokens at a time, and the
+    accepted prefixes end inside, at the end of, and past the first groups."""
+    rep = kda_inputs.make_replay(10, 9, 3, d, d, dtype, True, 0.05, 94, 8.0, 4.0)
+    rep.accepted[:] = torch.tensor([0, 1, 3, 4, 5, 7, 8, 9, 2, 6], dtype=torch.int32)
+    x = _replay_dev(rep)
+    yo, so = oracle.replay(rep)
+    # outputs and commit in one call
+    state = rep.S0.cuda()
+    y = kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                          accepted=rep.accepted.cuda(), z=x["z"])
+    torch.cuda.synchronize()
+    ey = rel_l2(y.cpu().double().numpy(), yo)
+    es = rel_l2(state.cpu().double().numpy(), so)
+    log(f"[parity] replay Td=9 {dtype} d{d}: y={ey:.3e} committed={es:.3e}")
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    # the commit alone gives the same states
+    state2 = rep.S0.cuda()
+    kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state2,
+                      accepted=rep.accepted.cuda(), z=x["z"], want_y=False)
+    torch.cuda.synchronize()
+    assert rel_l2(state2.cpu().double().numpy(), so) <= TOL[dtype]
+    assert torch.equal(state2[0].cpu(), rep.S0[0])
+
+
 def test_replay_full_acceptance_equals_decode_steps(kda):
     """Accepting every draft token = Td calls of kda_decode_step (same kernels'
     arithmetic per token, so the results agree to rounding)."""
