@@ -11,6 +11,9 @@ times, on outputs the oracle can compute one chain at a time.
   carried state matters): head 0's final state and the outputs of 3 segments.
 - Decode (128 requests x 96 heads, 1000 steps): every state and output after
   step 1, 32 sampled chains after step 10, 8 after step 1000.
+- Speculative replay (128 requests x 96 heads, 4 draft tokens, acceptance
+  uniform in [0, 4]): every draft output of the verify call and every state
+  after the commit call.
 """
 import sys
 
@@ -170,3 +173,21 @@ def test_decode_full_size(kda):
         ey, es = rel_l2(np.stack(ys), np.stack(yr)), rel_l2(np.stack(ss), np.stack(sr))
         log(f"[fullsize] decode step {steps} ({nchains} chains): y={ey:.3e} state={es:.3e}")
         assert ey <= BF16_TOL and es <= BF16_TOL
+
+
+def test_replay_full_size(kda):
+    rep = kda_inputs.make_replay(128, 4, 96, 128, 128, "bf16", True, 0.02, 95)
+    dev = torch.device("cuda")
+    x = {n: getattr(rep, n).to(dev) for n in ("q", "k", "v", "z", "g", "beta")}
+    state = rep.S0.to(dev)
+    y = kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state, z=x["z"])
+    kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                      accepted=rep.accepted.to(dev), z=x["z"], want_y=False)
+    torch.cuda.synchronize()
+    yo, so = oracle.replay(rep)
+    ey = rel_l2(y.cpu().double().numpy(), yo)
+    es = rel_l2(state.cpu().double().numpy(), so)
+    log(f"[fullsize] replay 128x96, 4 drafts: y={ey:.3e} committed={es:.3e}")
+    assert ey <= BF16_TOL and es <= BF16_TOL
+    untouched = (rep.accepted == 0).nonzero().flatten()
+    assert torch.equal(state[untouched].cpu(), rep.S0[untouched])
