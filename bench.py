@@ -77,11 +77,12 @@ def counter_traffic(kernel: str):
     return rec["traffic_bytes"] if h.hexdigest() == rec["src_sha256"] else None
 
 
-def time_steps(fn, steps: int, warmup: int, torch, warm_ms: float = 0.0):
+def time_steps(fn, steps: int, warmup: int, torch, warm_ms: float = 0.0, per_call: bool = False):
     """Average ms per call of fn over `steps` calls, HIP events on the current stream.
     Untimed first: `warmup` calls, then (warm_ms > 0) more calls until about
     warm_ms of GPU time has run, so that the clocks have settled (a cold GPU
-    runs the K3 layer ~10 % slower for the first few dozen calls)."""
+    runs the K3 layer ~10 % slower for the first few dozen calls).  per_call:
+    also the time of each call (events between the calls), as a third value."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -96,13 +97,43 @@ def time_steps(fn, steps: int, warmup: int, torch, warm_ms: float = 0.0):
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)] if per_call else []
     start.record()
-    for _ in range(steps):
+    for i in range(steps):
         fn()
+        if per_call and i < steps - 1:
+            marks[i].record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / steps, wall
+    ms = start.elapsed_time(end) / steps
+    if per_call:
+        ev = [start] + marks + [end]
+        return ms, wall, [a.elapsed_time(b) for a, b in zip(ev[:-1], ev[1:])]
+    return ms, wall
+
+
+def measured_peaks(torch, dev):
+    """Achievable peaks on this GPU through torch: a streaming read-and-write
+    pass over 2 GiB (an fp32 elementwise multiply into a second buffer, the
+    fastest of torch's copy, multiply and fill here: ~6.2 TB/s read + write,
+    against ~5.3 for copy_), and a bf16 GEMM of 8192^3 (hipBLASLt); best of 5."""
+    n = 2 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    _, _, t_copy = time_steps(lambda: torch.mul(src, 2.0, out=dst), 5, 2, torch, per_call=True)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    b = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    c = torch.empty(m, m, dtype=torch.bfloat16, device=dev)
+    _, _, t_mm = time_steps(lambda: torch.matmul(a, b, out=c), 5, 3, torch, per_call=True)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_stream_gbs": 2 * n / (min(t_copy) * 1e-3) / 1e9,
+            "bf16_gemm_tflops": 2 * m ** 3 / (min(t_mm) * 1e-3) / 1e12,
+            "how": "fp32 x 2.0 over 2 GiB into a second buffer (read + write bytes) and "
+                   "torch.matmul bf16 8192^3 (hipBLASLt), best of 5 each"}
 
 
 def gpu_inputs(torch, lens, H, dk, dv, gated, s0_std, seed, dev):
@@ -129,12 +160,15 @@ def bench_headline(args, torch, kda, kda_inputs, dev):
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C, y=y,
                       final_state=fs, workspace=ws)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, torch)
-    log(f"headline: {ms:.4f} ms per step ({args.steps} steps, wall {wall:.3f} s)")
+    ms, wall, calls = time_steps(step, args.steps, args.warmup, torch, per_call=True)
+    calls = sorted(calls)
+    log(f"headline: {ms:.4f} ms per step ({args.steps} steps, wall {wall:.3f} s; "
+        f"median {calls[len(calls) // 2]:.4f}, min {calls[0]:.4f})")
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True)
     flops = prefill_flops(T, H, dk, dv, C)
-    res = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), bytes=nbytes, flops=flops,
-               gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12)
+    res = dict(ms=ms, ms_median=calls[len(calls) // 2], ms_min=calls[0], tokens_per_s=T / (ms * 1e-3),
+               bytes=nbytes, flops=flops, gbs=nbytes / (ms * 1e-3) / 1e9,
+               tflops=flops / (ms * 1e-3) / 1e12)
     return inp, res, (y, fs)
 
 
@@ -157,13 +191,18 @@ def bench_cpu_baseline(args, inp, gpu_out, torch):
             break
     wall = total / reps
     log(f"cpu baseline: {reps} runs, {wall:.2f} s each")
+    t1 = time.perf_counter()
+    oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, z=inp.z,
+                      chains=[(0, heads[0])], nthreads=1)
+    one = time.perf_counter() - t1
     y, fs = gpu_out
     yg = y.cpu().double().numpy()[:, heads]
     sg = fs.cpu().double().numpy()[0, heads]
     ey = oracle.rel_l2(yg, yo[:, heads])
     es = oracle.rel_l2(sg, so)
     cpu = {"value": T / (wall * H / len(heads)), "unit": "tokens/s", "cores": threads,
-           "kind": "oracle",
+           "kind": "oracle", "chains_per_s": len(heads) / wall,
+           "single_thread_tokens_per_s": T / (one * H),
            "sample": (f"{len(heads)} of {H} heads of k3_layer_prefill (T={T}, full chains), fp64 "
                       f"sequential recurrence in C, run {reps} times ({total:.1f} s wall, "
                       f"{wall:.2f} s per run); value scaled to all {H} heads")}
@@ -406,12 +445,13 @@ def bench_decode_fused(args, torch, kda, kda_inputs, dev):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads (%s), 'all' or 'none'" % ",".join(ALL_WORKLOADS))
     ap.add_argument("--cpu-sample-heads", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time over which the CPU oracle sample is repeated")
     ap.add_argument("--decode-steps", type=int, default=1000,
@@ -442,6 +482,9 @@ def main() -> int:
         return 0
 
     inp, head, gpu_out = bench_headline(args, torch, kda, kda_inputs, dev)
+    peaks = measured_peaks(torch, dev) if not args.no_measured_peaks else None
+    if peaks:
+        log(f"measured peaks: {json.dumps(peaks)}")
     extras = ALL_WORKLOADS if args.workloads == "all" else tuple(
         x for x in args.workloads.split(",") if x and x != "none")
     workloads = {}
@@ -476,10 +519,16 @@ def main() -> int:
                      "traffic": counter_traffic("prefill"),
                      "kernel": ("kda_chunk_fwd = chunk_prep_kernel + chunk_state_kernel "
                                 "(bf16, dk=dv=128, chunk 64); time of the whole call"),
-                     "bytes_per_launch": head["bytes"]},
+                     "bytes_per_launch": head["bytes"],
+                     "frac_of_measured": head["gbs"] / peaks["hbm_stream_gbs"] if peaks else None},
         "mfma": {"achieved": head["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": head["tflops"] / BF16_MFMA_PEAK_TFLOPS,
-                 "flops_per_launch": head["flops"]},
+                 "flops_per_launch": head["flops"],
+                 "frac_of_measured": head["tflops"] / peaks["bf16_gemm_tflops"] if peaks else None},
+        "attainable_frac": max(head["gbs"] / HBM_PEAK_GBS, head["tflops"] / BF16_MFMA_PEAK_TFLOPS),
+        "ms_median": head["ms_median"],
+        "ms_min": head["ms_min"],
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "workloads": workloads,
