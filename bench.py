@@ -210,6 +210,27 @@ def bench_cpu_baseline(args, inp, gpu_out, torch):
     return cpu, parity
 
 
+def bench_cpu_kcp(args):
+    """The oracle's KCP-structured form (segment pairs, composition, outputs;
+    OpenMP over segments and heads) on a bounded slice of the 1M-token KCP
+    workload: its first 16 segments of 4096 tokens (the workload's segment
+    length), all 4 heads."""
+    import oracle
+    import kda_inputs
+    nseg, seg = 16, 4096
+    inp = kda_inputs.make_workload(3, lens=[nseg * seg])
+    threads = oracle.default_threads()
+    bounds = [i * seg for i in range(nseg + 1)]
+    t0 = time.perf_counter()
+    oracle.kcp(inp.q, inp.k, inp.v, inp.g, inp.beta, bounds, z=inp.z, nthreads=threads)
+    wall = time.perf_counter() - t0
+    log(f"cpu kcp: {nseg} segments x {seg} tokens, H={inp.H}: {wall:.2f} s on {threads} threads")
+    return {"value": nseg * seg / wall, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle, KCP-structured",
+            "sample": (f"first {nseg} of the 256 segments ({seg} tokens each) of kcp_long_sequence, "
+                       f"all {inp.H} heads, fp64, one run ({wall:.2f} s wall)")}
+
+
 def bench_varlen(args, torch, kda, kda_inputs, dev):
     w = kda_inputs.WORKLOADS[2]
     lens = kda_inputs.varlen_lengths()
@@ -498,6 +519,8 @@ def main() -> int:
     cpu, parity = (None, None)
     if not args.no_cpu_baseline:
         cpu, parity = bench_cpu_baseline(args, inp, gpu_out, torch)
+        if "kcp_long_sequence" in workloads:
+            workloads["kcp_long_sequence"]["cpu_baseline"] = bench_cpu_kcp(args)
 
     line = {
         "metric": METRIC,
