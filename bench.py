@@ -136,6 +136,12 @@ def measured_peaks(torch, dev):
                    "torch.matmul bf16 8192^3 (hipBLASLt), best of 5 each"}
 
 
+def device_info(torch, dev):
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+
+
 def gpu_inputs(torch, lens, H, dk, dv, gated, s0_std, seed, dev):
     """The synthetic recipe drawn on the GPU (kda_inputs.draw_on_device)."""
     import kda_inputs
@@ -552,6 +558,7 @@ def main() -> int:
         "ms_median": head["ms_median"],
         "ms_min": head["ms_min"],
         "measured_peaks": peaks,
+        "device": device_info(torch, dev),
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "workloads": workloads,
