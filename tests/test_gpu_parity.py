@@ -95,6 +95,28 @@ def test_decode_ungated_and_scaled(kda):
 
 
 # ---------------------------------------------------------------- prefill
+@pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-4), ("bf16", 128, 2e-2)])
+def test_decode_steps_equal_prefill(kda, dtype, d, tol):
+    """T decode steps of one request equal one prefill over the same T tokens
+    (two different kernels: the one-pass step and the two-pass chunked form),
+    with the tokens laid out [T, H, d] for the prefill and [1, H, d] per step."""
+    T, H = 70, 3
+    inp = kda_inputs.make_prefill([T], H, d, d, dtype, True, 0.05, 81, 8.0, 4.0)
+    y_p, s_p = run_prefill(kda, inp, chunk=64, scale=0.8)
+    state = inp.S0.clone().cuda()
+    ys = []
+    for t in range(T):
+        sl = slice(t, t + 1)
+        ys.append(kda.decode_step(inp.q[sl].cuda(), inp.k[sl].cuda(), inp.v[sl].cuda(),
+                                  inp.g[sl].cuda(), inp.beta[sl].cuda(), state,
+                                  z=inp.z[sl].cuda(), scale=0.8).cpu())
+    torch.cuda.synchronize()
+    ey = rel_l2(torch.cat(ys).double().numpy(), y_p.double().numpy())
+    es = rel_l2(state.cpu().double().numpy(), s_p.double().numpy())
+    log(f"[parity] decode x{T} vs prefill {dtype} d{d}: y={ey:.3e} state={es:.3e}")
+    assert ey <= tol and es <= tol
+
+
 def test_prefill_tiny_fp32_workload(kda):
     """B=1, H=2, T=256, dk=dv=64, chunk 16, fp32, ungated, S0 = 0."""
     inp = kda_inputs.make_workload(0)
