@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float scale, int H, const T
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
     __shared__ float s_u[RG][DV + 4], s_w[RG][DV + 4];
-    __shared__ float s_delta[DV];
+    __shared__ __attribute__((aligned(16))) float s_delta[DV];   // read as float4
     __shared__ float s_kq, s_ik, s_iq;
 
     const int nh = decode_head(blockIdx.x, gridDim.x);
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     // pass that also writes the state back, as in the decode step).
     __shared__ float s_k[TG][DK], s_q[TG][DK], s_a[TG][DK], s_v[TG][DV], s_z[TG][DV], s_b[TG];
     __shared__ float s_u[2][RG][DV + 4], s_w[2][RG][DV + 4];
-    __shared__ float s_delta[2][DV];
+    __shared__ __attribute__((aligned(16))) float s_delta[2][DV];   // read as float4
     __shared__ float s_kq[2];
 
     // placement as in the decode step (the commit, which writes the state, 3 % faster)
