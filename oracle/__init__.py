@@ -364,3 +364,26 @@ def rel_l2(a, b) -> float:
     d = np.linalg.norm(a - b)
     nb = np.linalg.norm(b)
     return float(d / nb) if nb > 0 else float(d)
+
+
+def row_err(a, b) -> float:
+    """Worst row of the difference, relative to the reference's typical row:
+    max_r ||a_r - b_r||_2 / sqrt(mean_r ||b_r||_2^2) in fp64, rows along the
+    last axis (one (token, head) output vector, or one row of a state), b the
+    reference.  Measured against the root-mean-square row norm rather than each
+    row's own norm, so a row whose reference is near zero does not dominate,
+    while an error confined to a few rows (one token of every chunk, say) is
+    not averaged away as it is in rel_l2.  The absolute worst row norm when b
+    is all zero; 0.0 for empty arrays."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        raise ValueError(f"row_err: shapes differ {a.shape} vs {b.shape}")
+    if a.size == 0:
+        return 0.0
+    n = b.shape[-1] if b.ndim else 1
+    a = a.reshape(-1, n)
+    b = b.reshape(-1, n)
+    d = np.sqrt(((a - b) ** 2).sum(axis=1)).max()
+    typ = np.sqrt((b ** 2).sum(axis=1).mean())
+    return float(d / typ) if typ > 0 else float(d)
