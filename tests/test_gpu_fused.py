@@ -15,10 +15,10 @@ import torch
 import kda_inputs
 import oracle
 from oracle import rel_l2
+from tests import parity
+from tests.parity import TOL
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def log(msg):
@@ -47,12 +47,7 @@ def run_fused(kda, raw, chunk, scale=1.0):
 
 
 def check(name, y, fs, yo, so, tol):
-    ey = rel_l2(y.double().numpy(), yo)
-    es = rel_l2(fs.double().numpy().reshape(so.shape), so)
-    log(f"[parity] {name}: rel_l2 y={ey:.3e} state={es:.3e} (tol {tol:g})")
-    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(fs).all()), f"{name}: non-finite"
-    assert ey <= tol, f"{name}: y rel-L2 {ey:.3e} > {tol:g}"
-    assert es <= tol, f"{name}: state rel-L2 {es:.3e} > {tol:g}"
+    parity.check(name, "f32" if tol <= TOL["f32"] else "bf16", y=(y, yo), state=(fs, so))
 
 
 @pytest.mark.parametrize("dtype,d,chunk,stress", [

@@ -15,10 +15,10 @@ import torch
 import kda_inputs
 import oracle
 from oracle import rel_l2
+from tests import parity
+from tests.parity import TOL
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def log(msg):
@@ -53,14 +53,11 @@ def oracle_prefill(inp, scale=1.0):
 
 
 def assert_parity(name, inp, y, fs, yo, so, tol):
-    ey = rel_l2(y.double().numpy(), yo)
-    es = rel_l2(fs.double().numpy().reshape(so.shape), so)
-    log(f"[parity] {name}: rel_l2 y={ey:.3e} state={es:.3e} (tol {tol:g})")
-    finite = bool(torch.isfinite(y).all()) and bool(torch.isfinite(fs).all())
-    assert finite, f"{name}: non-finite output"
-    assert ey <= tol, f"{name}: y rel-L2 {ey:.3e} > {tol:g}"
-    assert es <= tol, f"{name}: state rel-L2 {es:.3e} > {tol:g}"
-    return ey, es
+    """Whole-tensor rel-L2 <= tol (the dtype's tolerance) and every (token,
+    head) row and state row within the dtype's row bound (tests/parity.py)."""
+    dt = "f32" if tol <= TOL["f32"] else "bf16"
+    out = parity.check(name, dt, y=(y, yo), state=(fs, so))
+    return out["y"][0], out["state"][0]
 
 
 # ---------------------------------------------------------------- decode
@@ -76,10 +73,7 @@ def test_decode_matches_oracle(kda, dtype, d):
                             dec.beta[p].cuda(), state, z=dec.z[p].cuda())
     torch.cuda.synchronize()
     yo, _, so = oracle.decode_steps(dec, steps)
-    ey = rel_l2(y.cpu().double().numpy(), yo)
-    es = rel_l2(state.cpu().double().numpy().reshape(so.shape), so)
-    log(f"[parity] decode {dtype} d={d}: y={ey:.3e} state={es:.3e}")
-    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    parity.check(f"decode {dtype} d={d}", dtype, y=(y, yo), state=(state, so))
 
 
 def test_decode_ungated_and_scaled(kda):
@@ -310,10 +304,7 @@ def test_replay_verify_then_commit(kda, dtype, d):
                       accepted=rep.accepted.cuda(), z=x["z"], scale=0.5, want_y=False)
     torch.cuda.synchronize()
     yo, so = oracle.replay(rep, scale=0.5)
-    ey = rel_l2(y.cpu().double().numpy(), yo)
-    es = rel_l2(state.cpu().double().numpy(), so)
-    log(f"[parity] replay {dtype} d{d}: y={ey:.3e} committed={es:.3e}")
-    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    parity.check(f"replay {dtype} d{d}", dtype, y=(y, yo), committed=(state, so))
     # nothing accepted: bit-identical state
     assert torch.equal(state[0].cpu(), rep.S0[0])
 
@@ -326,8 +317,7 @@ def test_replay_outputs_and_commit_in_one_call(kda):
                           accepted=rep.accepted.cuda(), z=x["z"])
     torch.cuda.synchronize()
     yo, so = oracle.replay(rep)
-    assert rel_l2(y.cpu().double().numpy(), yo) <= TOL["bf16"]
-    assert rel_l2(state.cpu().double().numpy(), so) <= TOL["bf16"]
+    parity.check("replay outputs and commit", "bf16", y=(y, yo), committed=(state, so))
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
@@ -343,10 +333,7 @@ def test_replay_long_drafts_across_input_groups(kda, dtype, d):
     y = kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
                           accepted=rep.accepted.cuda(), z=x["z"])
     torch.cuda.synchronize()
-    ey = rel_l2(y.cpu().double().numpy(), yo)
-    es = rel_l2(state.cpu().double().numpy(), so)
-    log(f"[parity] replay Td=9 {dtype} d{d}: y={ey:.3e} committed={es:.3e}")
-    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    parity.check(f"replay Td=9 {dtype} d{d}", dtype, y=(y, yo), committed=(state, so))
     # the commit alone gives the same states
     state2 = rep.S0.cuda()
     kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state2,
@@ -390,9 +377,7 @@ def test_prefill_checkpoints_match_oracle(kda, chunk, interval):
                                 S_init=inp.S0)
     assert offs.cpu().tolist() == oo.tolist()      # integer offsets: exact
     n = int(oo[-1])
-    e = rel_l2(ck[:n].cpu().double().numpy(), co)
-    log(f"[parity] checkpoints c{chunk} every {interval}: {n} states, rel_l2={e:.3e}")
-    assert e <= TOL["bf16"]
+    parity.check(f"checkpoints c{chunk} every {interval} ({n} states)", "bf16", checkpoints=(ck[:n], co))
     yo, so = oracle_prefill(inp)
     assert_parity(f"checkpointed prefill c{chunk}", inp, y.cpu(), fs.cpu(), yo, so, TOL["bf16"])
 
@@ -406,9 +391,7 @@ def test_prefill_checkpoints_single_sequence_fp32(kda):
     co, oo = oracle.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, 32,
                                 S_init=inp.S0)
     assert offs.cpu().tolist() == oo.tolist() == [0, 8]
-    e = rel_l2(ck.cpu().double().numpy(), co)
-    log(f"[parity] checkpoints fp32 single sequence: rel_l2={e:.3e}")
-    assert e <= TOL["f32"]
+    parity.check("checkpoints fp32 single sequence", "f32", checkpoints=(ck, co))
 
 
 # ---------------------------------------------------------------- KCP
