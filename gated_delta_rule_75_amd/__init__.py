@@ -17,8 +17,9 @@ import torch
 
 __all__ = [
     "KDAError", "lib", "library_path", "kda_version", "kda_status_string",
-    "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_checkpointed", "kcp_scan",
-    "kcp_workspace_size", "decode_step", "decode_replay",
+    "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_workspace_min", "chunk_fwd_checkpointed",
+    "chunk_fwd_fused", "kcp_scan", "kcp_workspace_size", "kcp_workspace_min", "decode_step",
+    "decode_step_fused", "decode_replay",
     "KDA_BF16", "KDA_F32",
 ]
 
@@ -31,8 +32,9 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 
 # Every symbol include/kda.h declares.
-SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
-           "kda_chunk_fwd_checkpointed", "kda_kcp_workspace_size", "kda_kcp_scan",
+SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size",
+           "kda_chunk_fwd_workspace_min", "kda_chunk_fwd", "kda_chunk_fwd_checkpointed",
+           "kda_kcp_workspace_size", "kda_kcp_workspace_min", "kda_kcp_scan",
            "kda_decode_step", "kda_decode_replay", "kda_chunk_fwd_fused", "kda_decode_step_fused")
 
 
@@ -62,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i64]
     L.kda_chunk_fwd_workspace_size.restype = sz
+    L.kda_chunk_fwd_workspace_min.argtypes = [i, i, i, i, i, i, i64]
+    L.kda_chunk_fwd_workspace_min.restype = sz
     L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
@@ -72,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd_checkpointed.restype = i
     L.kda_kcp_workspace_size.argtypes = [i, i, i, i, i, i64, i]
     L.kda_kcp_workspace_size.restype = sz
+    L.kda_kcp_workspace_min.argtypes = [i, i, i, i, i, i64, i]
+    L.kda_kcp_workspace_min.restype = sz
     L.kda_kcp_scan.argtypes = [i, i, i, i, i, f, i64, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                sz, vp]
     L.kda_kcp_scan.restype = i
@@ -126,6 +132,29 @@ def _dev(*ts):
     return dev
 
 
+def _need(name: str, t, shape, dtype) -> None:
+    """A tensor the caller supplies must have exactly this shape and dtype.
+    Checked before any device or contiguity check, so a wrong buffer is
+    refused on the host whatever it holds."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def _need_workspace(ws) -> None:
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
+
+
 def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -152,53 +181,78 @@ def _check_inputs(q, k, v, g, beta, z, fused: bool = False):
 
 def chunk_fwd_workspace_size(dtype: int, H: int, dk: int, dv: int, chunk: int, num_seqs: int,
                              T_total: int) -> int:
+    """Bytes of workspace with which a prefill runs in one pass (the fastest)."""
     return int(lib().kda_chunk_fwd_workspace_size(dtype, H, dk, dv, chunk, num_seqs, T_total))
+
+
+def chunk_fwd_workspace_min(dtype: int, H: int, dk: int, dv: int, chunk: int, num_seqs: int,
+                            T_total: int) -> int:
+    """The smallest workspace a prefill accepts (time slabs of one chunk)."""
+    return int(lib().kda_chunk_fwd_workspace_min(dtype, H, dk, dv, chunk, num_seqs, T_total))
+
+
+def _workspace_bytes(full: int, least: int, limit: Optional[int]) -> int:
+    """The workspace to allocate: the full size, or at most `limit` bytes."""
+    if full == 0 or least == 0:
+        raise KDAError("workspace size query", 2)
+    if limit is None or limit >= full:
+        return full
+    if limit < least:
+        raise ValueError(f"max_workspace_bytes={limit} is below the minimum {least}")
+    return int(limit)
 
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=None,
               initial_state=None, output_final_state: bool = True, chunk: int = 64,
               scale: float = 1.0, y: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None,
+              max_workspace_bytes: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Prefill over packed sequences; returns (y, final_state or None).  The
-    workspace (uint8 device tensor) is allocated when not given."""
+    workspace (1-D uint8 device tensor) is allocated when not given: the full
+    size, or at most max_workspace_bytes (time slabs; at least
+    chunk_fwd_workspace_min bytes)."""
     return _chunk_fwd(False, q, k, v, g, beta, cu_seqlens, z, initial_state, output_final_state,
-                      chunk, scale, y, final_state, workspace)
+                      chunk, scale, y, final_state, workspace, max_workspace_bytes)
 
 
 def chunk_fwd_fused(q, k, v, a, b, cu_seqlens: Optional[torch.Tensor] = None, z=None,
                     initial_state=None, output_final_state: bool = True, chunk: int = 64,
                     scale: float = 1.0, y: Optional[torch.Tensor] = None,
                     final_state: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None,
+                    max_workspace_bytes: Optional[int] = None):
     """chunk_fwd on raw inputs: q, k unnormalised, a [T, H, dk] and b [T, H] the
     decay and beta pre-activations in q's dtype (g = -5 sigmoid(a), beta =
     sigmoid(b), unit q and k formed in the kernel)."""
     return _chunk_fwd(True, q, k, v, a, b, cu_seqlens, z, initial_state, output_final_state,
-                      chunk, scale, y, final_state, workspace)
+                      chunk, scale, y, final_state, workspace, max_workspace_bytes)
 
 
 def _chunk_fwd(fused, q, k, v, g, beta, cu_seqlens, z, initial_state, output_final_state, chunk,
-               scale, y, final_state, workspace):
+               scale, y, final_state, workspace, max_workspace_bytes=None):
     dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z, fused)
-    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state, workspace)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with at least two offsets")
         N = cu_seqlens.numel() - 1
     else:
         N = 1
+    _need("y", y, (T, H, dv), q.dtype)
+    _need("initial_state", initial_state, (N, H, dk, dv), torch.float32)
+    _need("final_state", final_state, (N, H, dk, dv), torch.float32)
+    _need_workspace(workspace)
+    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state, workspace)
     if y is None:
         y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
     if final_state is None and output_final_state:
         final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
-    for name, s in (("initial_state", initial_state), ("final_state", final_state)):
-        if s is not None and (s.dtype != torch.float32 or s.shape != (N, H, dk, dv)):
-            raise ValueError(f"{name} must be float32 [{N}, {H}, {dk}, {dv}]")
     if workspace is None:
-        need = chunk_fwd_workspace_size(dt, H, dk, dv, chunk, N, T)
-        if need == 0:
-            raise KDAError("kda_chunk_fwd_workspace_size", 2)
+        need = _workspace_bytes(chunk_fwd_workspace_size(dt, H, dk, dv, chunk, N, T),
+                                chunk_fwd_workspace_min(dt, H, dk, dv, chunk, N, T),
+                                max_workspace_bytes)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     fn = "kda_chunk_fwd_fused" if fused else "kda_chunk_fwd"
     st = getattr(lib(), fn)(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens), _ptr(q),
@@ -210,23 +264,26 @@ def _chunk_fwd(fused, q, k, v, g, beta, cu_seqlens, z, initial_state, output_fin
 
 
 def chunk_fwd_checkpointed(q, k, v, g, beta, interval: int, cu_seqlens=None, z=None,
-                           initial_state=None, chunk: int = 64, scale: float = 1.0):
+                           initial_state=None, chunk: int = 64, scale: float = 1.0,
+                           max_workspace_bytes: Optional[int] = None):
     """Prefill that also saves the state every `interval` tokens of each sequence.
     Returns (y, final_state, checkpoints [T // interval, H, dk, dv] (rows past
     offsets[-1] unused), offsets int32 [N + 1] (device))."""
     dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
-    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state)
     N = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    if interval <= 0 or interval % chunk != 0:
+        raise ValueError("interval must be a positive multiple of the chunk")
+    _need("initial_state", initial_state, (N, H, dk, dv), torch.float32)
+    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state)
     y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
     fs = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
     cap = max(T // interval, 1)
     ck = torch.empty(cap, H, dk, dv, dtype=torch.float32, device=dev)
     offs = torch.empty(N + 1, dtype=torch.int32, device=dev)
-    need = chunk_fwd_workspace_size(dt, H, dk, dv, chunk, N, T)
-    if need == 0:
-        raise KDAError("kda_chunk_fwd_workspace_size", 2)
+    need = _workspace_bytes(chunk_fwd_workspace_size(dt, H, dk, dv, chunk, N, T),
+                            chunk_fwd_workspace_min(dt, H, dk, dv, chunk, N, T), max_workspace_bytes)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib().kda_chunk_fwd_checkpointed(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens),
                                           _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
@@ -238,19 +295,36 @@ def chunk_fwd_checkpointed(q, k, v, g, beta, interval: int, cu_seqlens=None, z=N
 
 def kcp_workspace_size(dtype: int, H: int, dk: int, dv: int, chunk: int, T: int,
                        num_segments: int) -> int:
+    """Bytes of workspace with which a KCP scan forms its chunk products once."""
     return int(lib().kda_kcp_workspace_size(dtype, H, dk, dv, chunk, T, num_segments))
+
+
+def kcp_workspace_min(dtype: int, H: int, dk: int, dv: int, chunk: int, T: int,
+                      num_segments: int) -> int:
+    """The smallest workspace a KCP scan accepts (pairs and entering states plus
+    one chunk per head)."""
+    return int(lib().kda_kcp_workspace_min(dtype, H, dk, dv, chunk, T, num_segments))
 
 
 def kcp_scan(q, k, v, g, beta, num_segments: int, z=None, initial_state=None, chunk: int = 64,
              scale: float = 1.0, workspace: Optional[torch.Tensor] = None,
-             y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None):
-    """One long sequence split into segments composed by a prefix scan; returns (y, final_state)."""
+             y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+             max_workspace_bytes: Optional[int] = None):
+    """One long sequence split into segments composed by a prefix scan; returns
+    (y, final_state).  The workspace is allocated when not given: the full
+    size, or at most max_workspace_bytes."""
     dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    if not 1 <= num_segments <= max(T, 1):
+        raise ValueError("num_segments must lie in [1, T]")
+    _need("y", y, (T, H, dv), q.dtype)
+    _need("initial_state", initial_state, (1, H, dk, dv), torch.float32)
+    _need("final_state", final_state, (1, H, dk, dv), torch.float32)
+    _need_workspace(workspace)
     dev = _dev(q, k, v, g, beta, z, initial_state, workspace, y, final_state)
-    need = kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments)
-    if need == 0:
-        raise KDAError("kda_kcp_workspace_size", 2)
     if workspace is None:
+        need = _workspace_bytes(kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments),
+                                kcp_workspace_min(dt, H, dk, dv, chunk, T, num_segments),
+                                max_workspace_bytes)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if y is None:
         y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
@@ -280,9 +354,11 @@ def decode_step_fused(q, k, v, a, b, state, z=None, scale: float = 1.0,
 
 def _decode_step(fused, q, k, v, g, beta, state, z, scale, y):
     dt, N, H, dk, dv = _check_inputs(q, k, v, g, beta, z, fused)
+    if state is None:
+        raise ValueError("state is required")
+    _need("state", state, (N, H, dk, dv), torch.float32)
+    _need("y", y, (N, H, dv), q.dtype)
     dev = _dev(q, k, v, g, beta, z, state, y)
-    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
-        raise ValueError("state must be float32 [N, H, dk, dv]")
     if y is None:
         y = torch.empty(N, H, dv, dtype=q.dtype, device=dev)
     fn = "kda_decode_step_fused" if fused else "kda_decode_step"
@@ -309,10 +385,13 @@ def decode_replay(q, k, v, g, beta, state, accepted=None, z=None, scale: float =
         raise ValueError("replay inputs must be [N, Td, H, d] (beta [N, Td, H])")
     if g.dtype != torch.float32 or beta.dtype != torch.float32:
         raise TypeError("g and beta must be float32")
-    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
-        raise ValueError("state must be float32 [N, H, dk, dv]")
-    if accepted is not None and (accepted.dtype != torch.int32 or accepted.shape != (N,)):
-        raise ValueError("accepted must be int32 [N]")
+    _need("state", state, (N, H, dk, dv), torch.float32)
+    _need("accepted", accepted, (N,), torch.int32)
+    _need("y", y, (N, Td, H, dv), q.dtype)
+    if not want_y and y is not None:
+        raise ValueError("y given with want_y=False")
+    if not want_y and accepted is None:
+        raise ValueError("a replay needs outputs (want_y) or accepted lengths")
     dev = _dev(q, k, v, g, beta, z, state, accepted, y)
     if want_y and y is None:
         y = torch.empty(N, Td, H, dv, dtype=q.dtype, device=dev)

@@ -59,8 +59,9 @@ def test_chunk_fwd_rejects_bad_arguments(L):
     assert _fwd(L, s0=ctypes.c_void_p((1 << 20) + 8)) == INVALID # states need 16-byte alignment
     assert _fwd(L, ws=None) == INVALID
     assert _fwd(L, ws=ctypes.c_void_p((1 << 20) + 128)) == INVALID  # workspace: 256 bytes
-    need = L.kda_chunk_fwd_workspace_size(BF16, 2, 128, 128, 64, 1, 64)
-    assert _fwd(L, wsb=need - 1) == WS_SMALL
+    least = L.kda_chunk_fwd_workspace_min(BF16, 2, 128, 128, 64, 1, 64)
+    assert 0 < least <= L.kda_chunk_fwd_workspace_size(BF16, 2, 128, 128, 64, 1, 64)
+    assert _fwd(L, wsb=least - 1) == WS_SMALL
 
 
 def test_chunk_fwd_checkpointed_rejects_bad_arguments(L):
@@ -139,6 +140,30 @@ def test_kcp_workspace_size(L):
     assert L.kda_kcp_workspace_size(BF16, H, dk, dv, C, T, 0) == 0
 
 
+def test_workspace_minimum_does_not_grow_with_T(L):
+    """The smallest workspaces hold one chunk per head beside what does not
+    depend on the length: the carried states (prefill) or the segment pairs and
+    entering states (KCP)."""
+    H, dk, dv, C = 96, 128, 128, 64
+    one = _chunk_block_bytes(2, dk, dv, C, C) * H
+    for N, T in ((1, 8192), (1, 1 << 20), (16, 89000)):
+        least = L.kda_chunk_fwd_workspace_min(BF16, H, dk, dv, C, N, T)
+        carry = N * H * dk * dv * 4
+        assert carry + one <= least <= carry + one + 8 * 256 + 8 * N
+        assert least < L.kda_chunk_fwd_workspace_size(BF16, H, dk, dv, C, N, T)
+    # a call whose full workspace is one chunk per head needs no carry
+    assert L.kda_chunk_fwd_workspace_min(BF16, 2, 64, 64, 64, 1, 10) == \
+        L.kda_chunk_fwd_workspace_size(BF16, 2, 64, 64, 64, 1, 10)
+    assert L.kda_chunk_fwd_workspace_min(BF16, 0, dk, dv, C, 1, 64) == 0
+    # KCP at one 1M-token sequence, 4 heads, 256 segments: about 201 MB + one chunk per head
+    S, T = 256, 1 << 20
+    fixed = S * 4 * dk * (dk + dv) * 4 + S * 4 * dk * dv * 4 + 16 * 4 * dk * (dk + dv) * 4 + 16 * 4 * dk * dv * 4
+    least = L.kda_kcp_workspace_min(BF16, 4, dk, dv, C, T, S)
+    assert fixed + 4 * _chunk_block_bytes(2, dk, dv, C, C) <= least <= fixed + 4 * _chunk_block_bytes(2, dk, dv, C, C) + 4096
+    assert least == L.kda_kcp_workspace_min(BF16, 4, dk, dv, C, 4 * T, S)
+    assert L.kda_kcp_workspace_min(BF16, 4, dk, dv, C, T, 0) == 0
+
+
 def _kcp(L, T=4096, S=4, ws=P, wsb=1 << 40, dk=128, chunk=64, dt=BF16, y=P):
     return L.kda_kcp_scan(dt, 2, dk, dk, chunk, 1.0, T, S, P, P, P, P, P, None, None, None, y,
                           ws, wsb, None)
@@ -152,8 +177,9 @@ def test_kcp_rejects_bad_arguments(L):
     assert _kcp(L, y=None) == INVALID
     assert _kcp(L, dk=96) == UNSUPPORTED
     assert _kcp(L, chunk=8) == UNSUPPORTED
-    need = L.kda_kcp_workspace_size(BF16, 2, 128, 128, 64, 4096, 4)
-    assert _kcp(L, wsb=need - 1) == WS_SMALL
+    least = L.kda_kcp_workspace_min(BF16, 2, 128, 128, 64, 4096, 4)
+    assert 0 < least < L.kda_kcp_workspace_size(BF16, 2, 128, 128, 64, 4096, 4)
+    assert _kcp(L, wsb=least - 1) == WS_SMALL
 
 
 def test_decode_rejects_bad_arguments(L):
@@ -220,3 +246,67 @@ def test_binding_checks_fused_dtypes():
     with pytest.raises(TypeError):    # a must have q's dtype, not fp32 g beside bf16 q
         kda._check_inputs(q.bfloat16(), q.bfloat16(), q.bfloat16(), q, torch.zeros(4, 1).bfloat16(),
                           None, fused=True)
+
+
+def _cpu_prefill(T=8, H=2, d=64, dt=None):
+    import torch
+    dt = dt or torch.bfloat16
+    q = torch.zeros(T, H, d, dtype=dt)
+    return dict(q=q, k=q.clone(), v=q.clone(), g=torch.zeros(T, H, d), beta=torch.zeros(T, H))
+
+
+@pytest.mark.parametrize("name,bad,exc", [
+    ("y", dict(shape=(8, 2, 32)), ValueError),                   # too few value channels
+    ("y", dict(shape=(7, 2, 64)), ValueError),                   # too few tokens
+    ("y", dict(dtype="f32"), TypeError),                         # fp32 y beside bf16 inputs
+    ("final_state", dict(shape=(1, 2, 64, 32)), ValueError),
+    ("final_state", dict(dtype="bf16", shape=(1, 2, 64, 64)), TypeError),
+    ("initial_state", dict(shape=(2, 2, 64, 64)), ValueError),   # one sequence, two states
+    ("workspace", dict(dtype="f32", shape=(1024,)), TypeError),
+    ("workspace", dict(shape=(4, 256)), TypeError),
+])
+def test_binding_refuses_wrong_buffers_for_chunk_fwd(name, bad, exc):
+    """Buffers the caller passes are checked for shape and dtype before the
+    call: an undersized y or state would be written out of bounds."""
+    import torch
+    x = _cpu_prefill()
+    dts = {"f32": torch.float32, "bf16": torch.bfloat16}
+    default = {"y": ((8, 2, 64), torch.bfloat16), "final_state": ((1, 2, 64, 64), torch.float32),
+               "initial_state": ((1, 2, 64, 64), torch.float32), "workspace": ((1024,), torch.uint8)}
+    shape, dtype = default[name]
+    t = torch.zeros(bad.get("shape", shape), dtype=dts.get(bad.get("dtype"), dtype))
+    with pytest.raises(exc):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], **{name: t})
+
+
+def test_binding_refuses_wrong_buffers_elsewhere():
+    import torch
+    x = _cpu_prefill()
+    with pytest.raises(ValueError):      # kcp states are [1, H, dk, dv]
+        kda.kcp_scan(x["q"], x["k"], x["v"], x["g"], x["beta"], 2,
+                     initial_state=torch.zeros(2, 64, 64))
+    with pytest.raises(ValueError):
+        kda.kcp_scan(x["q"], x["k"], x["v"], x["g"], x["beta"], 2, y=torch.zeros(8, 2, 63).bfloat16())
+    with pytest.raises(ValueError):      # more segments than tokens
+        kda.kcp_scan(x["q"], x["k"], x["v"], x["g"], x["beta"], 9)
+    with pytest.raises(ValueError):      # interval not a multiple of the chunk
+        kda.chunk_fwd_checkpointed(x["q"], x["k"], x["v"], x["g"], x["beta"], 48, chunk=32)
+    # decode: q [N, H, dk]
+    q = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    g, b = torch.zeros(3, 2, 64), torch.zeros(3, 2)
+    with pytest.raises(ValueError):
+        kda.decode_step(q, q, q, g, b, torch.zeros(3, 2, 64, 32))
+    with pytest.raises(TypeError):
+        kda.decode_step(q, q, q, g, b, torch.zeros(3, 2, 64, 64, dtype=torch.float64))
+    with pytest.raises(TypeError):
+        kda.decode_step(q, q, q, g, b, torch.zeros(3, 2, 64, 64), y=torch.zeros(3, 2, 64))
+    # replay: inputs [N, Td, H, d]
+    r = torch.zeros(3, 4, 2, 64, dtype=torch.bfloat16)
+    rg, rb = torch.zeros(3, 4, 2, 64), torch.zeros(3, 4, 2)
+    st = torch.zeros(3, 2, 64, 64)
+    with pytest.raises(ValueError):
+        kda.decode_replay(r, r, r, rg, rb, st, y=torch.zeros(3, 3, 2, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        kda.decode_replay(r, r, r, rg, rb, st, accepted=torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        kda.decode_replay(r, r, r, rg, rb, st, want_y=False)     # nothing to produce
