@@ -4,6 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "launch.h"
 
 namespace {
@@ -23,13 +27,15 @@ kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HI
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace of the two-pass prefill: sequence plan, then the per-(chunk, head)
-// product arrays, each 256-byte aligned.
+// Workspace of the two-pass prefill: sequence plan, the carry of the state
+// between time slabs (bounded workspaces only), then the per-(chunk, head)
+// product arrays of one slab of nchunks chunks, each part 256-byte aligned.
 struct Layout {
-    size_t chunk_off, order, wn, qt, kht, pm, ut, gam, total;
+    size_t chunk_off, order, carry, wn, qt, kht, pm, ut, gam, total;
 };
 
-Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs, int64_t nchunks) {
+Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs, int64_t nchunks,
+                      size_t carry_bytes = 0) {
     const kda::TwoPassDims d = kda::twopass_dims((int)dt, dk, dv, chunk);
     const size_t nb = (size_t)nchunks * H;
     Layout l;
@@ -37,6 +43,7 @@ Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_se
     auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes, 256); return at; };
     l.chunk_off = take((size_t)(num_seqs + 1) * 4);
     l.order = take((size_t)num_seqs * 4);
+    l.carry = take(carry_bytes);
     l.wn = take(nb * d.wn() * d.esz);
     l.qt = take(nb * d.qt() * d.esz);
     l.kht = take(nb * d.kht() * d.esz);
@@ -45,6 +52,19 @@ Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_se
     l.gam = take(nb * d.gam() * 4);
     l.total = o;
     return l;
+}
+
+// Chunks per slab that fit `bytes` with the given carry, at most `all` (0 when
+// not even one chunk fits).
+int64_t slab_chunks(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs, int64_t all,
+                    size_t carry_bytes, size_t bytes) {
+    const size_t fixed = twopass_layout(dt, H, dk, dv, chunk, num_seqs, 0, carry_bytes).total;
+    if (bytes <= fixed) return 0;
+    const size_t per = kda::twopass_dims((int)dt, dk, dv, chunk).block_bytes() * (size_t)H;
+    int64_t n = (int64_t)((bytes - fixed) / per);
+    if (n > all) n = all;
+    while (n > 0 && twopass_layout(dt, H, dk, dv, chunk, num_seqs, n, carry_bytes).total > bytes) --n;
+    return n;
 }
 
 kda::TwoPassBufs bufs_at(void* ws, const Layout& l) {
@@ -72,9 +92,6 @@ int64_t seg_chunks(int64_t seg_len, int chunk, int num_seqs) {
 // loader waves apply (all but the KCP pairs), which measured faster there.
 int pick_nvt(int64_t chains, int dvt) {
     if (dvt % 128 != 0) return 1;
-#ifdef KDA_SCAN_NVT
-    return KDA_SCAN_NVT;
-#endif
     return chains * (dvt / 128) >= 1024 ? 2 : 1;
 }
 
@@ -113,6 +130,15 @@ size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chu
     return twopass_layout(dt, H, dk, dv, chunk, num_seqs, varlen_chunks(T_total, chunk, num_seqs)).total;
 }
 
+size_t kda_chunk_fwd_workspace_min(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs,
+                                   int64_t T_total) {
+    const size_t full = kda_chunk_fwd_workspace_size(dt, H, dk, dv, chunk, num_seqs, T_total);
+    if (full == 0) return 0;
+    const size_t one = twopass_layout(dt, H, dk, dv, chunk, num_seqs, 1,
+                                      (size_t)num_seqs * H * dk * dv * sizeof(float)).total;
+    return one < full ? one : full;
+}
+
 }  // extern "C"
 
 namespace {
@@ -148,10 +174,19 @@ kda_status chunk_fwd_impl(kda_dtype dt, bool fused, int H, int dk, int dv, int c
         !aligned(y, ea) || !aligned(g, ga) || !aligned(beta, ba) || !aligned(cu_seqlens, 4) ||
         !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256))
         return KDA_ERR_INVALID_ARGUMENT;
+    // all chunks of the call (an upper bound with packed sequences), and the
+    // slab the workspace holds: all of them, or as many as fit beside a carry
     const int64_t nchunks = cu_seqlens ? varlen_chunks(T_total, chunk, num_seqs)
                                        : seg_chunks(T_total, chunk, num_seqs);
-    const Layout l = twopass_layout(dt, H, dk, dv, chunk, num_seqs, varlen_chunks(T_total, chunk, num_seqs));
-    if (workspace_bytes < l.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    const size_t carry_bytes = (size_t)num_seqs * H * dk * dv * sizeof(float);
+    Layout l = twopass_layout(dt, H, dk, dv, chunk, num_seqs, varlen_chunks(T_total, chunk, num_seqs));
+    int64_t slab = nchunks;
+    bool bounded = workspace_bytes < l.total;
+    if (bounded) {
+        slab = slab_chunks(dt, H, dk, dv, chunk, num_seqs, nchunks, carry_bytes, workspace_bytes);
+        if (slab <= 0) return KDA_ERR_WORKSPACE_TOO_SMALL;
+        l = twopass_layout(dt, H, dk, dv, chunk, num_seqs, slab, carry_bytes);
+    }
     kda::TwoPassArgs a{};
     a.dtype = (int)dt;
     a.H = H;
@@ -177,7 +212,8 @@ kda_status chunk_fwd_impl(kda_dtype dt, bool fused, int H, int dk, int dv, int c
     a.mode = cu_seqlens ? kda::kModeVarlen : kda::kModeSeq;
     a.nvt = pick_nvt((int64_t)num_seqs * H, dv);
     a.bufs = bufs_at(workspace, l);
-    a.chunk_cap = varlen_chunks(T_total, chunk, num_seqs);
+    a.chunk_cap = nchunks;
+    a.carry = bounded ? reinterpret_cast<float*>(static_cast<char*>(workspace) + l.carry) : nullptr;
     a.ckpt = ckpt ? checkpoints : nullptr;
     a.ckpt_off = ckpt ? ckpt_offsets : nullptr;
     a.ckpt_every = ckpt ? ckpt_interval / chunk : 1;
@@ -194,8 +230,16 @@ kda_status chunk_fwd_impl(kda_dtype dt, bool fused, int H, int dk, int dv, int c
                                     order, ckpt ? ckpt_offsets : nullptr, stream) != hipSuccess)
             return KDA_ERR_HIP;
     }
-    if (kda::launch_chunk_prep(a, chunk_off, nchunks) != hipSuccess) return KDA_ERR_HIP;
-    return from_hip(kda::launch_chunk_state(a, chunk_off, order));
+    // one slab after the other on the stream: its products, then every chain's
+    // chunks inside it (with no chunks, one empty slab still runs the chains)
+    for (int64_t lo = 0; lo < nchunks || lo == 0; lo += slab) {
+        a.slab_lo = lo;
+        a.slab_hi = lo + slab < nchunks ? lo + slab : nchunks;
+        if (kda::launch_chunk_prep(a, chunk_off, a.slab_hi - lo) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_chunk_state(a, chunk_off, order) != hipSuccess) return KDA_ERR_HIP;
+        if (slab <= 0) break;
+    }
+    return KDA_OK;
 }
 
 // kda_decode_step; fused: q, k raw and g, beta the pre-activations a, b in dtype dt.
@@ -282,6 +326,16 @@ size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, in
            twopass_layout(dt, H, dk, dv, chunk, num_segments, seg_chunks(seg_len, chunk, num_segments)).total;
 }
 
+size_t kda_kcp_workspace_min(kda_dtype dt, int H, int dk, int dv, int chunk, int64_t T,
+                             int num_segments) {
+    const size_t full = kda_kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments);
+    if (full == 0) return 0;
+    size_t pairs, starts, gpairs, gstarts;
+    kcp_parts(H, dk, dv, num_segments, &pairs, &starts, &gpairs, &gstarts);
+    const size_t one = pairs + starts + gpairs + gstarts + twopass_layout(dt, H, dk, dv, chunk, num_segments, 1).total;
+    return one < full ? one : full;
+}
+
 kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float scale, int64_t T,
                         int num_segments, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const void* z,
@@ -298,7 +352,7 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
         !aligned(y, ea) || !aligned(g, 16) || !aligned(beta, 4) || !aligned(workspace, 256) ||
         !aligned(initial_state, 16) || !aligned(final_state, 16))
         return KDA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < kda_kcp_workspace_size(dt, H, dk, dv, chunk, T, num_segments))
+    if (workspace_bytes < kda_kcp_workspace_min(dt, H, dk, dv, chunk, T, num_segments))
         return KDA_ERR_WORKSPACE_TOO_SMALL;
     size_t pbytes, sbytes, gpbytes, gsbytes;
     kcp_parts(H, dk, dv, num_segments, &pbytes, &sbytes, &gpbytes, &gsbytes);
@@ -306,11 +360,17 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     float* starts = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes);
     float* gpairs = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes + sbytes);
     float* gstarts = reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes + sbytes + gpbytes);
-    void* tp = static_cast<char*>(workspace) + pbytes + sbytes + gpbytes + gsbytes;
+    const size_t fixed = pbytes + sbytes + gpbytes + gsbytes;
+    void* tp = static_cast<char*>(workspace) + fixed;
     // segments hold seg_len tokens each; with T not a multiple, trailing ones may be empty
     const int64_t seg_len = (T + num_segments - 1) / num_segments;
     const int64_t nchunks = seg_chunks(seg_len, chunk, num_segments);
-    const Layout l = twopass_layout(dt, H, dk, dv, chunk, num_segments, nchunks);
+    // the chunk products of all segments at once, or slabs of consecutive
+    // chunks (formed twice then: for the pairs and for the outputs)
+    int64_t slab = slab_chunks(dt, H, dk, dv, chunk, num_segments, nchunks, 0, workspace_bytes - fixed);
+    if (slab <= 0) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    const bool bounded = slab < nchunks;
+    const Layout l = twopass_layout(dt, H, dk, dv, chunk, num_segments, slab);
     kda::TwoPassArgs a{};
     a.dtype = (int)dt;
     a.H = H;
@@ -331,30 +391,44 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.bufs = bufs_at(tp, l);
     a.chunk_cap = nchunks;
     a.stream = stream;
-    // the chunk products serve both passes over the segments
-    if (kda::launch_chunk_prep(a, nullptr, nchunks) != hipSuccess) return KDA_ERR_HIP;
     // phase 1: (M, Sloc) of every segment, as the state that the augmented value
-    // block [0 | v] builds from the augmented start [I | 0]
+    // block [0 | v] builds from the augmented start [I | 0]; between slabs the
+    // augmented state waits in the pairs array itself
     a.mode = kda::kModePairs;
     a.nvt = pick_nvt((int64_t)num_segments * H, dk + dv);
     a.initial_state = nullptr;
     a.final_state = pairs;
     a.final_seq_lo = 0;
+    a.carry = pairs;
     a.y = nullptr;
-    if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
+    for (int64_t lo = 0; lo < nchunks; lo += slab) {
+        a.slab_lo = lo;
+        a.slab_hi = lo + slab < nchunks ? lo + slab : nchunks;
+        if (kda::launch_chunk_prep(a, nullptr, a.slab_hi - lo) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
+    }
     // phase 2: entering state of every segment
     if (kda::launch_kcp_scan(H, dk, dv, num_segments, pairs, initial_state, starts, gpairs, gstarts,
                              (hipStream_t)stream) != hipSuccess)
         return KDA_ERR_HIP;
     // phase 3: outputs of every segment from its entering state; the last
-    // segment's final state is the sequence's final state
+    // segment's final state is the sequence's final state.  Between slabs a
+    // segment's state waits in its own entering-state slot.
     a.mode = kda::kModeFinish;
     a.nvt = pick_nvt((int64_t)num_segments * H, dv);
     a.initial_state = starts;
     a.final_state = final_state;
     a.final_seq_lo = num_segments - 1;
+    a.carry = starts;
     a.y = y;
-    return from_hip(kda::launch_chunk_state(a, nullptr, nullptr));
+    for (int64_t lo = 0; lo < nchunks; lo += slab) {
+        a.slab_lo = lo;
+        a.slab_hi = lo + slab < nchunks ? lo + slab : nchunks;
+        // with one slab the products of phase 1 are still in place
+        if (bounded && kda::launch_chunk_prep(a, nullptr, a.slab_hi - lo) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
 }
 
 kda_status kda_decode_step(kda_dtype dt, int N, int H, int dk, int dv, float scale,
@@ -409,6 +483,36 @@ kda_status kda_decode_replay(kda_dtype dt, int N, int Td, int H, int dk, int dv,
 }  // extern "C"
 
 namespace kda {
+
+hipError_t ensure_lds_limit(const void* kern, int bytes) {
+    static std::mutex mu;
+    static std::set<std::pair<int, const void*>> done;   // (device, kernel) already raised
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({dev, kern})) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert({dev, kern});
+    return e;
+}
+
+hipError_t device_cu_count(int* cus) {
+    constexpr int kMaxDev = 64;
+    static int cached[kMaxDev] = {};   // 0: not queried yet
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) {
+        *cus = cached[dev];
+        return hipSuccess;
+    }
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDev) cached[dev] = *cus;
+    return e;
+}
 
 bool prefill_supported(int dtype, int dk, int dv, int chunk) {
     if (!((dk == 64 && dv == 64) || (dk == 128 && dv == 128))) return false;

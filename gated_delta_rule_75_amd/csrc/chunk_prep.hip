@@ -48,6 +48,7 @@ namespace kda {
 
 struct PrepParams {
     int H, num_seqs, cps;   // cps: chunks per segment when cu_seqlens is NULL
+    int gc0;                // global chunk of workspace block 0 (the first chunk of the slab)
     float scale;
     int64_t T_total, seg_len;
     const int32_t* cu_seqlens;
@@ -167,7 +168,7 @@ void chunk_prep_kernel(PrepParams p) {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t wsb = blockIdx.x;  // (chunk, head) block of the workspace
     const int h = (int)(wsb % H);
-    const int gc = (int)(wsb / H);
+    const int gc = p.gc0 + (int)(wsb / H);   // global chunk index
 
     // ---- locate the chunk ----------------------------------------------------
     int64_t ts;
@@ -602,6 +603,7 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
     p.H = a.H;
     p.num_seqs = a.num_seqs;
     p.cps = (int)((a.seg_len + a.chunk - 1) / a.chunk);
+    p.gc0 = (int)a.slab_lo;
     p.scale = a.scale;
     p.T_total = a.T_total;
     p.seg_len = a.seg_len;
@@ -615,9 +617,7 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
     p.ws = a.bufs;
     auto kern = chunk_prep_kernel<C>;
     if (C::BYTES > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)C::BYTES);
+        const hipError_t e = ensure_lds_limit((const void*)kern, (int)C::BYTES);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::NTHR), C::BYTES, (hipStream_t)a.stream, p);
@@ -638,6 +638,7 @@ static hipError_t launch_prep_dk(const TwoPassArgs& a, const int32_t* co, int64_
 }
 
 hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks) {
+    // the slab's chunks [slab_lo, slab_lo + nchunks) into workspace blocks 0 ..
     const int64_t nb = nchunks * a.H;
     if (a.dtype == 0)
         return a.dk == 128 ? launch_prep_dk<BF16, 128>(a, chunk_off, nb) : launch_prep_dk<BF16, 64>(a, chunk_off, nb);

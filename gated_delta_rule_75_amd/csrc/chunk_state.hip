@@ -49,7 +49,10 @@ namespace kda {
 
 struct StateParams {
     int H, num_seqs, nchains, nvg, dvt, final_seq_lo, cps;
-    int chunk_cap;  // chunks the workspace holds
+    int chunk_cap;          // bound on the global chunk count
+    int slab_lo, slab_hi;   // global chunks whose products the workspace holds
+    int first_slab;         // chains without chunks run here
+    float* carry;           // state between slabs, [num_seqs, H, dk, dvt]
     int64_t T_total, seg_len;
     const int32_t* cu_seqlens;
     const int32_t* chunk_off;
@@ -161,12 +164,28 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         len = t1 - t0;
         cbase = n * p.cps;
     }
-    // stay inside T_total and the workspace whatever the offsets say
+    // stay inside T_total and the chunk bound whatever the offsets say
     if (t0 >= p.T_total) len = 0;
     else if (t0 + len > p.T_total) len = p.T_total - t0;
     int nch = len > 0 ? (int)((len + CH - 1) / CH) : 0;
     if (cbase + nch > p.chunk_cap) nch = cbase < p.chunk_cap ? p.chunk_cap - cbase : 0;
     const int dvt = p.dvt;
+    // the chain's chunks [cb, ce) inside this slab; the chain is then shifted so
+    // that its window starts at chunk 0 (tokens t0.., workspace block cws + c)
+    const int64_t len_chain = len;
+    int cb = 0, ce = nch;
+    if (p.slab_lo > cbase) cb = p.slab_lo - cbase < nch ? p.slab_lo - cbase : nch;
+    if (p.slab_hi < cbase + nch) ce = p.slab_hi > cbase ? p.slab_hi - cbase : 0;
+    if (ce <= cb) {
+        if (nch > 0 || !p.first_slab) return;   // nothing of this chain in the slab
+        cb = ce = 0;
+    }
+    const bool from_start = cb == 0, to_end = ce == nch;
+    t0 += (int64_t)cb * CH;
+    len = len - (int64_t)cb * CH < (int64_t)(ce - cb) * CH ? len - (int64_t)cb * CH : (int64_t)(ce - cb) * CH;
+    const int ck0 = cb;                      // chunks of the chain before the window
+    const int cws = cbase + cb - p.slab_lo;  // workspace block of the window's first chunk
+    nch = ce - cb;
     // first value tile (16 columns of v / U) of the workgroup; negative for
     // the transition columns of mode 2, whose waves take no values
     const int vt_wg = (vg * C::CW - (C::AUG ? DK : 0)) / 16;
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             constexpr int NU = C::NCOPY - C::NF;
             constexpr int NG1 = NU + C::N_W, NG2 = C::NCOPY - NG1;
             auto stage_group = [&](int c, int b, auto G) {
-                const int64_t wsb = (int64_t)(cbase + c) * H + h;
+                const int64_t wsb = (int64_t)(cws + c) * H + h;
                 char* buf = smem + b * C::BUF;
                 const char* aw = wn + wsb * (int64_t)(CH * DK * sizeof(T));
                 const char* aq = qt + wsb * (int64_t)(CH * DK * sizeof(T));
@@ -268,8 +287,11 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[ct][vt][i] = (C::AUG && col == 16 * ct + 4 * g4 + i) ? 1.f : 0.f;
         }
-    if (!C::AUG && p.s0) {
-        const float* s0 = p.s0 + ((int64_t)n * H + h) * DK * (int64_t)dvt;
+    // entering state: the initial state at the chain's first chunk (zeros, or
+    // [I | 0] for the pairs), the carry of the previous slab otherwise
+    const float* sinit = from_start ? (C::AUG ? nullptr : p.s0) : p.carry;
+    if (sinit) {
+        const float* s0 = sinit + ((int64_t)n * H + h) * DK * (int64_t)dvt;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -321,7 +343,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     }
     // fragments [J0, J1) of this wave's share of chunk c into LDS buffer b
     auto stage = [&](int c, int b, auto J0, auto J1) {
-        const int64_t wsb = (int64_t)(cbase + c) * H + h;
+        const int64_t wsb = (int64_t)(cws + c) * H + h;
         char* buf = smem + b * C::BUF;
 #pragma unroll
         for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
@@ -382,7 +404,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     // U^T and z of the wave's columns, one chunk ahead in registers
     T4 ut[NTT][NVT], zz[NTT][NVT];
     auto load_uz = [&](int c) {
-        const int64_t wsb = (int64_t)(cbase + c) * H + h;
+        const int64_t wsb = (int64_t)(cws + c) * H + h;
         const T* UT = static_cast<const T*>(p.ws.ut) + wsb * (DV * CH);
         if constexpr (!C::LW) {
 #pragma unroll
@@ -579,8 +601,8 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
         if constexpr (!C::AUG) {
             // prefix-cache checkpoint: the state after this chunk
-            if (ckpt && (c + 1) % ck_every == 0 && (int64_t)(c + 1) * CH <= len) {
-                const int64_t row = ck_base + (c + 1) / ck_every - 1;
+            if (ckpt && (ck0 + c + 1) % ck_every == 0 && (int64_t)(ck0 + c + 1) * CH <= len_chain) {
+                const int64_t row = ck_base + (ck0 + c + 1) / ck_every - 1;
                 if (row < ck_cap) {
                     // global address space: a generic store would also count on the
                     // LDS wait counter
@@ -680,16 +702,18 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
     }
 
-    // ---- final state ---------------------------------------------------------
-    if (p.sfin && n >= p.final_seq_lo) {
-        const int64_t sb = ((int64_t)(n - p.final_seq_lo) * H + h) * DK * (int64_t)dvt;
+    // ---- final state, or the carry to the next slab ----------------------------
+    float* sout = nullptr;
+    if (!to_end) sout = p.carry + ((int64_t)n * H + h) * DK * (int64_t)dvt;
+    else if (p.sfin && n >= p.final_seq_lo) sout = p.sfin + ((int64_t)(n - p.final_seq_lo) * H + h) * DK * (int64_t)dvt;
+    if (sout) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
                 const int col = colw + 16 * vt + l16;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p.sfin[sb + (int64_t)(16 * ct + 4 * g4 + i) * dvt + col] = S[ct][vt][i];
+                for (int i = 0; i < 4; ++i) sout[(int64_t)(16 * ct + 4 * g4 + i) * dvt + col] = S[ct][vt][i];
             }
     }
 }
@@ -760,6 +784,10 @@ template <class C>
 static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order) {
     StateParams p;
     p.chunk_cap = (int)a.chunk_cap;
+    p.slab_lo = (int)a.slab_lo;
+    p.slab_hi = (int)a.slab_hi;
+    p.first_slab = a.slab_lo == 0;
+    p.carry = a.carry;
     p.H = a.H;
     p.num_seqs = a.num_seqs;
     p.nchains = a.num_seqs * a.H;
@@ -784,8 +812,7 @@ static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_of
     if (p.nchains == 0) return hipSuccess;
     auto kern = chunk_state_kernel<C>;
     if (C::BYTES > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
+        const hipError_t e = ensure_lds_limit((const void*)kern, (int)C::BYTES);
         if (e != hipSuccess) return e;
     }
     const long nblk = (long)((p.nchains + 7) / 8) * 8 * p.nvg;

@@ -251,9 +251,8 @@ __global__ __launch_bounds__(256) void kcp_chain_wide_kernel(ChainParams p) {
 template <int DK>
 static hipError_t launch_chain_t(const ChainParams& p, int nchain, hipStream_t stream) {
     // narrow form while its workgroups fit in one round at two per CU
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
     const int64_t narrow_wgs = (int64_t)nchain * p.H * (p.ncol / 16);
     if (narrow_wgs <= 2 * (int64_t)cus) {
@@ -262,7 +261,7 @@ static hipError_t launch_chain_t(const ChainParams& p, int nchain, hipStream_t s
     }
     constexpr int MBUF = (DK / (1024 / (DK * 4))) * (1024 + 16);
     auto kern = kcp_chain_wide_kernel<DK>;
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * MBUF);
+    e = ensure_lds_limit((const void*)kern, 2 * MBUF);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(nchain, p.H, p.ncol / 64), dim3(256), 2 * MBUF, stream, p);
     return hipGetLastError();

@@ -50,7 +50,15 @@ struct TwoPassArgs {
     int mode;                    // ScanMode
     int nvt;                     // 16-column value tiles per scan wave (1 or 2)
     TwoPassBufs bufs;            // chunk products (workspace)
-    int64_t chunk_cap;           // chunks the workspace arrays hold
+    int64_t chunk_cap;           // bound on the global chunk count of the call
+    // Time slab: the workspace arrays hold the products of global chunks
+    // [slab_lo, slab_hi) only.  A chain then runs just its chunks inside the
+    // slab: from its initial state when the slab holds its first chunk, else
+    // from carry[n]; into its final state when the slab holds its last chunk,
+    // else into carry[n].  Chains with no chunks at all run in the first slab.
+    // One slab [0, chunk_cap) with no carry covers the whole call.
+    int64_t slab_lo, slab_hi;
+    float* carry;                // [num_seqs, H, dk, dv] (mode 2: dk + dv columns), or NULL
     // prefix-cache checkpoints (modes 0 and 1): the state after every
     // ckpt_every chunks of a sequence, at row ckpt_off[n] + j of ckpt
     float* ckpt;                 // [capacity, H, dk, dv] or NULL
@@ -61,6 +69,12 @@ struct TwoPassArgs {
 };
 
 bool prefill_supported(int dtype, int dk, int dv, int chunk);
+
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per (device, kernel):
+// later calls on the same device return at once.
+hipError_t ensure_lds_limit(const void* kern, int bytes);
+// Compute units of the current device, queried once per device.
+hipError_t device_cu_count(int* cus);
 
 // Per-sequence plan, each output optional: chunk offsets ([num_seqs + 1]),
 // a longest-first order ([num_seqs]) and checkpoint offsets ([num_seqs + 1],

@@ -39,7 +39,9 @@
  *     Niveau 2 Q9 -- with unit keys I - beta k k^T does not expand the state;
  *   - g lies in [g_min, 0] with g_min = -5 (page "Exercices", Niveau 2 Q8:
  *     the cumulative log-decay of a 16-token tile is then >= -80, and e^80
- *     fits the bf16 range); the kernels stay finite for g >= -5.4;
+ *     fits the bf16 range); the kernels keep their accuracy down to
+ *     g = -5.4 over whole 16-token tiles (e^86.4 still fits bf16), which the
+ *     GPU tests check on every entry point that carries a state;
  *   - beta lies in [0, 1];
  *   - cu_seqlens is non-decreasing, cu_seqlens[0] = 0,
  *     cu_seqlens[num_seqs] = T_total.
@@ -96,9 +98,11 @@ const char* kda_status_string(kda_status status);
  *   final_state     fp32 [num_seqs, H, dk, dv] or NULL (not written).  May
  *                   alias initial_state (each state is read before written).
  *   y               output [T_total, H, dv] in dtype dt; must not alias inputs.
- *   workspace       device buffer of at least kda_chunk_fwd_workspace_size
- *                   bytes for the same (dt, H, dk, dv, chunk, num_seqs,
- *                   T_total), 256-byte aligned; overwritten.
+ *   workspace       device buffer, 256-byte aligned, overwritten; of
+ *   workspace_bytes at least kda_chunk_fwd_workspace_min bytes for the same
+ *                   (dt, H, dk, dv, chunk, num_seqs, T_total), else
+ *                   KDA_ERR_WORKSPACE_TOO_SMALL; kda_chunk_fwd_workspace_size
+ *                   bytes or more run in one pass.
  *
  * Two passes on `stream`: every (chunk, head) first forms the products of its
  * chunk that do not involve the entering state (the gated Gram products, the
@@ -142,14 +146,27 @@ kda_status kda_chunk_fwd_fused(kda_dtype dt, int H, int dk, int dv, int chunk, f
                                void* stream);
 
 /*
- * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd
- * needs: per (chunk, head) about 3 dk C + dv C + C^2 / 2 elements of dtype dt
- * plus dk fp32 (70.5 KiB at bf16, dk = dv = 128, C = 64), for up to
- * T_total / chunk + num_seqs chunks.  Returns 0 for invalid or unsupported
- * sizes.
+ * kda_chunk_fwd_workspace_size -- bytes of device workspace with which
+ * kda_chunk_fwd (and its _fused and _checkpointed forms) runs every chunk in
+ * one pass of each kernel, the fastest way: per (chunk, head) about
+ * 3 dk C + dv C + C^2 / 2 elements of dtype dt plus dk fp32 (70.5 KiB at bf16,
+ * dk = dv = 128, C = 64), for up to T_total / chunk + num_seqs chunks.
+ * Returns 0 for invalid or unsupported sizes.
+ *
+ * kda_chunk_fwd_workspace_min -- the smallest workspace those calls accept:
+ * one chunk per head plus a carry of num_seqs * H * dk * dv fp32 states.  Any
+ * size from the minimum up works, so the memory of a prefill need not grow
+ * with T_total (the state itself has a fixed size whatever the length: page
+ * "Exercices", Niveau 1 Q6).  With less than the full size the chunks are
+ * taken in time slabs of as many chunks as fit, one slab after the other on
+ * the stream, each chain's state carried between slabs through the carry
+ * (the same arithmetic, so the same results bit for bit); each slab costs two
+ * more kernel launches and one read and write of the carried states.
  */
 size_t kda_chunk_fwd_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs,
                                     int64_t T_total);
+size_t kda_chunk_fwd_workspace_min(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs,
+                                   int64_t T_total);
 
 /*
  * kda_chunk_fwd_checkpointed -- kda_chunk_fwd that also saves the state every
@@ -182,14 +199,23 @@ kda_status kda_chunk_fwd_checkpointed(kda_dtype dt, int H, int dk, int dv, int c
                                       size_t workspace_bytes, void* stream);
 
 /*
- * kda_kcp_workspace_size -- bytes of device workspace kda_kcp_scan needs for
- * H heads of a T-token sequence split into num_segments segments: the segment
- * pairs (M [dk x dk], Sloc [dk x dv]) and the entering states [dk x dv], all
- * fp32, plus the chunk products of kda_chunk_fwd over the segments.  Returns 0
- * for invalid or unsupported sizes.
+ * kda_kcp_workspace_size -- bytes of device workspace with which kda_kcp_scan
+ * runs fastest for H heads of a T-token sequence split into num_segments
+ * segments: the segment pairs (M [dk x dk], Sloc [dk x dv]) and the entering
+ * states [dk x dv], all fp32, plus the chunk products of kda_chunk_fwd over
+ * all segments, formed once for the pairs and the outputs.  Returns 0 for
+ * invalid or unsupported sizes.
+ *
+ * kda_kcp_workspace_min -- the smallest workspace kda_kcp_scan accepts: the
+ * pairs and entering states (which do not depend on T) plus one chunk per
+ * head.  Between the two sizes the chunk products are formed in slabs of
+ * consecutive chunks, twice (once for the pairs, once for the outputs), and a
+ * segment cut by a slab boundary waits in its own pair or entering-state slot.
  */
 size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, int64_t T,
                               int num_segments);
+size_t kda_kcp_workspace_min(kda_dtype dt, int H, int dk, int dv, int chunk, int64_t T,
+                             int num_segments);
 
 /*
  * kda_kcp_scan -- one long sequence of T tokens split into num_segments equal
@@ -205,8 +231,10 @@ size_t kda_kcp_workspace_size(kda_dtype dt, int H, int dk, int dv, int chunk, in
  *
  *   T, num_segments  T >= num_segments >= 1.
  *   q..z, initial_state, final_state, y: as kda_chunk_fwd with one sequence.
- *   workspace        device buffer of at least kda_kcp_workspace_size bytes,
- *                    256-byte aligned; overwritten.
+ *   workspace        device buffer, 256-byte aligned, overwritten, of at least
+ *                    kda_kcp_workspace_min bytes (else
+ *                    KDA_ERR_WORKSPACE_TOO_SMALL); kda_kcp_workspace_size
+ *                    bytes or more form the chunk products only once.
  */
 kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float scale, int64_t T,
                         int num_segments, const void* q, const void* k, const void* v,
