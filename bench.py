@@ -24,7 +24,9 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
-WARM_MS = 50.0                   # untimed GPU work before each extra workload's timed calls
+WARMUP_POLICY = ("the device peaks are measured first (about 1 s of GPU work, skipped with "
+                 "--no-measured-peaks); then every workload runs `warmup` untimed calls "
+                 "(decode: `warmup` untimed steps) before its timed calls")
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
 ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode", "prefill_checkpoints",
@@ -77,23 +79,13 @@ def counter_traffic(kernel: str):
     return rec["traffic_bytes"] if h.hexdigest() == rec["src_sha256"] else None
 
 
-def time_steps(fn, steps: int, warmup: int, torch, warm_ms: float = 0.0, per_call: bool = False):
-    """Average ms per call of fn over `steps` calls, HIP events on the current stream.
-    Untimed first: `warmup` calls, then (warm_ms > 0) more calls until about
-    warm_ms of GPU time has run, so that the clocks have settled (a cold GPU
-    runs the K3 layer ~10 % slower for the first few dozen calls).  per_call:
-    also the time of each call (events between the calls), as a third value."""
+def time_steps(fn, steps: int, warmup: int, torch, per_call: bool = False):
+    """Average ms per call of fn over `steps` calls, HIP events on the current
+    stream, after `warmup` untimed calls.  per_call: also the time of each call
+    (events between the calls), as a third value."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    if warm_ms > 0:
-        t = time.perf_counter()
-        fn()
-        torch.cuda.synchronize()
-        one = max((time.perf_counter() - t) * 1e3, 1e-3)
-        for _ in range(int(warm_ms / one)):
-            fn()
-        torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -253,7 +245,7 @@ def bench_varlen(args, torch, kda, kda_inputs, dev):
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], z=d["z"],
                       initial_state=d["s0"], chunk=w["chunk"], y=y, final_state=fs, workspace=ws)
 
-    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch, WARM_MS)
+    ms, _ = time_steps(step, max(1, args.steps // 4), args.warmup, torch)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, len(lens), True, True)
     out = dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3),
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -277,7 +269,7 @@ def bench_kcp(args, torch, kda, kda_inputs, dev):
         kda.kcp_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], S, chunk=w["chunk"],
                      workspace=ws, y=y, final_state=fs)
 
-    ms, _ = time_steps(step, max(1, args.steps // 4), 1, torch, WARM_MS)
+    ms, _ = time_steps(step, max(1, args.steps // 4), args.warmup, torch)
     nbytes = prefill_bytes(T, H, dk, dv, 2, False, 1, False, True)
     out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), segments=S,
                gbs_single_pass=nbytes / (ms * 1e-3) / 1e9,
@@ -309,12 +301,13 @@ def bench_decode(args, torch, kda, kda_inputs, dev):
             g=-5.0 * torch.sigmoid(torch.randn(N, H, dk, generator=gen, device=dev))))
     y = torch.empty(N, H, dv, dtype=torch.bfloat16, device=dev)
 
-    def run_all():
-        for s in range(steps):
+    def run_all(n=steps):
+        for s in range(n):
             p = pool[s % P]
             kda.decode_step(p["q"], p["k"], p["v"], p["g"], p["beta"], state, z=p["z"], y=y)
 
-    ms_all, _ = time_steps(run_all, 1, 1, torch)
+    run_all(args.warmup)
+    ms_all, _ = time_steps(run_all, 1, 0, torch)
     ms = ms_all / steps
     nbytes = decode_bytes(N, H, dk, dv, 2, True)
     out = dict(ms_per_step=ms, steps=steps, tokens_per_s=N / (ms * 1e-3),
@@ -335,7 +328,7 @@ def bench_checkpoints(args, torch, kda, kda_inputs, dev):
     d = gpu_inputs(torch, [T], H, dk, dv, True, 0.0, kda_inputs.workload_seed(1), dev)
     ms, _ = time_steps(lambda: kda.chunk_fwd_checkpointed(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                           interval, z=d["z"], chunk=C),
-                       max(1, args.steps // 2), 2, torch, WARM_MS)
+                       max(1, args.steps // 2), args.warmup, torch)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True) + (T // interval) * H * dk * dv * 4
     out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), interval=interval, checkpoints=T // interval,
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -365,9 +358,9 @@ def bench_replay(args, torch, kda, kda_inputs, dev):
     acc = torch.randint(0, Td + 1, (N,), generator=gen, device=dev).to(torch.int32)
     y = torch.empty(N, Td, H, dv, dtype=torch.bfloat16, device=dev)
     ms_v, _ = time_steps(lambda: kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
-                                                   z=x["z"], y=y), 20, 2, torch, WARM_MS)
+                                                   z=x["z"], y=y), 20, args.warmup, torch)
     ms_c, _ = time_steps(lambda: kda.decode_replay(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
-                                                   accepted=acc, z=x["z"], want_y=False), 20, 2, torch, WARM_MS)
+                                                   accepted=acc, z=x["z"], want_y=False), 20, args.warmup, torch)
     st = H * dk * dv * 4                              # one request's states
     tok = H * (2 * dk * 2 + dv * 2 * 2 + dk * 4 + 4)   # one draft token's inputs
     a = [int(t) for t in acc.cpu().tolist()]
@@ -396,7 +389,7 @@ def bench_prefill_chunk32(args, torch, kda, kda_inputs, dev):
     ws = torch.empty(kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, C, 1, T), dtype=torch.uint8,
                      device=dev)
     ms, _ = time_steps(lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C,
-                                             y=y, final_state=fs, workspace=ws), args.steps, 2, torch, WARM_MS)
+                                             y=y, final_state=fs, workspace=ws), args.steps, args.warmup, torch)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True)
     out = dict(ms=ms, chunk=C, tokens_per_s=T / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -428,7 +421,7 @@ def bench_prefill_fused(args, torch, kda, kda_inputs, dev):
         kda.chunk_fwd_fused(d["q"], d["k"], d["v"], d["a"], d["b"], z=d["z"], chunk=C, y=y,
                             final_state=fs, workspace=ws)
 
-    ms, _ = time_steps(step, args.steps, 2, torch, WARM_MS)
+    ms, _ = time_steps(step, args.steps, args.warmup, torch)
     nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True, gate_elt=2)
     out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), bytes=nbytes,
                gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -454,12 +447,13 @@ def bench_decode_fused(args, torch, kda, kda_inputs, dev):
                  a=torch.randn(N, H, dk, generator=gen, device=dev).to(bf)) for _ in range(P)]
     y = torch.empty(N, H, dv, dtype=bf, device=dev)
 
-    def run_all():
-        for s in range(steps):
+    def run_all(n=steps):
+        for s in range(n):
             p = pool[s % P]
             kda.decode_step_fused(p["q"], p["k"], p["v"], p["a"], p["b"], state, z=p["z"], y=y)
 
-    ms_all, _ = time_steps(run_all, 1, 1, torch)
+    run_all(args.warmup)
+    ms_all, _ = time_steps(run_all, 1, 0, torch)
     ms = ms_all / steps
     nbytes = decode_bytes(N, H, dk, dv, 2, True, gate_elt=2)
     out = dict(ms_per_step=ms, steps=steps, tokens_per_s=N / (ms * 1e-3), bytes_per_step=nbytes,
@@ -508,10 +502,10 @@ def main() -> int:
         print(json.dumps({"calibrate_copy_bytes": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}))
         return 0
 
-    inp, head, gpu_out = bench_headline(args, torch, kda, kda_inputs, dev)
     peaks = measured_peaks(torch, dev) if not args.no_measured_peaks else None
     if peaks:
         log(f"measured peaks: {json.dumps(peaks)}")
+    inp, head, gpu_out = bench_headline(args, torch, kda, kda_inputs, dev)
     extras = ALL_WORKLOADS if args.workloads == "all" else tuple(
         x for x in args.workloads.split(",") if x and x != "none")
     workloads = {}
@@ -535,6 +529,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_policy": WARMUP_POLICY,
         "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",
