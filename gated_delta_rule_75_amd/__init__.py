@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "KDAError", "lib", "library_path", "kda_version", "kda_status_string",
     "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_workspace_min", "chunk_fwd_checkpointed",
-    "chunk_fwd_fused", "kcp_scan", "kcp_workspace_size", "kcp_workspace_min", "decode_step",
+    "chunk_fwd_fused", "chunk_fwd_noalloc", "kcp_scan", "kcp_workspace_size", "kcp_workspace_min", "decode_step",
     "decode_step_fused", "decode_replay",
     "KDA_BF16", "KDA_F32",
 ]
@@ -35,7 +35,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 SYMBOLS = ("kda_version", "kda_status_string", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_workspace_min", "kda_chunk_fwd", "kda_chunk_fwd_checkpointed",
            "kda_kcp_workspace_size", "kda_kcp_workspace_min", "kda_kcp_scan",
-           "kda_decode_step", "kda_decode_replay", "kda_chunk_fwd_fused", "kda_decode_step_fused")
+           "kda_decode_step", "kda_decode_replay", "kda_chunk_fwd_fused", "kda_decode_step_fused",
+           "kda_chunk_fwd_noalloc", "kda_noalloc_scratch_bytes")
 
 
 class KDAError(RuntimeError):
@@ -69,6 +70,11 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
+    L.kda_chunk_fwd_noalloc.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp]
+    L.kda_chunk_fwd_noalloc.restype = i
+    L.kda_noalloc_scratch_bytes.argtypes = []
+    L.kda_noalloc_scratch_bytes.restype = sz
     L.kda_chunk_fwd_fused.argtypes = L.kda_chunk_fwd.argtypes
     L.kda_chunk_fwd_fused.restype = i
     L.kda_chunk_fwd_checkpointed.argtypes = [i, i, i, i, i, f, i, i64, vp, vp, vp, vp, vp, vp, vp,
@@ -214,6 +220,31 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=Non
     chunk_fwd_workspace_min bytes)."""
     return _chunk_fwd(False, q, k, v, g, beta, cu_seqlens, z, initial_state, output_final_state,
                       chunk, scale, y, final_state, workspace, max_workspace_bytes)
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens: Optional[torch.Tensor] = None, z=None,
+                      initial_state=None, chunk: int = 64, scale: float = 1.0,
+                      y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None):
+    """chunk_fwd through kda_chunk_fwd_noalloc: no workspace, the library's own
+    per-GPU scratch instead.  y and final_state are allocated here when not
+    given (the C call itself allocates nothing); both are returned."""
+    dt, T, H, dk, dv = _check_inputs(q, k, v, g, beta, z)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    N = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    _need("y", y, (T, H, dv), q.dtype)
+    _need("initial_state", initial_state, (N, H, dk, dv), torch.float32)
+    _need("final_state", final_state, (N, H, dk, dv), torch.float32)
+    dev = _dev(q, k, v, g, beta, z, cu_seqlens, initial_state, y, final_state)
+    if y is None:
+        y = torch.empty(T, H, dv, dtype=q.dtype, device=dev)
+    if final_state is None:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    st = lib().kda_chunk_fwd_noalloc(dt, H, dk, dv, chunk, scale, N, T, _ptr(cu_seqlens), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                                     _ptr(initial_state), _ptr(final_state), _ptr(y), _stream(dev))
+    _check("kda_chunk_fwd_noalloc", st)
+    return y, final_state
 
 
 def chunk_fwd_fused(q, k, v, a, b, cu_seqlens: Optional[torch.Tensor] = None, z=None,

@@ -291,6 +291,61 @@ kda_status kda_chunk_fwd(kda_dtype dt, int H, int dk, int dv, int chunk, float s
                           stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device scratch of kda_chunk_fwd_noalloc: a file-scope array that every GPU
+// holds a copy of from the moment the library is loaded until the process
+// ends.  Host code never names it directly (its host-side name is only a
+// stand-in for the symbol); the device address of each GPU's copy is looked up
+// once, with that GPU current, and kept per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+kda_status scratch_on_current_device(void** out) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* ptrs[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDev) return KDA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KDA_ERR_HIP;
+        ptrs[dev] = ptr;
+    }
+    *out = ptrs[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+kda_status kda_chunk_fwd_noalloc(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                                 int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                                 const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const void* z, const float* initial_state,
+                                 float* final_state, void* y, void* stream) {
+    // a shape whose smallest workspace exceeds the scratch is refused before
+    // anything is looked up or launched
+    const size_t least = kda_chunk_fwd_workspace_min(dt, H, dk, dv, chunk, num_seqs, T_total);
+    if (least == 0) {
+        return (dt != KDA_BF16 && dt != KDA_F32) || H <= 0 || num_seqs <= 0 || T_total < 0
+                   ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
+    }
+    if (least > kScratchBytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    const kda_status st = scratch_on_current_device(&ws);
+    if (st != KDA_OK) return st;
+    return chunk_fwd_impl(dt, false, H, dk, dv, chunk, scale, num_seqs, T_total, cu_seqlens, q, k, v, g, beta,
+                          z, initial_state, final_state, y, 0, nullptr, nullptr, 0, ws, kScratchBytes, stream);
+}
+
 kda_status kda_chunk_fwd_fused(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
                                int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
                                const void* q, const void* k, const void* v, const void* a,

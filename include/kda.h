@@ -199,6 +199,30 @@ kda_status kda_chunk_fwd_checkpointed(kda_dtype dt, int H, int dk, int dv, int c
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation): the same arguments minus the workspace.  The chunk
+ * products go to a scratch array of kda_noalloc_scratch_bytes() (64 MiB) that
+ * the library holds on every GPU it is loaded on until the process ends; the
+ * call runs in time slabs of as many chunks as fit there (as kda_chunk_fwd
+ * with that workspace: the same results bit for bit).  It allocates nothing,
+ * calls no allocating routine and needs nothing zeroed.
+ *
+ *   Returns KDA_ERR_WORKSPACE_TOO_SMALL when even one chunk per head plus the
+ *   carried states (num_seqs * H * dk * dv fp32) exceed the scratch
+ *   (kda_chunk_fwd_workspace_min above kda_noalloc_scratch_bytes()).
+ *   Every call on one GPU uses that GPU's one scratch: calls that overlap in
+ *   time on one GPU (different streams, or different host threads) race and
+ *   corrupt each other's results; callers must order them.
+ */
+kda_status kda_chunk_fwd_noalloc(kda_dtype dt, int H, int dk, int dv, int chunk, float scale,
+                                 int num_seqs, int64_t T_total, const int32_t* cu_seqlens,
+                                 const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const void* z, const float* initial_state,
+                                 float* final_state, void* y, void* stream);
+size_t kda_noalloc_scratch_bytes(void);
+
+/*
  * kda_kcp_workspace_size -- bytes of device workspace with which kda_kcp_scan
  * runs fastest for H heads of a T-token sequence split into num_segments
  * segments: the segment pairs (M [dk x dk], Sloc [dk x dv]) and the entering
