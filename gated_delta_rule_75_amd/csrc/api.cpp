@@ -31,7 +31,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // between time slabs (bounded workspaces only), then the per-(chunk, head)
 // product arrays of one slab of nchunks chunks, each part 256-byte aligned.
 struct Layout {
-    size_t chunk_off, order, carry, wn, qt, kht, pm, ut, gam, total;
+    size_t chunk_off, order, carry, wn, qt, kht, pm, tt, gam, total;
 };
 
 Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_seqs, int64_t nchunks,
@@ -48,7 +48,7 @@ Layout twopass_layout(kda_dtype dt, int H, int dk, int dv, int chunk, int num_se
     l.qt = take(nb * d.qt() * d.esz);
     l.kht = take(nb * d.kht() * d.esz);
     l.pm = take(nb * d.pm() * d.esz);
-    l.ut = take(nb * d.ut() * d.esz);
+    l.tt = take(nb * d.tt() * d.esz);
     l.gam = take(nb * d.gam() * 4);
     l.total = o;
     return l;
@@ -74,7 +74,7 @@ kda::TwoPassBufs bufs_at(void* ws, const Layout& l) {
     x.qt = b + l.qt;
     x.kht = b + l.kht;
     x.pm = b + l.pm;
-    x.ut = b + l.ut;
+    x.tt = b + l.tt;
     x.gam = reinterpret_cast<float*>(b + l.gam);
     return x;
 }

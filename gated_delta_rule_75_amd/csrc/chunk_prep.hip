@@ -6,7 +6,7 @@
 //  1. decay: a wave owns 64 channels of a slice of consecutive tokens, so each
 //     load instruction reads whole 128-byte rows (a layout with fewer channels
 //     per wave touched four times the cache lines per byte); a thread holds
-//     TPT consecutive tokens x 4 consecutive channels of g, k, q, v (beta and
+//     TPT consecutive tokens x 4 consecutive channels of g, k and q (beta and
 //     g are loaded first, so that the sums below wait for them alone).  The
 //     in-chunk running sum G of g is a per-thread sum, a shuffle scan over
 //     the wave's token groups, and a sum of the earlier slices' totals
@@ -21,13 +21,13 @@
 //  3. L = I + diag(beta) A is unit lower triangular; its inverse is blocked:
 //     16 x 16 diagonal blocks by forward substitution, then off-diagonal
 //     blocks level by level, X_ab = -X_aa sum_{b<=c<a} L_ac X_cb (fp32 MFMA).
-//     Each block is also written, times beta_j, in bf16 into the table of
-//     L^{-1} diag(beta) that phase 4 reads.
-//  4. W = L^{-1} diag(beta) (K e^G) and U = L^{-1} diag(beta) V on MFMA, a
-//     wave taking one channel tile of W and one value tile of U, so that
-//     every fragment of L^{-1} diag(beta) feeds both products.
-// Qt, Kh and gam leave straight from the decay phase; the tiles of W, U and
-// P leave as they are produced.
+//     Each block is also written, times beta_j, in the storage type into the
+//     table of Tb = L^{-1} diag(beta) that phase 4 reads.
+//  4. W = Tb (K e^G) on MFMA, a wave taking one channel tile; Tb itself leaves
+//     as fragments for the scan kernel, which forms U = Tb V from v (v is not
+//     read here at all).
+// Qt, Kh and gam leave straight from the decay phase; the tiles of W and P
+// leave as they are produced.
 //
 // Waves share data only through LDS, so the barriers between phases wait for
 // LDS operations alone; the global stores of each phase (and loads still in
@@ -53,7 +53,7 @@ struct PrepParams {
     int64_t T_total, seg_len;
     const int32_t* cu_seqlens;
     const int32_t* chunk_off;  // [num_seqs + 1] chunk offsets of packed sequences, or NULL
-    const void *q, *k, *v;
+    const void *q, *k;      // v is not read here: U = Tb V is formed by the scan kernel
     const void *g, *beta;   // fp32 g and beta, or (FUSED) the pre-activations a, b in the storage dtype
     TwoPassBufs ws;
 };
@@ -86,11 +86,11 @@ struct PrepCfg {
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t SZ_TAB = (size_t)CH * LK * sizeof(T);
     static constexpr size_t SZ_X1 = 3 * SZ_TAB;                       // Kr, Qr, Kc
-    static constexpr size_t SZ_KVT = al((size_t)DK * LC * sizeof(T));  // Kt^T or V^T
+    static constexpr size_t SZ_KVT = al((size_t)DK * LC * sizeof(T));  // Kt^T
     static constexpr size_t SZ_LB = al((size_t)CH * LC * sizeof(T));
-    static constexpr size_t SZ_X2 = 2 * SZ_KVT + SZ_LB;                // after the Gram
+    static constexpr size_t SZ_X2 = SZ_KVT + SZ_LB;                    // after the Gram
     static constexpr size_t O_KR = 0, O_QR = SZ_TAB, O_KC = 2 * SZ_TAB;
-    static constexpr size_t O_KTT = 0, O_VTT = SZ_KVT, O_LB = 2 * SZ_KVT;
+    static constexpr size_t O_KTT = 0, O_LB = SZ_KVT;
     static constexpr size_t SZ_X = al(SZ_X1 > SZ_X2 ? SZ_X1 : SZ_X2);
     static constexpr size_t O_L = SZ_X;                         // blocks of beta A
     static constexpr size_t O_Z = O_L + (size_t)NPAIR * BLK * 4;  // blocks of L^{-1}
@@ -148,7 +148,6 @@ void chunk_prep_kernel(PrepParams p) {
     T* sQr = reinterpret_cast<T*>(smem + C::O_QR);
     T* sKc = reinterpret_cast<T*>(smem + C::O_KC);
     T* sKtT = reinterpret_cast<T*>(smem + C::O_KTT);
-    T* sVtT = reinterpret_cast<T*>(smem + C::O_VTT);
     T* sLB = reinterpret_cast<T*>(smem + C::O_LB);
     float* sL = reinterpret_cast<float*>(smem + C::O_L);
     float* sZ = reinterpret_cast<float*>(smem + C::O_Z);
@@ -161,7 +160,6 @@ void chunk_prep_kernel(PrepParams p) {
     const int cset = wave % C::NWC, tsl = wave / C::NWC;   // wave-uniform
     const T* gq = static_cast<const T*>(p.q);
     const T* gk = static_cast<const T*>(p.k);
-    const T* gv = static_cast<const T*>(p.v);
     using T4 = typename Vec4<T>::type;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -202,12 +200,12 @@ void chunk_prep_kernel(PrepParams p) {
     const int c0 = cset * 64 + 4 * cg;
     const int tl0 = tsl * TPW + tg * TPT;
     // the block's inputs as stored, converted where they are used: g (fp32)
-    // or the pre-activation a, k, q, v, and one beta (or b) per thread below C
+    // or the pre-activation a, k, q, and one beta (or b) per thread below C
     using GRaw = typename std::conditional<C::FUSED, T4, f32x4_t>::type;
     GRaw rg[TPT];
-    T4 rk[TPT], rq[TPT], rv[TPT];
+    T4 rk[TPT], rq[TPT];
     // beta, then g: vector loads complete in issue order, so the running
-    // sums below wait for these alone while k, q and v are still on their way
+    // sums below wait for these alone while k and q are still on their way
     using BRaw = typename std::conditional<C::FUSED, T, float>::type;
     BRaw braw = BRaw(0.f);
     if (tid < CH && tid < nvalid) {
@@ -226,8 +224,6 @@ void chunk_prep_kernel(PrepParams p) {
     for (int i = 0; i < TPT; ++i) rk[i] = *reinterpret_cast<const T4*>(gk + rows[i] * DK + c0);
 #pragma unroll
     for (int i = 0; i < TPT; ++i) rq[i] = *reinterpret_cast<const T4*>(gq + rows[i] * DK + c0);
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) rv[i] = *reinterpret_cast<const T4*>(gv + rows[i] * DV + c0);
     if (tid < CH) {
         if constexpr (C::FUSED) sBeta[tid] = tid < nvalid ? sigmoid(to_f32(braw)) : 0.f;
         else sBeta[tid] = braw;
@@ -237,11 +233,11 @@ void chunk_prep_kernel(PrepParams p) {
     T* Qt = static_cast<T*>(p.ws.qt) + wsb * (CH * DK);
     T* KhT = static_cast<T*>(p.ws.kht) + wsb * (DK * CP);
     T* Pm = static_cast<T*>(p.ws.pm) + wsb * (C::NPM * 64 * (K::KB / 4));
-    T* UT = static_cast<T*>(p.ws.ut) + wsb * (DV * CH);
+    T* Tb = static_cast<T*>(p.ws.tt) + wsb * (C::NPM * 64 * (K::KB / 4));
     float* gam = p.ws.gam + wsb * DK;
 
     // ---- 1. loads and decay ----------------------------------------------------
-    // k, q and v stay in the storage type (rk, rq, rv) until they are used
+    // k and q stay in the storage type (rk, rq) until they are used
     f32x4_t G[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -261,7 +257,6 @@ void chunk_prep_kernel(PrepParams p) {
                 G[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 rk[i] = T4{};
                 rq[i] = T4{};
-                rv[i] = T4{};
             }
     }
     float* sNorm = sL;  // FUSED: [2][NWC][CH] partial squared norms (k, then q)
@@ -464,30 +459,23 @@ void chunk_prep_kernel(PrepParams p) {
     }
     barrier_keep_loads();
 
-    // ---- 3. operands of W and U; inverse of L ----------------------------------
+    // ---- 3. operand of W; inverse of L ---------------------------------------
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
         T* kt = sKtT + (c0 + ch) * LC + tl0;
-        T* vt = sVtT + (c0 + ch) * LC + tl0;
         if constexpr (TPT % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < TPT; i += 4) {
+            for (int i = 0; i < TPT; i += 4)
                 *reinterpret_cast<T4*>(kt + i) = T4{kw[i][ch], kw[i + 1][ch], kw[i + 2][ch], kw[i + 3][ch]};
-                *reinterpret_cast<T4*>(vt + i) = T4{rv[i][ch], rv[i + 1][ch], rv[i + 2][ch], rv[i + 3][ch]};
-            }
         } else {
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                kt[i] = kw[i][ch];
-                vt[i] = rv[i][ch];
-            }
+            for (int i = 0; i < TPT; ++i) kt[i] = kw[i][ch];
         }
     }
     if constexpr (CP > CH) {
         for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
             const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
             sKtT[c * LC + t] = from_f32<T>(0.f);
-            sVtT[c * LC + t] = from_f32<T>(0.f);
         }
     }
     if (wave < NT) {  // diagonal block `wave`, one column per lane (lanes >= 16 repeat)
@@ -557,39 +545,42 @@ void chunk_prep_kernel(PrepParams p) {
         barrier_keep_loads();
     }
 
-    // ---- 4. W^T = (K e^G)^T (L^{-1} diag(beta))^T and U = L^{-1} diag(beta) V ----
-    // A wave owns channel tile ct of W and value tile ct of U: their operands
-    // along the tokens are loaded once, and each fragment of L^{-1} diag(beta)
-    // feeds both products (as the B operand of W^T, the A operand of U).  With
-    // fewer tiles than waves, one set of waves takes W and the other U.
+    // ---- 4. Tb = L^{-1} diag(beta) out as fragments; W^T = (K e^G)^T Tb^T ------
+    // Tb's fragments on or below the diagonal (those of Pm), natural k order:
+    // lane (row r, group g) holds Tb[16 ta + r][u KB + g KB/4 ..], one 16-byte
+    // read of the table and one 16-byte store each
+    {
+        int f = 0;
+#pragma unroll
+        for (int ta = 0; ta < NT; ++ta)
+#pragma unroll
+            for (int u = 0; u < C::NKT; ++u)
+                if (u * K::KB <= 16 * ta + 15) {
+                    if (f % NW == wave) {
+                        const uint4 x = *reinterpret_cast<const uint4*>(sLB + (16 * ta + l16) * LC + u * K::KB +
+                                                                        g4 * (K::KB / 4));
+                        *reinterpret_cast<uint4*>(Tb + (f * 64 + lane) * (K::KB / 4)) = x;
+                    }
+                    ++f;
+                }
+    }
+    // A wave owns channel tile ct of W: its operand along the tokens is loaded
+    // once, and each fragment of Tb is the B operand of W^T.
     {
         constexpr int NKK = (16 * NT + E::KSTEP - 1) / E::KSTEP;  // k-steps of the last token tile
-        constexpr bool SPLIT = NCT < NW;
-        static_assert(!SPLIT || 2 * NCT <= NW, "tiles per wave");
-        for (int j = wave; j < (SPLIT ? 2 * NCT : NCT); j += NW) {
-            const int ct = SPLIT ? j % NCT : j;
-            const bool dw = !SPLIT || j < NCT, du = !SPLIT || j >= NCT;   // wave-uniform
-            typename E::Frag fk[NKK], fv[NKK];
+        for (int ct = wave; ct < NCT; ct += NW) {
+            typename E::Frag fk[NKK];
 #pragma unroll
-            for (int s = 0; s < NKK; ++s) {
-                if (dw) fk[s] = lds_frag<E>(sKtT, LC, 16 * ct, s * E::KSTEP, lane);
-                if (du) fv[s] = lds_frag<E>(sVtT, LC, 16 * ct, s * E::KSTEP, lane);
-            }
+            for (int s = 0; s < NKK; ++s) fk[s] = lds_frag<E>(sKtT, LC, 16 * ct, s * E::KSTEP, lane);
 #pragma unroll
             for (int ta = 0; ta < NT; ++ta) {
-                f32x4_t aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
+                f32x4_t aw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s * E::KSTEP < 16 * (ta + 1); ++s) {
-                    const typename E::Frag fl = lds_frag<E>(sLB, LC, 16 * ta, s * E::KSTEP, lane);
-                    if (dw) aw = E::mma(fk[s], fl, aw);
-                    if (du) au = E::mma(fl, fv[s], au);
-                }
-                if (dw) {  // lane holds W[16ta+l16][16ct+4g4+i]; stored negated
-                    const int c = 16 * ct + 4 * g4;
-                    st4(Wn + frag_elem<K>((c / K::KB) * NT + ta, l16, c), -aw[0], -aw[1], -aw[2], -aw[3]);
-                }
-                if (du)    // lane holds U[16ta+4g4+i][16ct+l16]: the accumulator-layout tile (ct, ta)
-                    st4(UT + ((ct * NT + ta) * 64 + lane) * 4, au[0], au[1], au[2], au[3]);
+                for (int s = 0; s * E::KSTEP < 16 * (ta + 1); ++s)
+                    aw = E::mma(fk[s], lds_frag<E>(sLB, LC, 16 * ta, s * E::KSTEP, lane), aw);
+                // lane holds W[16ta+l16][16ct+4g4+i]; stored negated
+                const int c = 16 * ct + 4 * g4;
+                st4(Wn + frag_elem<K>((c / K::KB) * NT + ta, l16, c), -aw[0], -aw[1], -aw[2], -aw[3]);
             }
         }
     }
@@ -611,7 +602,6 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
     p.chunk_off = chunk_off;
     p.q = a.q;
     p.k = a.k;
-    p.v = a.v;
     p.g = a.g;
     p.beta = a.beta;
     p.ws = a.bufs;

@@ -57,6 +57,7 @@ struct StateParams {
     const int32_t* cu_seqlens;
     const int32_t* chunk_off;
     const int32_t* order;
+    const void* v;
     const void* z;
     void* y;
     const float* s0;
@@ -86,17 +87,22 @@ struct StCfg {
     static constexpr int NPM = pm_frags(NTT, NKT, KB);  // stored fragments of Pm
     // fragment index ranges in an LDS buffer (1 KiB each)
     static constexpr int F_W = 0, N_W = NKC * NTT;
-    static constexpr int F_Q = F_W + N_W, N_Q = AUG ? 0 : NKC * NTT;
+    static constexpr int F_T = F_W + N_W, N_T = NPM;    // L^{-1} diag(beta), operand of U = T V
+    static constexpr int F_Q = F_T + N_T, N_Q = AUG ? 0 : NKC * NTT;
     static constexpr int F_K = F_Q + N_Q, N_K = NCT * NKT;
     static constexpr int F_P = F_K + N_K, N_P = AUG ? 0 : NPM;
     static constexpr int F_G = F_P + N_P;               // gam: dk fp32, repeated to fill 1 KiB
     static constexpr int NF = F_G + 1;
     static constexpr int FPW = (NF + NW - 1) / NW;      // fragment loads per wave
-    // U^T of the workgroup's columns: NW NVT value tiles x NTT token tiles in
-    // accumulator layout (64 lanes x 4 elements each), after the fragments
-    static constexpr int UTT = 64 * 4 * (int)sizeof(T);  // bytes of one U^T tile
-    static constexpr int UTB = NW * NVT * NTT * UTT;
-    static_assert(UTB % 1024 == 0, "U^T in whole 1 KiB copies");
+    // rows of v for the workgroup's columns, after the fragments: [CH][CW]
+    // row-major, the 16-byte units of row t stored at unit x ^ vswz(t), so
+    // that the rows one k-block spreads over the four lane groups of a
+    // fragment read land in different banks.  Copied by the loader waves, or
+    // without them by the compute waves beside their share of the fragments
+    static constexpr int VRB = CW * (int)sizeof(T);     // bytes of one row
+    static constexpr int VTB = CH * VRB;
+    static constexpr int VRPC = 1024 / VRB;             // rows per 1 KiB copy
+    static_assert(VTB % 1024 == 0 && 1024 % VRB == 0, "v rows in whole 1 KiB copies");
     // z and y tiles of the workgroup's columns, [CH][CW] row-major in LDS with
     // the 16-byte units of row t stored at unit x ^ (t % ZXR), which spreads
     // the 16 rows a wave's fragment access touches over the banks
@@ -106,17 +112,29 @@ struct StCfg {
     // loader waves (with two value tiles per wave the compute waves' registers
     // are at the 256 limit already; they keep staging their own operands);
     // the z and y rows go in whole 1 KiB copies per compute wave
-    static constexpr bool LW = NVT == 1 && ZT % (1024 * NW) == 0 && 2 * (NF * 1024 + UTB) + 4 * ZT <= 160 * 1024;
-    static constexpr int BUF = NF * 1024 + (LW ? UTB : 0);
-    static constexpr int NBUF = LW || 2 * BUF <= 150 * 1024 ? 2 : 1;
-    static constexpr int O_Z = NBUF * BUF;                 // with LW: two z tiles, then two y tiles
-    static constexpr int O_Y = O_Z + 2 * ZT;
-    static constexpr int BYTES = NBUF * BUF + (LW ? 4 * ZT : 0);
+    static constexpr bool LW = NVT == 1 && ZT % (1024 * NW) == 0 && 2 * (NF * 1024 + VTB) + 2 * ZT <= 160 * 1024;
+    static constexpr int BUF = NF * 1024 + VTB;
+    static constexpr int NVC = VTB / 1024;              // v-row copies per chunk
+    static constexpr int VPW = (NVC + NW - 1) / NW;     // of them per compute wave (no loader waves)
+    // double buffers unless the pairs, whose workgroups fit two to a CU in
+    // registers, would then lose that: one buffer each, and the other
+    // workgroup of the CU overlaps the copies instead
+    static constexpr int NBUF = LW ? 2 : AUG && 2 * BUF > 80 * 1024 && BUF <= 80 * 1024 ? 1
+                                         : 2 * BUF <= 150 * 1024 ? 2 : 1;
+    // with LW: one z tile and one y tile.  The z rows of chunk c are written
+    // at its top, after every wave has passed the second barrier of chunk c-1
+    // and so has read its z of chunk c-1; the outputs of chunk c are written
+    // after its second barrier, by which every wave has stored chunk c-1's
+    // rows out of the tile
+    static constexpr int O_Z = NBUF * BUF;
+    static constexpr int O_Y = O_Z + ZT;
+    static constexpr int BYTES = NBUF * BUF + (LW ? 2 * ZT : 0);
+    static_assert(BYTES <= 160 * 1024, "LDS");
     // loader waves: four (a wave issues a 1 KiB copy about every 170 cycles
     // on its own; with the copies dealt round-robin, two, three and four
     // loaders reach 324, 317 and 314 us on the 96-head layer)
     static constexpr int NLW = LW ? 4 : 0;
-    static constexpr int NCOPY = NF + UTB / 1024;            // 1 KiB copies per chunk
+    static constexpr int NCOPY = NF + NVC;                   // 1 KiB copies per chunk (LW)
     static constexpr int NTHR = 64 * (NW + NLW);
 };
 
@@ -132,6 +150,13 @@ template <> __device__ __forceinline__ bf16x4_t from_f32x4<__bf16>(f32x4_t x) {
     return bf16x4_t{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
 }
 template <> __device__ __forceinline__ f32x4_t from_f32x4<float>(f32x4_t x) { return x; }
+
+// 16-byte unit swizzle of a v row in LDS: the KPL-row groups that the four
+// lane groups of a fragment read fall on different units
+template <class C>
+__device__ __forceinline__ int vswz(int row) {
+    return ((row / (C::KB / 4)) & 3) * (int)sizeof(typename C::T);
+}
 
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
@@ -189,6 +214,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     // first value tile (16 columns of v / U) of the workgroup; negative for
     // the transition columns of mode 2, whose waves take no values
     const int vt_wg = (vg * C::CW - (C::AUG ? DK : 0)) / 16;
+    const T* gv = static_cast<const T*>(p.v);
 
     if constexpr (C::LW) {
         if (wave >= NW) {
@@ -200,16 +226,22 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             const char* kh = static_cast<const char*>(p.ws.kht) + 16 * lane;
             const char* pm = static_cast<const char*>(p.ws.pm) + 16 * lane;
             const char* gm = reinterpret_cast<const char*>(p.ws.gam) + 16 * (lane % (DK / 4));
-            const char* ut = static_cast<const char*>(p.ws.ut) + 16 * lane;
-            // copy k of a chunk: fragment k (k < NF) or U^T copy k - NF.  Two
-            // groups, each with a barrier of its own: group 1 (U^T and Wn, the
-            // operands of Delta) and group 2 (gam, Kh^T, Qt, Pm), whose last
-            // copies land while Delta is formed.  The U^T copies, private to
-            // the workgroup and so never in L2 already, go out first; the
-            // copies of a group are dealt to the loaders in turn.
+            const char* tt = static_cast<const char*>(p.ws.tt) + 16 * lane;
+            // v rows: lane l of copy j holds row j VRPC + l / units, its
+            // 16-byte unit x stored at x ^ vswz(row); the columns of a
+            // transition workgroup (mode 2) take no values: any valid row
+            constexpr int VU = C::VRB / 16;                    // units per row
+            const int vrow_l = lane / VU, vx = lane % VU;
+            const int vcol_wg = vt_wg > 0 ? 16 * vt_wg : 0;
+            // copy k of a chunk: fragment k (k < NF) or v-row copy k - NF.  Two
+            // groups, each with a barrier of its own: group 1 (v rows, T and Wn,
+            // the operands of Delta) and group 2 (gam, Kh^T, Qt, Pm), whose last
+            // copies land while Delta is formed.  The v rows, private to the
+            // workgroup and so never in L2 already, go out first; the copies
+            // of a group are dealt to the loaders in turn.
             const int li = wave - NW;
             constexpr int NU = C::NCOPY - C::NF;
-            constexpr int NG1 = NU + C::N_W, NG2 = C::NCOPY - NG1;
+            constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
             auto stage_group = [&](int c, int b, auto G) {
                 const int64_t wsb = (int64_t)(cws + c) * H + h;
                 char* buf = smem + b * C::BUF;
@@ -218,29 +250,29 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 const char* ak = kh + wsb * (int64_t)(DK * CP * sizeof(T));
                 const char* ap = pm + wsb * (int64_t)(C::NPM * FB);
                 const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
-                const char* au = ut + wsb * (int64_t)(DV * CH * sizeof(T));
-                constexpr int TPC = 1024 / C::UTT;   // U^T tiles per copy
+                const char* at = tt + wsb * (int64_t)(C::NPM * FB);
+                const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
                 constexpr int NJ = decltype(G)::value == 1 ? NG1 : NG2;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     if (j % C::NLW != li) continue;
                     int k;
-                    if constexpr (decltype(G)::value == 1) k = j < NU ? C::NF + j : C::F_W + j - NU;
+                    if constexpr (decltype(G)::value == 1) k = j < NU ? C::NF + j : C::F_W + j - NU;  // v, Wn, T
                     else k = j == 0 ? C::F_G : j <= C::N_K ? C::F_K + j - 1 : j <= C::N_K + C::N_Q ? C::F_Q + j - 1 - C::N_K
                                                                                             : C::F_P + j - 1 - C::N_K - C::N_Q;
                     const char* src;
-                    if (k < C::F_Q) src = aw + (k - C::F_W) * FB;
+                    if (k < C::F_T) src = aw + (k - C::F_W) * FB;
+                    else if (k < C::F_Q) src = at + (k - C::F_T) * FB;
                     else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
                     else if (k < C::F_P) src = ak + (k - C::F_K) * FB;
                     else if (k < C::F_G) src = ap + (k - C::F_P) * FB;
                     else if (k == C::F_G) src = ag;
                     else {
-                        // U^T tiles [vt_wg, vt_wg + NW NVT) x all token tiles, contiguous;
-                        // transition tiles (vt < 0) copy a valid tile nobody reads
-                        const int lt = (k - C::NF) * TPC;   // first (wave tile, token tile)
-                        int g = vt_wg + lt / NTT;
-                        g = g < 0 ? 0 : g;
-                        src = au + (int64_t)(g * NTT + lt % NTT) * C::UTT;
+                        // v row of this lane (rows past the chunk's end repeat its last one)
+                        int row = (k - C::NF) * C::VRPC + vrow_l;
+                        row = row < nv ? row : nv - 1;
+                        src = reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
+                              16 * (vx ^ vswz<C>(row));
                     }
                     lds_dma16(src, buf + k * 1024);
                 }
@@ -318,10 +350,14 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         int f = wave + NW * j;
         f = f < C::NF ? f : C::NF - 1;   // the last wave repeats its last fragment
         constexpr int FB = 64 * KPL * (int)sizeof(T);   // bytes of one fragment
-        if (f < C::F_Q) {
+        if (f < C::F_T) {
             fbase[j] = static_cast<const char*>(p.ws.wn);
             fstride[j] = (int64_t)CH * DK * sizeof(T);
             foff[j] = (f - C::F_W) * FB;
+        } else if (f < C::F_Q) {
+            fbase[j] = static_cast<const char*>(p.ws.tt);
+            fstride[j] = (int64_t)C::NPM * FB;
+            foff[j] = (f - C::F_T) * FB;
         } else if (f < C::F_K) {
             fbase[j] = static_cast<const char*>(p.ws.qt);
             fstride[j] = (int64_t)CH * DK * sizeof(T);
@@ -341,10 +377,31 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
         foff[j] += 16 * lane;
     }
+    // v-row copies wave + NW j of chunk c (no loader waves): lane l holds row
+    // copy * VRPC + l / units, its unit x stored at x ^ vswz(row)
+    auto stage_v = [&](int c, int b) {
+        if (vt_wg < 0) return;                     // transition columns: no values
+        constexpr int VU = C::VRB / 16;
+        const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+        char* buf = smem + b * C::BUF + C::NF * 1024;
+#pragma unroll
+        for (int j = 0; j < C::VPW; ++j) {
+            const int cp = wave + NW * j;
+            if (cp < C::NVC) {
+                int row = cp * C::VRPC + lane / VU;
+                row = row < nv ? row : nv - 1;
+                lds_dma16(reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + 16 * vt_wg) +
+                              16 * ((lane % VU) ^ vswz<C>(row)),
+                          buf + cp * 1024);
+            }
+        }
+    };
     // fragments [J0, J1) of this wave's share of chunk c into LDS buffer b
+    // (with J0 = 0 also its v-row copies)
     auto stage = [&](int c, int b, auto J0, auto J1) {
         const int64_t wsb = (int64_t)(cws + c) * H + h;
         char* buf = smem + b * C::BUF;
+        if constexpr (decltype(J0)::value == 0) stage_v(c, b);
 #pragma unroll
         for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
             const int f = wave + NW * j < C::NF ? wave + NW * j : C::NF - 1;
@@ -388,33 +445,29 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         if constexpr (ZJW >= 2) zrow1 = *zrow_src(c, 1);
     };
     auto store_yrows = [&](int c) {
-        const char* yt = smem + C::O_Y + (c % 2) * C::ZT;
+        const char* yt = smem + C::O_Y;
         const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
 #pragma unroll
         for (int jj = 0; jj < ZJW; ++jj) {
             const int j = jj * NW + wave;
             int t, x;
             zpos(j, t, x);
-            const uint4 v = *reinterpret_cast<const uint4*>(yt + j * 1024 + 16 * lane);
+            typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(yt + j * 1024 + 16 * lane);
+            // written once, read by nobody here: stored past the caches
             if (t < nv)
-                *reinterpret_cast<uint4*>(reinterpret_cast<char*>(
-                    gy + ((t0 + (int64_t)c * CH + t) * H + h) * DV + vcw) + 16 * x) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(
+                    gy + ((t0 + (int64_t)c * CH + t) * H + h) * DV + vcw) + 16 * x));
         }
     };
-    // U^T and z of the wave's columns, one chunk ahead in registers
-    T4 ut[NTT][NVT], zz[NTT][NVT];
+    // B operand of U = T V for value tile vt of the wave: lane (group g4,
+    // column l16) holds v at the KPL tokens u KB + g4 KPL + e of k-block u, in
+    // the order the T fragments were stored (tokens past the chunk are zero in
+    // T; those past C give zeros here, those past the data repeat the last row)
+    auto vfrag_elem = [&](int u, int e) { return u * KB + g4 * KPL + e; };
+    // without loader waves: z of the wave's columns, one chunk ahead in registers
+    T4 zz[NTT][NVT];
     auto load_uz = [&](int c) {
-        const int64_t wsb = (int64_t)(cws + c) * H + h;
-        const T* UT = static_cast<const T*>(p.ws.ut) + wsb * (DV * CH);
-        if constexpr (!C::LW) {
-#pragma unroll
-            for (int ta = 0; ta < NTT; ++ta)
-#pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) {
-                    const int vtg = ident ? 0 : vcol0 / 16 + vt;   // value tile of the U^T block
-                    ut[ta][vt] = *reinterpret_cast<const T4*>(UT + ((vtg * NTT + ta) * 64 + lane) * 4);
-                }
-        }
         if constexpr (C::LW && !C::AUG) {
             if (gz && c == 0) load_zrows(c);   // later chunks' rows go out right after the first barrier
         } else if (!C::AUG && gz) {
@@ -464,20 +517,18 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         const char* buf = smem + (c % C::NBUF) * C::BUF;
         const int nb = (c + 1) % C::NBUF;
         const int cn = c + 1 < nch ? c + 1 : c;   // the last chunk refetches its own (harmless)
-        wait_vmcnt<0>();                           // chunk c (and U^T, z) of this wave
-        T4 utc[NTT][NVT], zzc[NTT][NVT];
+        wait_vmcnt<0>();                           // chunk c (and v, z) of this wave
+        T4 zzc[NTT][NVT];
+        Frag vfc[NVT][NKT];
+        if constexpr (!C::LW) {
 #pragma unroll
-        for (int ta = 0; ta < NTT; ++ta)
+            for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) {
-                if constexpr (!C::LW) {
-                    utc[ta][vt] = ut[ta][vt];
-                    zzc[ta][vt] = zz[ta][vt];
-                }
-            }
+                for (int ta = 0; ta < NTT; ++ta) zzc[ta][vt] = zz[ta][vt];
+        }
         if constexpr (C::LW && !C::AUG) {
             if (gz) {   // this wave's z rows of chunk c into the z tile
-                char* zt = smem + C::O_Z + (c % 2) * C::ZT;
+                char* zt = smem + C::O_Z;
                 if constexpr (ZJW >= 1) *reinterpret_cast<uint4*>(zt + wave * 1024 + 16 * lane) = zrow0;
                 if constexpr (ZJW >= 2) *reinterpret_cast<uint4*>(zt + (NW + wave) * 1024 + 16 * lane) = zrow1;
             }
@@ -486,16 +537,26 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         // every wave's part of chunk c has landed, and every wave is done with
         // the buffer the next chunk goes to
         barrier_keep_loads();
+        // the wave's v fragments from the v rows of the chunk
+        if (!ident) {
+            const char* vt_rows = buf + C::NF * 1024;
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                for (int u = 0; u < NKT; ++u)
+#pragma unroll
+                    for (int e = 0; e < KPL; ++e) {
+                        const int row = vfrag_elem(u, e);
+                        const int cb = (wave * 16 * NVT + 16 * vt + l16) * (int)sizeof(T);
+                        const T x = row < CH ? *reinterpret_cast<const T*>(vt_rows + row * C::VRB +
+                                                                           ((cb / 16) ^ vswz<C>(row)) * 16 + cb % 16)
+                                             : from_f32<T>(0.f);
+                        K::set(vfc[vt][u], e, x);
+                    }
+        }
         if constexpr (C::LW) {
-#pragma unroll
-            for (int ta = 0; ta < NTT; ++ta)
-#pragma unroll
-                for (int vt = 0; vt < NVT; ++vt)
-                    utc[ta][vt] = *reinterpret_cast<const T4*>(buf + C::NF * 1024 +
-                                                               ((wave * NVT + vt) * NTT + ta) * C::UTT +
-                                                               lane * 4 * (int)sizeof(T));
             if (!C::AUG && gz) {
-                const char* zt = smem + C::O_Z + (c % 2) * C::ZT;
+                const char* zt = smem + C::O_Z;
 #pragma unroll
                 for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
@@ -513,16 +574,32 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt)
                 sf[s][vt] = K::from_acc(S[s * TPB][vt], S[s * TPB + TPB - 1][vt]);
+        // U = T V (T lower triangular: k-blocks on or below the diagonal tile)
         f32x4_t D[NTT][NVT];
 #pragma unroll
         for (int ta = 0; ta < NTT; ++ta)
 #pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = ident ? f32x4_t{0.f, 0.f, 0.f, 0.f} : to_f32x4(utc[ta][vt]);
+            for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (!ident) {
+#pragma unroll
+            for (int ta = 0; ta < NTT; ++ta)
+#pragma unroll
+                for (int u = 0; u < NKT; ++u)
+                    if (u * KB <= 16 * ta + 15) {
+                        const Frag tf = frag(buf, C::F_T + pm_frag_index(ta, u, NKT, KB));
+#pragma unroll
+                        for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(tf, vfc[vt][u], D[ta][vt]);
+                    }
+        }
         // With one value tile per wave, each phase reads all its fragments
         // before its first product, so that the reads overlap one another
         // instead of each product waiting for its own (two tiles have no
         // registers for that).
         constexpr bool PRE = NVT == 1;
+        // the output phase keeps the bf16/fp32 copy of the old state alive
+        // beside its fragments: with fp32 operands and eight waves a
+        // workgroup (256 registers) they are read as they are used instead
+        constexpr bool PRE_O = PRE && !(C::LW && sizeof(T) == 4 && NKC * NTT > 8);
         if constexpr (PRE) {
             Frag wf[NKC][NTT];
 #pragma unroll
@@ -626,7 +703,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
                 for (int ta = 0; ta < NTT; ++ta) O[vt][ta] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (PRE) {
+            if constexpr (PRE_O) {
                 Frag qf[NKC][NTT], pf[NTT][NKT];
 #pragma unroll
                 for (int s = 0; s < NKC; ++s)
@@ -677,7 +754,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                         for (int i = 0; i < 4; ++i) o[i] *= sigmoid(zf[i]);
                     }
                     if constexpr (C::LW)
-                        *reinterpret_cast<T4*>(smem + C::O_Y + (c % 2) * C::ZT + zy_off(ta, vt)) = from_f32x4<T>(o);
+                        *reinterpret_cast<T4*>(smem + C::O_Y + zy_off(ta, vt)) = from_f32x4<T>(o);
                     else
                         yd[ta][vt] = from_f32x4<T>(o);
                 }
@@ -800,6 +877,7 @@ static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_of
     p.cu_seqlens = a.cu_seqlens;
     p.chunk_off = chunk_off;
     p.order = order;
+    p.v = a.v;
     p.z = a.z;
     p.y = a.y;
     p.s0 = a.initial_state;

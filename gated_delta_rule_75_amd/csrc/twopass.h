@@ -6,14 +6,17 @@
 // "Exercices", Niveau 2 Q7; the pages cite the blocked "UT transform" form
 // without printing it, so it is derived here), with G_t the in-chunk running
 // sum of g and A_tj = sum_c k_tc k_jc e^{G_tc - G_jc} (j < t):
-//     Delta = U - W S                       W = L^{-1} diag(beta) (K e^G)
-//     O     = Qt S + Pm Delta               U = L^{-1} diag(beta) V
-//     S    <- gam * S + Kh^T Delta          L = I + diag(beta) A
+//     Delta = U - W S                       W = Tb (K e^G)
+//     O     = Qt S + Pm Delta               U = Tb V
+//     S    <- gam * S + Kh^T Delta          Tb = L^{-1} diag(beta), L = I + diag(beta) A
 // with Qt = scale Q e^G, Pm_tj = scale sum_c q_tc k_jc e^{G_tc - G_jc} (j <= t),
 // Kh = K e^{G_C - G} and gam = e^{G_C}.  Everything except the three
 // S-products depends on the chunk alone, so the preparation kernel forms it
 // for every (chunk, head) at once, and the scan kernel carries the state
 // through the chunks of a sequence with three small products per chunk.
+// U = Tb V is left to the scan kernel, off the state's path: it needs only
+// the C x C triangle Tb beside v itself, so the preparation kernel neither
+// reads v nor writes a C x dv product per chunk.
 //
 // Workspace arrays, one block per (chunk, head), chunk-major ("chunk" is the
 // global chunk index over all sequences):
@@ -22,16 +25,18 @@
 //   KhT  Kh^T    [dk x CP]   rows c, reduction over tokens
 //   Pm           [C x CP]    rows t, reduction over tokens j (zero for j > t);
 //                            only the fragments on or below the diagonal
-//   UT   U^T     [dv x C]
+//   Tb           [C x CP]    rows t, reduction over tokens j (zero for j > t);
+//                            the same fragments as Pm, k in natural order
 //   gam          [dk] fp32
 // CP is C rounded up to a whole k-block (tokens past C are zero).  The
 // operand matrices are stored as MFMA fragments: a fragment is 16 rows x one
 // k-block, 64 lanes x 16 bytes in lane order, lane l = (row % 16) + 16 * slot
 // holding the k-block positions [slot * KB/4, (slot + 1) * KB/4) of its row
 // (positions in the k-block order below).  A fragment is then one contiguous
-// 1 KiB read, and the lanes of a wave read it with one 16-byte access each.  U^T is stored in accumulator layout: for each 16 x 16 tile
-// (value tile vt, token tile ta), lane l holds rows 4(l/16) .. 4(l/16)+3 of
-// token column l%16, i.e. U[16 ta + 4(l/16) + i][16 vt + l%16].
+// 1 KiB read, and the lanes of a wave read it with one 16-byte access each.
+// Tb's fragments keep the natural k order (lane group g holds k-block
+// positions g KB/4 ..): both operands of U = Tb V come from memory, so no
+// accumulator order constrains them.
 //
 // k-block order.  The scan kernel keeps S and Delta in MFMA accumulator tiles,
 // where lane l holds rows 4*(l/16)+i (i < 4) of column l%16, and feeds them
@@ -80,6 +85,7 @@ template <> struct KBlk<BF16> {
         for (int i = 0; i < 8; ++i) f[i] = (__bf16)0.f;
         return f;
     }
+    static __device__ __forceinline__ void set(Frag& f, int e, T x) { f[e] = x; }
 };
 
 template <> struct KBlk<F32> {
@@ -95,6 +101,7 @@ template <> struct KBlk<F32> {
     }
     static __device__ __forceinline__ Frag from_acc(f32x4_t lo, f32x4_t) { return lo; }
     static __device__ __forceinline__ Frag zero() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+    static __device__ __forceinline__ void set(Frag& f, int e, T x) { f[e] = x; }
 };
 
 // Element offset, inside one array block, of element (row, k) of an operand
@@ -130,10 +137,10 @@ struct TwoPassDims {
     size_t kht() const { return (size_t)dk * CP; }
     size_t pm() const { return (size_t)pm_frags(C / 16, CP / (esz == 2 ? 32 : 16), esz == 2 ? 32 : 16) * 64 *
                                (esz == 2 ? 8 : 4); }
-    size_t ut() const { return (size_t)dv * C; }
+    size_t tt() const { return pm(); }
     size_t gam() const { return (size_t)dk; }
     // bytes of one (chunk, head) block over all arrays
-    size_t block_bytes() const { return (wn() + qt() + kht() + pm() + ut()) * esz + gam() * 4; }
+    size_t block_bytes() const { return (wn() + qt() + kht() + pm() + tt()) * esz + gam() * 4; }
 };
 
 inline TwoPassDims twopass_dims(int dtype, int dk, int dv, int chunk) {
@@ -149,7 +156,7 @@ inline TwoPassDims twopass_dims(int dtype, int dk, int dv, int chunk) {
 
 // Device pointers of the workspace arrays.
 struct TwoPassBufs {
-    void *wn, *qt, *kht, *pm, *ut;
+    void *wn, *qt, *kht, *pm, *tt;
     float* gam;
 };
 

@@ -91,11 +91,12 @@ def _pm_frags(C, kb):
 
 
 def _chunk_block_bytes(elt, dk, dv, C, CP):
-    """Bytes of the chunk products of one (chunk, head): Wn, Qt [C, dk], Kh^T [dk, CP],
-    U^T [dv, C] in the input dtype, the 1 KiB fragments of Pm on or below the
-    diagonal, and gam [dk] fp32."""
+    """Bytes of the chunk products of one (chunk, head): Wn, Qt [C, dk], Kh^T [dk, CP]
+    in the input dtype, the 1 KiB fragments of Pm and of L^-1 diag(beta) on or
+    below the diagonal, and gam [dk] fp32 (no C x dv product: U is formed from v
+    by the state pass)."""
     kb = 32 if elt == 2 else 16
-    return (2 * C * dk + dk * CP + dv * C) * elt + _pm_frags(C, kb) * 1024 + dk * 4
+    return (2 * C * dk + dk * CP) * elt + 2 * _pm_frags(C, kb) * 1024 + dk * 4
 
 
 def _rnd(x):
@@ -107,13 +108,14 @@ def test_chunk_fwd_workspace_size(L):
     nb = (T // C + N) * H
     parts = [N + 1, N]   # chunk offsets and order, int32
     parts = [_rnd(4 * x) for x in parts]
-    for n in (C * dk, C * dk, dk * C, _pm_frags(C, 32) * 512, dv * C):
+    for n in (C * dk, C * dk, dk * C, _pm_frags(C, 32) * 512, _pm_frags(C, 32) * 512):
         parts.append(_rnd(nb * n * 2))
     parts.append(_rnd(nb * dk * 4))
     assert L.kda_chunk_fwd_workspace_size(BF16, H, dk, dv, C, N, T) == sum(parts)
-    # per (chunk, head) 70.5 KiB at this shape: 6 of the 8 fragments of P are stored
+    # per (chunk, head) 60.5 KiB at this shape: 6 of the 8 fragments of P (and of
+    # L^-1 diag(beta)) are stored
     assert _pm_frags(64, 32) == 6
-    assert _chunk_block_bytes(2, dk, dv, C, C) == 72192
+    assert _chunk_block_bytes(2, dk, dv, C, C) == 61952
     # bf16 k-blocks are 32 tokens: chunk 16 pads K^T and P to 32 columns
     small = L.kda_chunk_fwd_workspace_size(BF16, 1, 64, 64, 16, 1, 16)
     assert small >= 2 * _chunk_block_bytes(2, 64, 64, 16, 32)
