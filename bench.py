@@ -30,7 +30,8 @@ WARMUP_POLICY = ("the device peaks are measured first (about 1 s of GPU work, sk
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
 ALL_WORKLOADS = ("varlen_prefill", "kcp_long_sequence", "decode", "prefill_checkpoints",
-                 "decode_replay", "prefill_fused_gates", "decode_fused_gates", "prefill_chunk32")
+                 "decode_replay", "prefill_fused_gates", "decode_fused_gates", "prefill_chunk32",
+                 "prefill_bounded_workspace", "kcp_bounded_workspace")
 
 
 def log(msg: str) -> None:
@@ -377,6 +378,51 @@ def bench_replay(args, torch, kda, kda_inputs, dev):
     return out
 
 
+def bench_prefill_bounded(args, torch, kda, kda_inputs, dev):
+    """The K3 layer prefill in a 256 MiB workspace instead of its one-pass
+    894 MB: time slabs with the state carried between them (the same results
+    bit for bit); the workspace no longer grows with T."""
+    w = kda_inputs.WORKLOADS[1]
+    H, dk, dv, T, C = w["H"], w["dk"], w["dv"], w["lens"][0], w["chunk"]
+    limit = 256 << 20
+    d = gpu_inputs(torch, [T], H, dk, dv, True, 0.0, kda_inputs.workload_seed(1), dev)
+    y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(limit, dtype=torch.uint8, device=dev)
+    ms, _ = time_steps(lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], z=d["z"], chunk=C,
+                                             y=y, final_state=fs, workspace=ws), args.steps, args.warmup, torch)
+    nbytes = prefill_bytes(T, H, dk, dv, 2, True, 1, False, True)
+    full = kda.chunk_fwd_workspace_size(kda.KDA_BF16, H, dk, dv, C, 1, T)
+    out = dict(ms=ms, workspace_bytes=limit, one_pass_workspace_bytes=full,
+               min_workspace_bytes=kda.chunk_fwd_workspace_min(kda.KDA_BF16, H, dk, dv, C, 1, T),
+               tokens_per_s=T / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
+               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del d, y, fs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_kcp_bounded(args, torch, kda, kda_inputs, dev):
+    """The 1M-token KCP scan in a 512 MiB workspace instead of its one-pass
+    size (~4.3 GB): the chunk products in slabs, formed twice."""
+    w = kda_inputs.WORKLOADS[3]
+    H, dk, dv, T, S = w["H"], w["dk"], w["dv"], w["lens"][0], w["segments"]
+    limit = 512 << 20
+    d = gpu_inputs(torch, [T], H, dk, dv, False, 0.0, kda_inputs.workload_seed(3), dev)
+    ws = torch.empty(limit, dtype=torch.uint8, device=dev)
+    y = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    ms, _ = time_steps(lambda: kda.kcp_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], S, chunk=w["chunk"],
+                                            workspace=ws, y=y, final_state=fs),
+                       max(1, args.steps // 4), args.warmup, torch)
+    out = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), segments=S, workspace_bytes=limit,
+               one_pass_workspace_bytes=kda.kcp_workspace_size(kda.KDA_BF16, H, dk, dv, w["chunk"], T, S),
+               min_workspace_bytes=kda.kcp_workspace_min(kda.KDA_BF16, H, dk, dv, w["chunk"], T, S))
+    del d, ws, y, fs
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_prefill_chunk32(args, torch, kda, kda_inputs, dev):
     """The K3 layer prefill with 32-token chunks (the headline fixes 64): the
     same result up to rounding, a smaller per-chunk triangular block."""
@@ -513,7 +559,9 @@ def main() -> int:
         fn = {"varlen_prefill": bench_varlen, "kcp_long_sequence": bench_kcp,
               "decode": bench_decode, "prefill_checkpoints": bench_checkpoints,
               "decode_replay": bench_replay, "prefill_fused_gates": bench_prefill_fused,
-              "decode_fused_gates": bench_decode_fused, "prefill_chunk32": bench_prefill_chunk32}[name]
+              "decode_fused_gates": bench_decode_fused, "prefill_chunk32": bench_prefill_chunk32,
+              "prefill_bounded_workspace": bench_prefill_bounded,
+              "kcp_bounded_workspace": bench_kcp_bounded}[name]
         workloads[name] = fn(args, torch, kda, kda_inputs, dev)
         log(f"{name}: {json.dumps(workloads[name])}")
     cpu, parity = (None, None)
