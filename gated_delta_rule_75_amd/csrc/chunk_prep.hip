@@ -39,8 +39,8 @@
 // while loading, beta = sigmoid(b), and scales each token's q and k to unit
 // length (unit keys: page "Exercices", Niveau 2 Q9; the low-rank W_alpha and
 // W_beta that produce a and b: page "Retrouver les 2,8 T de paramètres",
-// Bloc 4).  The squared norms are summed over the lanes of a wave by
-// shuffles and across waves through LDS that phase 2 later reuses.
+// Bloc 4).  The squared norms are summed over the 16 lanes of a token group
+// by DPP moves and across waves through LDS that phase 2 later reuses.
 #include "launch.h"
 #include "twopass.h"
 
@@ -272,11 +272,9 @@ void chunk_prep_kernel(PrepParams p) {
                 sk += kk[ch] * kk[ch];
                 sq += qq[ch] * qq[ch];
             }
-#pragma unroll
-            for (int d = 1; d < CGW; d <<= 1) {
-                sk += __shfl_xor(sk, d, 64);
-                sq += __shfl_xor(sq, d, 64);
-            }
+            static_assert(CGW == 16, "a token group is one 16-lane row");
+            sk = row16_sum(sk);
+            sq = row16_sum(sq);
             if (cg == 0) {
                 sNorm[cset * CH + tl0 + i] = sk;
                 sNorm[(C::NWC + cset) * CH + tl0 + i] = sq;

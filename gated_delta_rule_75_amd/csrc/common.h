@@ -156,6 +156,23 @@ __device__ __forceinline__ void barrier_keep_loads() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Sum over each row of 16 consecutive lanes, the total in every lane of the
+// row: DPP quad permutations [1,0,3,2] and [2,3,0,1] for lane distances 1
+// and 2, then the half-row and row mirrors for 4 and 8.  Four VALU adds and
+// no LDS traffic (a __shfl_xor is an LDS permute); every lane adds the same
+// pairs in the same order, so all of them hold the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
+    return x;
+}
+
 // Fused input step: unit q and k as x / sqrt(sum x^2 + kNormEps), the
 // log-decay g = kGMin * sigmoid(a) in (kGMin, 0), beta = sigmoid(b).
 constexpr float kGMin = -5.0f;
