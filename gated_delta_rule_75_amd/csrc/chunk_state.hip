@@ -86,20 +86,30 @@ struct StCfg {
     static_assert(NKC * TPB == NCT, "channel k-blocks");
     static constexpr int NPM = pm_frags(NTT, NKT, KB);  // stored fragments of Pm
     // fragment index ranges in an LDS buffer (1 KiB each)
+    // The KCP pairs with two value tiles a wave mix their columns: waves
+    // 0 .. NW/2-1 take transition columns and the others value columns, so
+    // each workgroup needs v for half its columns, and T and the v rows sit
+    // in one region of their own (restaged mid-chunk) while the rest is
+    // double-buffered: 80 KB, two workgroups a CU.
+    static constexpr bool MIX = AUG && NVT == 2;
     static constexpr int F_W = 0, N_W = NKC * NTT;
-    static constexpr int F_T = F_W + N_W, N_T = NPM;    // L^{-1} diag(beta), operand of U = T V
-    static constexpr int F_Q = F_T + N_T, N_Q = AUG ? 0 : NKC * NTT;
+    static constexpr int N_T = NPM;                     // L^{-1} diag(beta), operand of U = T V
+    static constexpr int F_T0 = F_W + N_W;              // T beside Wn (loader group 1: v, Wn, T)
+    static constexpr int F_Q = MIX ? F_T0 : F_T0 + N_T, N_Q = AUG ? 0 : NKC * NTT;
     static constexpr int F_K = F_Q + N_Q, N_K = NCT * NKT;
     static constexpr int F_P = F_K + N_K, N_P = AUG ? 0 : NPM;
     static constexpr int F_G = F_P + N_P;               // gam: dk fp32, repeated to fill 1 KiB
-    static constexpr int NF = F_G + 1;
-    static constexpr int FPW = (NF + NW - 1) / NW;      // fragment loads per wave
+    static constexpr int NFB = F_G + 1;                 // fragments held in a buffer
+    static constexpr int F_T = MIX ? NFB : F_T0;        // MIX: T after those, in its own region
+    static constexpr int NF = NFB + (MIX ? N_T : 0);
+    static constexpr int FPW = (NFB + NW - 1) / NW;     // buffered fragment loads per wave
     // rows of v for the workgroup's columns, after the fragments: [CH][CW]
     // row-major, the 16-byte units of row t stored at unit x ^ vswz(t), so
     // that the rows one k-block spreads over the four lane groups of a
     // fragment read land in different banks.  Copied by the loader waves, or
     // without them by the compute waves beside their share of the fragments
-    static constexpr int VRB = CW * (int)sizeof(T);     // bytes of one row
+    static constexpr int VCOLS = MIX ? CW / 2 : CW;     // value columns of a workgroup
+    static constexpr int VRB = VCOLS * (int)sizeof(T);  // bytes of one row
     static constexpr int VTB = CH * VRB;
     static constexpr int VRPC = 1024 / VRB;             // rows per 1 KiB copy
     static_assert(VTB % 1024 == 0 && 1024 % VRB == 0, "v rows in whole 1 KiB copies");
@@ -113,14 +123,14 @@ struct StCfg {
     // are at the 256 limit already; they keep staging their own operands);
     // the z and y rows go in whole 1 KiB copies per compute wave
     static constexpr bool LW = NVT == 1 && ZT % (1024 * NW) == 0 && 2 * (NF * 1024 + VTB) + 2 * ZT <= 160 * 1024;
-    static constexpr int BUF = NF * 1024 + VTB;
+    static constexpr int BUF = NFB * 1024 + (MIX ? 0 : VTB);
     static constexpr int NVC = VTB / 1024;              // v-row copies per chunk
     static constexpr int VPW = (NVC + NW - 1) / NW;     // of them per compute wave (no loader waves)
     // double buffers unless the pairs, whose workgroups fit two to a CU in
     // registers, would then lose that: one buffer each, and the other
     // workgroup of the CU overlaps the copies instead
-    static constexpr int NBUF = LW ? 2 : AUG && 2 * BUF > 80 * 1024 && BUF <= 80 * 1024 ? 1
-                                         : 2 * BUF <= 150 * 1024 ? 2 : 1;
+    static constexpr int NBUF = LW || MIX ? 2 : AUG && 2 * BUF > 80 * 1024 && BUF <= 80 * 1024 ? 1
+                                              : 2 * BUF <= 150 * 1024 ? 2 : 1;
     // with LW: one z tile and one y tile.  The z rows of chunk c are written
     // at its top, after every wave has passed the second barrier of chunk c-1
     // and so has read its z of chunk c-1; the outputs of chunk c are written
@@ -128,8 +138,10 @@ struct StCfg {
     // rows out of the tile
     static constexpr int O_Z = NBUF * BUF;
     static constexpr int O_Y = O_Z + ZT;
-    static constexpr int BYTES = NBUF * BUF + (LW ? 2 * ZT : 0);
+    static constexpr int O_TV = NBUF * BUF;                // MIX: T fragments, then the v rows
+    static constexpr int BYTES = NBUF * BUF + (LW ? 2 * ZT : 0) + (MIX ? N_T * 1024 + VTB : 0);
     static_assert(BYTES <= 160 * 1024, "LDS");
+    static_assert(!MIX || sizeof(T) == 4 || BYTES <= 80 * 1024, "two pairs workgroups a CU");
     // loader waves: four (a wave issues a 1 KiB copy about every 170 cycles
     // on its own; with the copies dealt round-robin, two, three and four
     // loaders reach 324, 317 and 314 us on the 96-head layer)
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     nch = ce - cb;
     // first value tile (16 columns of v / U) of the workgroup; negative for
     // the transition columns of mode 2, whose waves take no values
-    const int vt_wg = (vg * C::CW - (C::AUG ? DK : 0)) / 16;
+    const int vt_wg = C::MIX ? vg * C::VCOLS / 16 : (vg * C::CW - (C::AUG ? DK : 0)) / 16;
     const T* gv = static_cast<const T*>(p.v);
 
     if constexpr (C::LW) {
@@ -261,8 +273,8 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                     else k = j == 0 ? C::F_G : j <= C::N_K ? C::F_K + j - 1 : j <= C::N_K + C::N_Q ? C::F_Q + j - 1 - C::N_K
                                                                                             : C::F_P + j - 1 - C::N_K - C::N_Q;
                     const char* src;
-                    if (k < C::F_T) src = aw + (k - C::F_W) * FB;
-                    else if (k < C::F_Q) src = at + (k - C::F_T) * FB;
+                    if (k < C::F_T0) src = aw + (k - C::F_W) * FB;
+                    else if (k < C::F_Q) src = at + (k - C::F_T0) * FB;
                     else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
                     else if (k < C::F_P) src = ak + (k - C::F_K) * FB;
                     else if (k < C::F_G) src = ap + (k - C::F_P) * FB;
@@ -305,7 +317,11 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
     }
 
-    const int colw = vg * C::CW + wave * 16 * NVT;  // first state column of the wave
+    // first state column of the wave (MIX: the first half of the waves on
+    // transition columns, the second half on value columns)
+    const int colw = !C::MIX ? vg * C::CW + wave * 16 * NVT
+                   : wave < NW / 2 ? vg * C::VCOLS + wave * 16 * NVT
+                                   : DK + vg * C::VCOLS + (wave - NW / 2) * 16 * NVT;
     const bool ident = C::AUG && colw < DK;         // transition columns: start I, values 0
     const int vcol0 = C::AUG ? colw - DK : colw;    // its first column of v / z / y
 
@@ -348,16 +364,16 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
     for (int j = 0; j < C::FPW; ++j) {
         int f = wave + NW * j;
-        f = f < C::NF ? f : C::NF - 1;   // the last wave repeats its last fragment
+        f = f < C::NFB ? f : C::NFB - 1;   // the last wave repeats its last fragment
         constexpr int FB = 64 * KPL * (int)sizeof(T);   // bytes of one fragment
-        if (f < C::F_T) {
+        if (f < C::F_T0) {
             fbase[j] = static_cast<const char*>(p.ws.wn);
             fstride[j] = (int64_t)CH * DK * sizeof(T);
             foff[j] = (f - C::F_W) * FB;
-        } else if (f < C::F_Q) {
+        } else if (f < C::F_T0 + C::N_T && !C::MIX) {
             fbase[j] = static_cast<const char*>(p.ws.tt);
             fstride[j] = (int64_t)C::NPM * FB;
-            foff[j] = (f - C::F_T) * FB;
+            foff[j] = (f - C::F_T0) * FB;
         } else if (f < C::F_K) {
             fbase[j] = static_cast<const char*>(p.ws.qt);
             fstride[j] = (int64_t)CH * DK * sizeof(T);
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         if (vt_wg < 0) return;                     // transition columns: no values
         constexpr int VU = C::VRB / 16;
         const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
-        char* buf = smem + b * C::BUF + C::NF * 1024;
+        char* buf = C::MIX ? smem + C::O_TV + C::N_T * 1024 : smem + b * C::BUF + C::NFB * 1024;
 #pragma unroll
         for (int j = 0; j < C::VPW; ++j) {
             const int cp = wave + NW * j;
@@ -397,16 +413,29 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         }
     };
     // fragments [J0, J1) of this wave's share of chunk c into LDS buffer b
-    // (with J0 = 0 also its v-row copies)
+    // (with J0 = 0 also its v-row copies, except with MIX)
     auto stage = [&](int c, int b, auto J0, auto J1) {
         const int64_t wsb = (int64_t)(cws + c) * H + h;
         char* buf = smem + b * C::BUF;
-        if constexpr (decltype(J0)::value == 0) stage_v(c, b);
+        if constexpr (decltype(J0)::value == 0 && !C::MIX) stage_v(c, b);
 #pragma unroll
         for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
-            const int f = wave + NW * j < C::NF ? wave + NW * j : C::NF - 1;
+            const int f = wave + NW * j < C::NFB ? wave + NW * j : C::NFB - 1;
             lds_dma16(fbase[j] + wsb * fstride[j] + foff[j], buf + f * 1024);
         }
+    };
+    // MIX: T fragments and v rows of chunk c into their own region
+    auto stage_tv = [&](int c) {
+        const int64_t wsb = (int64_t)(cws + c) * H + h;
+        const char* tsrc = static_cast<const char*>(p.ws.tt) + wsb * (int64_t)(C::NPM * 1024) + 16 * lane;
+#pragma unroll
+        for (int f = wave; f < C::N_T; f += NW) lds_dma16(tsrc + f * 1024, smem + C::O_TV + f * 1024);
+        stage_v(c, 0);
+    };
+    // fragment i of T for buffer buf
+    auto tfrag = [&](const char* buf, int i) -> Frag {
+        const char* at = C::MIX ? smem + C::O_TV + i * 1024 : buf + (C::F_T + i) * 1024;
+        return *reinterpret_cast<const Frag*>(at + 16 * lane);
     };
     using J_0 = std::integral_constant<int, 0>;
     using J_H = std::integral_constant<int, C::FPW / 2>;
@@ -511,6 +540,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     asm volatile("" : "+s"(ckpt), "+s"(ck_every), "+s"(ck_cap), "+s"(ck_base));
     if (nch > 0) {
         if constexpr (!C::LW) stage(0, 0, J_0{}, J_E{});
+        if constexpr (C::MIX) stage_tv(0);
         load_uz(0);
     }
     for (int c = 0; c < nch; ++c) {
@@ -539,7 +569,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         barrier_keep_loads();
         // the wave's v fragments from the v rows of the chunk
         if (!ident) {
-            const char* vt_rows = buf + C::NF * 1024;
+            const char* vt_rows = C::MIX ? smem + C::O_TV + C::N_T * 1024 : buf + C::NFB * 1024;
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
@@ -547,7 +577,8 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
                     for (int e = 0; e < KPL; ++e) {
                         const int row = vfrag_elem(u, e);
-                        const int cb = (wave * 16 * NVT + 16 * vt + l16) * (int)sizeof(T);
+                        const int wv = C::MIX ? wave - NW / 2 : wave;   // the wave's place among the value columns
+                        const int cb = (wv * 16 * NVT + 16 * vt + l16) * (int)sizeof(T);
                         const T x = row < CH ? *reinterpret_cast<const T*>(vt_rows + row * C::VRB +
                                                                            ((cb / 16) ^ vswz<C>(row)) * 16 + cb % 16)
                                              : from_f32<T>(0.f);
@@ -586,7 +617,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 #pragma unroll
                 for (int u = 0; u < NKT; ++u)
                     if (u * KB <= 16 * ta + 15) {
-                        const Frag tf = frag(buf, C::F_T + pm_frag_index(ta, u, NKT, KB));
+                        const Frag tf = tfrag(buf, pm_frag_index(ta, u, NKT, KB));
 #pragma unroll
                         for (int vt = 0; vt < NVT; ++vt) D[ta][vt] = K::mma(tf, vfc[vt][u], D[ta][vt]);
                     }
@@ -627,6 +658,10 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             } else if (yd_nvalid > 0) {
                 store_y();
             }
+        }
+        if constexpr (C::MIX) {
+            barrier_keep_loads();                  // every wave is done with T and v of chunk c
+            if (c + 1 < nch) stage_tv(c + 1);
         }
         if constexpr (C::NBUF == 2 && !C::LW) stage(cn, nb, J_0{}, J_H{});
         Frag df[NKT][NVT];

@@ -409,6 +409,22 @@ def test_kcp_scan_matches_sequential_oracle(kda, dtype, d, chunk):
     assert_parity(f"kcp {dtype} d{d} c{chunk}", inp, y.cpu(), fs.cpu(), yo, so, TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype,d,chunk,H,T", [("bf16", 128, 64, 2, 10000), ("f32", 128, 64, 2, 9000),
+                                                 ("bf16", 64, 16, 4, 7000), ("f32", 64, 32, 4, 8192)])
+def test_kcp_many_segments_two_value_tiles(kda, dtype, d, chunk, H, T):
+    """256 segments a head: enough (transition, local state) chains for the
+    pair pass to take two value tiles a wave, whose workgroups split their
+    waves between transition and value columns; ragged last segments."""
+    inp = kda_inputs.make_workload(3, "segment", lens=[T], H=H, dk=d, dv=d, dtype=dtype,
+                                   s0_std=0.05, gated=True)
+    y, fs = kda.kcp_scan(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.g.cuda(),
+                         inp.beta.cuda(), 256, z=inp.z.cuda(), initial_state=inp.S0.cuda(),
+                         chunk=chunk)
+    torch.cuda.synchronize()
+    yo, so = oracle_prefill(inp)
+    assert_parity(f"kcp 256 segments {dtype} d{d} c{chunk}", inp, y.cpu(), fs.cpu(), yo, so, TOL[dtype])
+
+
 def test_kcp_ragged_segments(kda):
     """T not a multiple of the segment count (trailing segments shorter or empty)."""
     inp = kda_inputs.make_workload(3, "segment", lens=[1001], H=2, s0_std=0.05)
