@@ -40,7 +40,8 @@
 // length (unit keys: page "Exercices", Niveau 2 Q9; the low-rank W_alpha and
 // W_beta that produce a and b: page "Retrouver les 2,8 T de paramètres",
 // Bloc 4).  The squared norms are summed over the 16 lanes of a token group
-// by DPP moves and across waves through LDS that phase 2 later reuses.
+// by DPP moves; each thread then adds the channel sets' partials of its own
+// tokens from LDS that phase 2 later reuses.
 #include "launch.h"
 #include "twopass.h"
 
@@ -101,9 +102,8 @@ struct PrepCfg {
     static constexpr size_t BYTES = O_TOT + (size_t)NTS * DK * 4;
     static_assert(BYTES <= 160 * 1024, "LDS");
     // FUSED: partial squared norms of k and q per channel set, [2][NWC][CH]
-    // fp32, on the L blocks, and the inverse norms, [2][CH], on the L^{-1} blocks
+    // fp32, on the L blocks
     static_assert(!FUSED || 2 * NWC * CH * 4 <= NPAIR * BLK * 4, "norm scratch");
-    static_assert(!FUSED || (2 * CH * 4 <= NPAIR * BLK * 4 && CH <= 64 && NW >= 2), "inverse norms");
     // waves per SIMD the LDS allows (2 workgroups of 8 waves per CU at 80 KB
     // or less): the register budget is held to match
     static constexpr int WPE = BYTES <= 80 * 1024 ? (2 * NTHR / 64 + 3) / 4 : 1;
@@ -330,16 +330,21 @@ void chunk_prep_kernel(PrepParams p) {
             }
         st4(gam + c0, exp2_fast(GC[0]), exp2_fast(GC[1]), exp2_fast(GC[2]), exp2_fast(GC[3]));
     }
-    float* sInv = sZ;  // FUSED: [2][CH] inverse norms (on the L^{-1} blocks, unused until phase 3)
+    // FUSED: each thread sums the channel-set partials of its own tokens (the
+    // barrier above has made them visible), with no further exchange
+    float ik[TPT], iq[TPT];
     if constexpr (C::FUSED) {
-        // waves 0 and 1 sum the partials of k and q, one token per lane
-        if (wave < 2 && lane < CH) {
-            float s2 = 0.f;
 #pragma unroll
-            for (int w = 0; w < C::NWC; ++w) s2 += sNorm[(wave * C::NWC + w) * CH + lane];
-            sInv[wave * CH + lane] = rsqrtf(s2 + kNormEps);
+        for (int i = 0; i < TPT; ++i) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < C::NWC; ++w) {
+                sk += sNorm[w * CH + tl0 + i];
+                sq += sNorm[(C::NWC + w) * CH + tl0 + i];
+            }
+            ik[i] = rsqrtf(sk + kNormEps);
+            iq[i] = rsqrtf(sq + kNormEps);
         }
-        barrier_keep_loads();
     }
     // two exponentials per element, e^{G - R} <= 1 and e^{R - G} <= e^80 (R the
     // sub-tile reference); e^G and e^{G_C - G} follow by per-channel factors
@@ -359,8 +364,8 @@ void chunk_prep_kernel(PrepParams p) {
         const int t = tl0 + i;
         f32x4_t kx = cvt4(rk[i]), qx = cvt4(rq[i]);
         if constexpr (C::FUSED) {
-            kx *= sInv[t];
-            qx *= sInv[CH + t];
+            kx *= ik[i];
+            qx *= iq[i];
         }
         f32x4_t kr, qr, kc, qt, kg;
 #pragma unroll
