@@ -89,9 +89,9 @@ struct PrepCfg {
     static constexpr size_t SZ_X1 = 3 * SZ_TAB;                       // Kr, Qr, Kc
     static constexpr size_t SZ_KVT = al((size_t)DK * LC * sizeof(T));  // Kt^T
     static constexpr size_t SZ_LB = al((size_t)CH * LC * sizeof(T));
-    static constexpr size_t SZ_X2 = SZ_KVT + SZ_LB;                    // after the Gram
+    static constexpr size_t SZ_X2 = 2 * SZ_KVT + SZ_LB;                // after the Gram: Kt^T, Tb, Kh^T
     static constexpr size_t O_KR = 0, O_QR = SZ_TAB, O_KC = 2 * SZ_TAB;
-    static constexpr size_t O_KTT = 0, O_LB = SZ_KVT;
+    static constexpr size_t O_KTT = 0, O_LB = SZ_KVT, O_KHT = SZ_KVT + SZ_LB;
     static constexpr size_t SZ_X = al(SZ_X1 > SZ_X2 ? SZ_X1 : SZ_X2);
     static constexpr size_t O_L = SZ_X;                         // blocks of beta A
     static constexpr size_t O_Z = O_L + (size_t)NPAIR * BLK * 4;  // blocks of L^{-1}
@@ -149,6 +149,7 @@ void chunk_prep_kernel(PrepParams p) {
     T* sKc = reinterpret_cast<T*>(smem + C::O_KC);
     T* sKtT = reinterpret_cast<T*>(smem + C::O_KTT);
     T* sLB = reinterpret_cast<T*>(smem + C::O_LB);
+    T* sKhT = reinterpret_cast<T*>(smem + C::O_KHT);
     float* sL = reinterpret_cast<float*>(smem + C::O_L);
     float* sZ = reinterpret_cast<float*>(smem + C::O_Z);
     float* sD = reinterpret_cast<float*>(smem + C::O_D);
@@ -357,7 +358,7 @@ void chunk_prep_kernel(PrepParams p) {
         eCR[ch] = exp2_fast(GC[ch] - Ro[ch]);
         sR[ch] = scale * eR[ch];
     }
-    f32x4_t kh[TPT];
+    T4 kh[TPT];  // K e^{G_C - G}, the rows of Kh^T, in the storage type until phase 3
     T4 kw[TPT];  // K e^G, the W operand, in the storage type until phase 3
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -367,7 +368,7 @@ void chunk_prep_kernel(PrepParams p) {
             kx *= ik[i];
             qx *= iq[i];
         }
-        f32x4_t kr, qr, kc, qt, kg;
+        f32x4_t kr, qr, kc, qt, kg, kx2;
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
             const float d = G[i][ch] - RoL[ch];
@@ -377,40 +378,15 @@ void chunk_prep_kernel(PrepParams p) {
             qr[ch] = qx[ch] * er;
             kc[ch] = kx[ch] * ec;
             qt[ch] = qr[ch] * sR[ch];         // scale q e^G
-            kh[i][ch] = kc[ch] * eCR[ch];     // k e^{G_C - G}
+            kx2[ch] = kc[ch] * eCR[ch];       // k e^{G_C - G}
             kg[ch] = kr[ch] * eR[ch];         // k e^G
         }
         kw[i] = pack4<T>(kg[0], kg[1], kg[2], kg[3]);
+        kh[i] = pack4<T>(kx2[0], kx2[1], kx2[2], kx2[3]);
         st4(sKr + t * LK + c0, kr[0], kr[1], kr[2], kr[3]);
         st4(sQr + t * LK + c0, qr[0], qr[1], qr[2], qr[3]);
         st4(sKc + t * LK + c0, kc[0], kc[1], kc[2], kc[3]);
         st4(Qt + frag_elem<K>((c0 / K::KB) * NT + t / 16, t, c0), qt[0], qt[1], qt[2], qt[3]);
-    }
-    // Kh^T rows: TPT consecutive tokens of each of the thread's channels
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-        const int c = c0 + ch;
-        if constexpr (TPT >= 4) {
-#pragma unroll
-            for (int r = 0; r < TPT; r += 4) {
-                const int t = tl0 + r;
-                st4(KhT + frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t), kh[r][ch], kh[r + 1][ch],
-                    kh[r + 2][ch], kh[r + 3][ch]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                const int t = tl0 + i;
-                KhT[frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t)] = from_f32<T>(kh[i][ch]);
-            }
-        }
-    }
-    // zero padding of Kh^T past C (k-blocks over tokens)
-    if constexpr (CP > CH) {
-        for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
-            const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
-            KhT[frag_elem<K>((c / 16) * C::NKT + t / K::KB, c, t)] = from_f32<T>(0.f);
-        }
     }
     barrier_keep_loads();
 
@@ -462,23 +438,30 @@ void chunk_prep_kernel(PrepParams p) {
     }
     barrier_keep_loads();
 
-    // ---- 3. operand of W; inverse of L ---------------------------------------
+    // ---- 3. operand of W and the Kh^T table; inverse of L --------------------
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
         T* kt = sKtT + (c0 + ch) * LC + tl0;
+        T* kb = sKhT + (c0 + ch) * LC + tl0;
         if constexpr (TPT % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < TPT; i += 4)
+            for (int i = 0; i < TPT; i += 4) {
                 *reinterpret_cast<T4*>(kt + i) = T4{kw[i][ch], kw[i + 1][ch], kw[i + 2][ch], kw[i + 3][ch]};
+                *reinterpret_cast<T4*>(kb + i) = T4{kh[i][ch], kh[i + 1][ch], kh[i + 2][ch], kh[i + 3][ch]};
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) kt[i] = kw[i][ch];
+            for (int i = 0; i < TPT; ++i) {
+                kt[i] = kw[i][ch];
+                kb[i] = kh[i][ch];
+            }
         }
     }
     if constexpr (CP > CH) {
         for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
             const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
             sKtT[c * LC + t] = from_f32<T>(0.f);
+            sKhT[c * LC + t] = from_f32<T>(0.f);
         }
     }
     if (wave < NT) {  // diagonal block `wave`, one column per lane (lanes >= 16 repeat)
@@ -566,6 +549,30 @@ void chunk_prep_kernel(PrepParams p) {
                     }
                     ++f;
                 }
+    }
+    // Kh^T fragments (channel tile ct, k-block u over tokens): lane (row r,
+    // group g) holds element e at token u KB + k, pos(k) = g KB/4 + e; runs of
+    // four consecutive tokens are consecutive elements, so the lane reads its
+    // runs from the table and stores its 16 bytes at once
+    {
+        constexpr int KPL = K::KB / 4;
+        for (int f = wave; f < NCT * C::NKT; f += NW) {
+            const int ct = f / C::NKT, u = f % C::NKT;
+            const T* row = sKhT + (16 * ct + l16) * LC + u * K::KB;
+            typename K::Frag x;
+#pragma unroll
+            for (int r = 0; r < KPL / 4; ++r) {
+                // the run holding element 4 r of this lane: token k with pos(k) = g4 KPL + 4 r
+                int k = 0;
+#pragma unroll
+                for (int kk = 0; kk < K::KB; kk += 4)
+                    if (K::pos(kk) == g4 * KPL + 4 * r) k = kk;
+                const T4 v = *reinterpret_cast<const T4*>(row + k);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) K::set(x, 4 * r + e, v[e]);
+            }
+            *reinterpret_cast<typename K::Frag*>(KhT + (f * 64 + lane) * KPL) = x;
+        }
     }
     // A wave owns channel tile ct of W: its operand along the tokens is loaded
     // once, and each fragment of Tb is the B operand of W^T.
