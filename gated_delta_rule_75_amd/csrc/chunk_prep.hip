@@ -439,29 +439,41 @@ void chunk_prep_kernel(PrepParams p) {
     barrier_keep_loads();
 
     // ---- 3. operand of W and the Kh^T table; inverse of L --------------------
+    // In the [channel][token] tables the 16-byte unit x of row c sits at unit
+    // x ^ ((c >> 3) & SWM): the rows four channels apart that one write
+    // instruction covers then fall on different banks (bank conflicts of these
+    // writes were most of pass 1's), while a fragment read still takes whole
+    // units of eight consecutive rows
+    constexpr int TU = 16 / (int)sizeof(T);   // tokens per 16-byte unit
+    constexpr int NU = CP / TU;
+    static_assert((NU & (NU - 1)) == 0, "units per row");
+    constexpr int SWM = (NU < 8 ? NU : 8) - 1;
+    auto tcol = [](int c, int t) { return ((t / TU) ^ ((c >> 3) & SWM)) * TU + t % TU; };
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-        T* kt = sKtT + (c0 + ch) * LC + tl0;
-        T* kb = sKhT + (c0 + ch) * LC + tl0;
+        const int c = c0 + ch;
+        T* kt = sKtT + c * LC;
+        T* kb = sKhT + c * LC;
         if constexpr (TPT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < TPT; i += 4) {
-                *reinterpret_cast<T4*>(kt + i) = T4{kw[i][ch], kw[i + 1][ch], kw[i + 2][ch], kw[i + 3][ch]};
-                *reinterpret_cast<T4*>(kb + i) = T4{kh[i][ch], kh[i + 1][ch], kh[i + 2][ch], kh[i + 3][ch]};
+                const int x = tcol(c, tl0 + i);   // four tokens inside one unit
+                *reinterpret_cast<T4*>(kt + x) = T4{kw[i][ch], kw[i + 1][ch], kw[i + 2][ch], kw[i + 3][ch]};
+                *reinterpret_cast<T4*>(kb + x) = T4{kh[i][ch], kh[i + 1][ch], kh[i + 2][ch], kh[i + 3][ch]};
             }
         } else {
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
-                kt[i] = kw[i][ch];
-                kb[i] = kh[i][ch];
+                kt[tcol(c, tl0 + i)] = kw[i][ch];
+                kb[tcol(c, tl0 + i)] = kh[i][ch];
             }
         }
     }
     if constexpr (CP > CH) {
         for (int idx = tid; idx < DK * (CP - CH); idx += NTHR) {
             const int c = idx / (CP - CH), t = CH + idx % (CP - CH);
-            sKtT[c * LC + t] = from_f32<T>(0.f);
-            sKhT[c * LC + t] = from_f32<T>(0.f);
+            sKtT[c * LC + tcol(c, t)] = from_f32<T>(0.f);
+            sKhT[c * LC + tcol(c, t)] = from_f32<T>(0.f);
         }
     }
     if (wave < NT) {  // diagonal block `wave`, one column per lane (lanes >= 16 repeat)
@@ -558,7 +570,8 @@ void chunk_prep_kernel(PrepParams p) {
         constexpr int KPL = K::KB / 4;
         for (int f = wave; f < NCT * C::NKT; f += NW) {
             const int ct = f / C::NKT, u = f % C::NKT;
-            const T* row = sKhT + (16 * ct + l16) * LC + u * K::KB;
+            const int rc = 16 * ct + l16;
+            const T* row = sKhT + rc * LC;
             typename K::Frag x;
 #pragma unroll
             for (int r = 0; r < KPL / 4; ++r) {
@@ -567,7 +580,7 @@ void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int kk = 0; kk < K::KB; kk += 4)
                     if (K::pos(kk) == g4 * KPL + 4 * r) k = kk;
-                const T4 v = *reinterpret_cast<const T4*>(row + k);
+                const T4 v = *reinterpret_cast<const T4*>(row + tcol(rc, u * K::KB + k));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) K::set(x, 4 * r + e, v[e]);
             }
@@ -581,7 +594,12 @@ void chunk_prep_kernel(PrepParams p) {
         for (int ct = wave; ct < NCT; ct += NW) {
             typename E::Frag fk[NKK];
 #pragma unroll
-            for (int s = 0; s < NKK; ++s) fk[s] = lds_frag<E>(sKtT, LC, 16 * ct, s * E::KSTEP, lane);
+            for (int s = 0; s < NKK; ++s) {
+                // lds_frag's element order on the swizzled table: E::KPL consecutive
+                // tokens from a 16-byte boundary lie inside one unit
+                const int rc = 16 * ct + l16, t = s * E::KSTEP + E::KPL * g4;
+                fk[s] = *reinterpret_cast<const typename E::Frag*>(sKtT + rc * LC + tcol(rc, t));
+            }
 #pragma unroll
             for (int ta = 0; ta < NT; ++ta) {
                 f32x4_t aw = {0.f, 0.f, 0.f, 0.f};
