@@ -76,7 +76,7 @@ struct StCfg {
     using T = typename K::T;
     static constexpr int DK = DK_, DV = DV_, CH = CH_, NVT = NVT_, MODE = MODE_;
     static constexpr bool AUG = MODE_ == kModePairs;
-    static constexpr int NW = 4;
+    static constexpr int NW = 4;                        // compute waves
     static constexpr int CW = 16 * NVT * NW;            // state columns per workgroup
     static constexpr int NTT = CH / 16, NCT = DK / 16;
     static constexpr int KB = K::KB, TPB = K::TPB;
@@ -146,6 +146,12 @@ struct StCfg {
     // on its own; with the copies dealt round-robin, two, three and four
     // loaders reach 324, 317 and 314 us on the 96-head layer)
     static constexpr int NLW = LW ? 4 : 0;
+    // group 1 of the loaders' copies staged through registers two chunks
+    // ahead: the single-sequence and varlen scans, whose few workgroups wait
+    // on memory latency (K3 layer: pass 2 372 -> 327 us); the KCP outputs,
+    // eight rounds of workgroups that keep HBM busy, keep the direct copies
+    // (4.00 against 3.86 ms a call with registers)
+    static constexpr bool LWREG = LW && (MODE == kModeSeq || MODE == kModeVarlen);
     static constexpr int NCOPY = NF + NVC;                   // 1 KiB copies per chunk (LW)
     static constexpr int NTHR = 64 * (NW + NLW);
 };
@@ -169,6 +175,9 @@ template <class C>
 __device__ __forceinline__ int vswz(int row) {
     return ((row / (C::KB / 4)) & 3) * (int)sizeof(typename C::T);
 }
+
+// 16 bytes as a native vector (arrays of it stay in registers)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 
     if constexpr (C::LW) {
         if (wave >= NW) {
-            // ---- loader waves: chunk c+1 into buffer (c+1) % 2 during chunk c ----
+            // ---- loader waves: the operands of chunk c+1 into buffer (c+1) % 2 during chunk c ----
             constexpr int FB = 64 * KPL * (int)sizeof(T);   // bytes of one fragment (1 KiB)
             static_assert(FB == 1024, "fragment size");
             const char* wn = static_cast<const char*>(p.ws.wn) + 16 * lane;
@@ -245,70 +254,172 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             constexpr int VU = C::VRB / 16;                    // units per row
             const int vrow_l = lane / VU, vx = lane % VU;
             const int vcol_wg = vt_wg > 0 ? 16 * vt_wg : 0;
-            // copy k of a chunk: fragment k (k < NF) or v-row copy k - NF.  Two
-            // groups, each with a barrier of its own: group 1 (v rows, T and Wn,
-            // the operands of Delta) and group 2 (gam, Kh^T, Qt, Pm), whose last
-            // copies land while Delta is formed.  The v rows, private to the
-            // workgroup and so never in L2 already, go out first; the copies
-            // of a group are dealt to the loaders in turn.
-            const int li = wave - NW;
-            constexpr int NU = C::NCOPY - C::NF;
-            constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
-            auto stage_group = [&](int c, int b, auto G) {
-                const int64_t wsb = (int64_t)(cws + c) * H + h;
-                char* buf = smem + b * C::BUF;
-                const char* aw = wn + wsb * (int64_t)(CH * DK * sizeof(T));
-                const char* aq = qt + wsb * (int64_t)(CH * DK * sizeof(T));
-                const char* ak = kh + wsb * (int64_t)(DK * CP * sizeof(T));
-                const char* ap = pm + wsb * (int64_t)(C::NPM * FB);
-                const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
-                const char* at = tt + wsb * (int64_t)(C::NPM * FB);
-                const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
-                constexpr int NJ = decltype(G)::value == 1 ? NG1 : NG2;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    if (j % C::NLW != li) continue;
-                    int k;
-                    if constexpr (decltype(G)::value == 1) k = j < NU ? C::NF + j : C::F_W + j - NU;  // v, Wn, T
-                    else k = j == 0 ? C::F_G : j <= C::N_K ? C::F_K + j - 1 : j <= C::N_K + C::N_Q ? C::F_Q + j - 1 - C::N_K
-                                                                                            : C::F_P + j - 1 - C::N_K - C::N_Q;
-                    const char* src;
-                    if (k < C::F_T0) src = aw + (k - C::F_W) * FB;
-                    else if (k < C::F_Q) src = at + (k - C::F_T0) * FB;
-                    else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
-                    else if (k < C::F_P) src = ak + (k - C::F_K) * FB;
-                    else if (k < C::F_G) src = ap + (k - C::F_P) * FB;
-                    else if (k == C::F_G) src = ag;
-                    else {
-                        // v row of this lane (rows past the chunk's end repeat its last one)
-                        int row = (k - C::NF) * C::VRPC + vrow_l;
-                        row = row < nv ? row : nv - 1;
-                        src = reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
-                              16 * (vx ^ vswz<C>(row));
+            if constexpr (C::LWREG) {
+                // copy j of a chunk (1 KiB): the v rows first (private to the
+                // workgroup, so never in L2 already), then Wn, T, gam, Kh^T, Qt, Pm;
+                // LDS slot k of copy j: fragment k, or v-row copy k - NF.  The copies
+                // are dealt to the loaders in turn.  Group 1 (v, Wn, T: the operands
+                // of Delta, needed at the top of a chunk) goes through registers:
+                // its loads for chunk c+2 go out at the top of chunk c and land in
+                // LDS buffer (c+2) % 2 after the middle barrier of chunk c+1, about
+                // one and a half chunks later.  Group 2 (gam, Kh^T, Qt, Pm, needed
+                // after the middle barrier) is copied straight into LDS after the
+                // middle barrier of the chunk before.
+                constexpr int NU = C::NCOPY - C::NF;
+                constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
+                constexpr int P1MIN = NG1 / C::NLW;
+                static_assert(P1MIN + NG2 / C::NLW <= 63, "vmcnt range");
+                auto src_of = [&](int c, int k) __attribute__((always_inline)) -> const char* {
+                    const int64_t wsb = (int64_t)(cws + c) * H + h;
+                    if (k < C::F_T0) return wn + wsb * (int64_t)(CH * DK * sizeof(T)) + (k - C::F_W) * FB;
+                    if (k < C::F_Q) return tt + wsb * (int64_t)(C::NPM * FB) + (k - C::F_T0) * FB;
+                    if (k < C::F_K) return qt + wsb * (int64_t)(CH * DK * sizeof(T)) + (k - C::F_Q) * FB;
+                    if (k < C::F_P) return kh + wsb * (int64_t)(DK * CP * sizeof(T)) + (k - C::F_K) * FB;
+                    if (k < C::F_G) return pm + wsb * (int64_t)(C::NPM * FB) + (k - C::F_P) * FB;
+                    if (k == C::F_G) return gm + wsb * (int64_t)(DK * sizeof(float));
+                    // v row of this lane (rows past the chunk's end repeat its last one)
+                    const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+                    int row = (k - C::NF) * C::VRPC + vrow_l;
+                    row = row < nv ? row : nv - 1;
+                    return reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
+                           16 * (vx ^ vswz<C>(row));
+                };
+                // the loader's program, with its index LI a constant, so that each
+                // copy's slot, source array and register fold at compile time
+                auto loader = [&](auto LI) __attribute__((always_inline)) {
+                    constexpr int li = decltype(LI)::value;
+                    constexpr int P1 = (NG1 - li + C::NLW - 1) / C::NLW;   // group-1 copies of this loader
+                    constexpr auto kslot = [](int j) -> int {
+                        if (j < NU) return C::NF + j;                     // v rows
+                        j -= NU;
+                        if (j < C::N_W + C::N_T) return C::F_W + j;       // Wn, then T
+                        j -= C::N_W + C::N_T;
+                        if (j == 0) return C::F_G;
+                        if (j <= C::N_K) return C::F_K + j - 1;
+                        if (j <= C::N_K + C::N_Q) return C::F_Q + j - 1 - C::N_K;
+                        return C::F_P + j - 1 - C::N_K - C::N_Q;
+                    };
+                    auto load_g1 = [&](int c, u32x4_t (&r)[P1]) __attribute__((always_inline)) {
+    #pragma unroll
+                        for (int i = 0; i < P1; ++i)
+                            r[i] = *reinterpret_cast<const u32x4_t*>(src_of(c, kslot(li + C::NLW * i)));
+                    };
+                    auto write_g1 = [&](int b, const u32x4_t (&r)[P1]) __attribute__((always_inline)) {
+                        char* buf = smem + b * C::BUF;
+    #pragma unroll
+                        for (int i = 0; i < P1; ++i)
+                            *reinterpret_cast<u32x4_t*>(buf + kslot(li + C::NLW * i) * 1024 + 16 * lane) = r[i];
+                    };
+                    auto copy_g2 = [&](int c, int b) __attribute__((always_inline)) {
+                        char* buf = smem + b * C::BUF;
+    #pragma unroll
+                        for (int j = NG1; j < C::NCOPY; ++j)
+                            if (j % C::NLW == li) lds_dma16(src_of(c, kslot(j)), buf + kslot(j) * 1024);
+                    };
+                    u32x4_t ra[P1], rb[P1];
+                    // chunk c: rc is free (chunk c's group 1 is in LDS), rn holds the
+                    // loads of chunk c+1's group 1
+                    auto step = [&](int c, u32x4_t (&rc)[P1], u32x4_t (&rn)[P1]) __attribute__((always_inline)) {
+                        barrier_keep_loads();       // chunk c's group 1 is in LDS; the compute waves are done with chunk c-1
+                        if (c + 2 < nch) {
+                            load_g1(c + 2, rc);
+                            wait_vmcnt<P1MIN>();    // group 2 of chunk c, and group 1 of chunk c+1, have landed
+                        } else {
+                            wait_vmcnt<0>();
+                        }
+                        barrier_keep_loads();       // group 2 of chunk c is in LDS
+                        if (c + 1 < nch) {
+                            write_g1((c + 1) % 2, rn);
+                            copy_g2(c + 1, (c + 1) % 2);
+                        }
+                    };
+                    if (nch > 0) {
+                        load_g1(0, ra);
+                        copy_g2(0, 0);
+                        if (nch > 1) load_g1(1, rb);
+                        // group 1 of chunk 0 (group 2 of chunk 0 and group 1 of chunk 1 may be in flight)
+                        if (nch > 1) wait_vmcnt<P1MIN + NG2 / C::NLW>();
+                        else wait_vmcnt<NG2 / C::NLW>();
+                        write_g1(0, ra);
                     }
-                    lds_dma16(src, buf + k * 1024);
+                    for (int c = 0; c < nch; c += 2) {
+                        step(c, ra, rb);
+                        if (c + 1 < nch) step(c + 1, rb, ra);
+                    }
+                };
+                static_assert(C::NLW == 4, "loader count");
+                switch (wave - NW) {
+                    case 0: loader(std::integral_constant<int, 0>{}); break;
+                    case 1: loader(std::integral_constant<int, 1>{}); break;
+                    case 2: loader(std::integral_constant<int, 2>{}); break;
+                    default: loader(std::integral_constant<int, 3>{}); break;
                 }
-            };
-            using G1 = std::integral_constant<int, 1>;
-            using G2 = std::integral_constant<int, 2>;
-            // copies of a group that every loader issues at least
-            constexpr int M1 = NG1 / C::NLW, M2 = NG2 / C::NLW;
-            static_assert(M1 <= 63 && M2 <= 63, "vmcnt range");
-            if (nch > 0) {
-                stage_group(0, 0, G1{});
-                stage_group(0, 0, G2{});
-            }
-            for (int c = 0; c < nch; ++c) {
-                wait_vmcnt<M2>();           // group 1 of chunk c has landed (group 2 may be in flight)
-                barrier_keep_loads();       // ... and the compute waves are done with chunk c-1
-                if (c + 1 < nch) {
-                    stage_group(c + 1, (c + 1) % 2, G1{});
-                    wait_vmcnt<M1>();       // group 2 of chunk c (group 1 of c+1 may be in flight)
-                } else {
-                    wait_vmcnt<0>();
+            } else {
+                // copy k of a chunk: fragment k (k < NF) or v-row copy k - NF.  Two
+                // groups, each with a barrier of its own: group 1 (v rows, T and Wn,
+                // the operands of Delta) and group 2 (gam, Kh^T, Qt, Pm), whose last
+                // copies land while Delta is formed.  The v rows, private to the
+                // workgroup and so never in L2 already, go out first; the copies
+                // of a group are dealt to the loaders in turn.
+                const int li = wave - NW;
+                constexpr int NU = C::NCOPY - C::NF;
+                constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
+                auto stage_group = [&](int c, int b, auto G) {
+                    const int64_t wsb = (int64_t)(cws + c) * H + h;
+                    char* buf = smem + b * C::BUF;
+                    const char* aw = wn + wsb * (int64_t)(CH * DK * sizeof(T));
+                    const char* aq = qt + wsb * (int64_t)(CH * DK * sizeof(T));
+                    const char* ak = kh + wsb * (int64_t)(DK * CP * sizeof(T));
+                    const char* ap = pm + wsb * (int64_t)(C::NPM * FB);
+                    const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
+                    const char* at = tt + wsb * (int64_t)(C::NPM * FB);
+                    const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+                    constexpr int NJ = decltype(G)::value == 1 ? NG1 : NG2;
+    #pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        if (j % C::NLW != li) continue;
+                        int k;
+                        if constexpr (decltype(G)::value == 1) k = j < NU ? C::NF + j : C::F_W + j - NU;  // v, Wn, T
+                        else k = j == 0 ? C::F_G : j <= C::N_K ? C::F_K + j - 1 : j <= C::N_K + C::N_Q ? C::F_Q + j - 1 - C::N_K
+                                                                                                : C::F_P + j - 1 - C::N_K - C::N_Q;
+                        const char* src;
+                        if (k < C::F_T0) src = aw + (k - C::F_W) * FB;
+                        else if (k < C::F_Q) src = at + (k - C::F_T0) * FB;
+                        else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
+                        else if (k < C::F_P) src = ak + (k - C::F_K) * FB;
+                        else if (k < C::F_G) src = ap + (k - C::F_P) * FB;
+                        else if (k == C::F_G) src = ag;
+                        else {
+                            // v row of this lane (rows past the chunk's end repeat its last one)
+                            int row = (k - C::NF) * C::VRPC + vrow_l;
+                            row = row < nv ? row : nv - 1;
+                            src = reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
+                                  16 * (vx ^ vswz<C>(row));
+                        }
+                        lds_dma16(src, buf + k * 1024);
+                    }
+                };
+                using G1 = std::integral_constant<int, 1>;
+                using G2 = std::integral_constant<int, 2>;
+                // copies of a group that every loader issues at least
+                constexpr int M1 = NG1 / C::NLW, M2 = NG2 / C::NLW;
+                static_assert(M1 <= 63 && M2 <= 63, "vmcnt range");
+                if (nch > 0) {
+                    stage_group(0, 0, G1{});
+                    stage_group(0, 0, G2{});
                 }
-                barrier_keep_loads();       // group 2 of chunk c is in LDS
-                if (c + 1 < nch) stage_group(c + 1, (c + 1) % 2, G2{});
+                for (int c = 0; c < nch; ++c) {
+                    wait_vmcnt<M2>();           // group 1 of chunk c has landed (group 2 may be in flight)
+                    barrier_keep_loads();       // ... and the compute waves are done with chunk c-1
+                    if (c + 1 < nch) {
+                        stage_group(c + 1, (c + 1) % 2, G1{});
+                        wait_vmcnt<M1>();       // group 2 of chunk c (group 1 of c+1 may be in flight)
+                    } else {
+                        wait_vmcnt<0>();
+                    }
+                    barrier_keep_loads();       // group 2 of chunk c is in LDS
+                    if (c + 1 < nch) stage_group(c + 1, (c + 1) % 2, G2{});
+                }
             }
             if constexpr (!C::AUG) {
                 if (nch > 0) barrier_keep_loads();   // matches the compute waves' last y hand-off
@@ -460,18 +571,18 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     };
     const int vcw = vcol0 - wave * 16 * NVT;   // first value column of the workgroup
     static_assert(!C::LW || ZJW <= 2, "z rows per wave");
-    uint4 zrow0 = {0, 0, 0, 0}, zrow1 = {0, 0, 0, 0};   // rows in flight (copies wave, wave + NW)
-    auto zrow_src = [&](int c, int jj) -> const uint4* {
+    u32x4_t zrow[ZJW > 0 ? ZJW : 1];   // rows in flight (copies wave, wave + NW, ...)
+    auto zrow_src = [&](int c, int jj) -> const u32x4_t* {
         const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
         int t, x;
         zpos(jj * NW + wave, t, x);
         t = t < nv ? t : nv - 1;
-        return reinterpret_cast<const uint4*>(
+        return reinterpret_cast<const u32x4_t*>(
             reinterpret_cast<const char*>(gz + ((t0 + (int64_t)c * CH + t) * H + h) * DV + vcw) + 16 * x);
     };
     auto load_zrows = [&](int c) {
-        if constexpr (ZJW >= 1) zrow0 = *zrow_src(c, 0);
-        if constexpr (ZJW >= 2) zrow1 = *zrow_src(c, 1);
+#pragma unroll
+        for (int jj = 0; jj < ZJW; ++jj) zrow[jj] = *zrow_src(c, jj);
     };
     auto store_yrows = [&](int c) {
         const char* yt = smem + C::O_Y;
@@ -481,7 +592,6 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             const int j = jj * NW + wave;
             int t, x;
             zpos(j, t, x);
-            typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(yt + j * 1024 + 16 * lane);
             // written once, read by nobody here: stored past the caches
             if (t < nv)
@@ -559,8 +669,9 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         if constexpr (C::LW && !C::AUG) {
             if (gz) {   // this wave's z rows of chunk c into the z tile
                 char* zt = smem + C::O_Z;
-                if constexpr (ZJW >= 1) *reinterpret_cast<uint4*>(zt + wave * 1024 + 16 * lane) = zrow0;
-                if constexpr (ZJW >= 2) *reinterpret_cast<uint4*>(zt + (NW + wave) * 1024 + 16 * lane) = zrow1;
+#pragma unroll
+                for (int jj = 0; jj < ZJW; ++jj)
+                    *reinterpret_cast<u32x4_t*>(zt + (jj * NW + wave) * 1024 + 16 * lane) = zrow[jj];
             }
         }
         const int nvalid = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
