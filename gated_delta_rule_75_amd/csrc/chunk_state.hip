@@ -260,11 +260,11 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                 // LDS slot k of copy j: fragment k, or v-row copy k - NF.  The copies
                 // are dealt to the loaders in turn.  Group 1 (v, Wn, T: the operands
                 // of Delta, needed at the top of a chunk) goes through registers:
-                // its loads for chunk c+2 go out at the top of chunk c and land in
-                // LDS buffer (c+2) % 2 after the middle barrier of chunk c+1, about
-                // one and a half chunks later.  Group 2 (gam, Kh^T, Qt, Pm, needed
-                // after the middle barrier) is copied straight into LDS after the
-                // middle barrier of the chunk before.
+                // its loads for chunk c+3 go out after the middle barrier of chunk
+                // c and are written into LDS buffer (c+3) % 2 after the middle
+                // barrier of chunk c+2, two chunks later.  Group 2 (gam, Kh^T, Qt,
+                // Pm, needed after the middle barrier) is copied straight into LDS
+                // after the middle barrier of the chunk before.
                 constexpr int NU = C::NCOPY - C::NF;
                 constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
                 constexpr int P1MIN = NG1 / C::NLW;
@@ -300,51 +300,51 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                         return C::F_P + j - 1 - C::N_K - C::N_Q;
                     };
                     auto load_g1 = [&](int c, u32x4_t (&r)[P1]) __attribute__((always_inline)) {
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < P1; ++i)
                             r[i] = *reinterpret_cast<const u32x4_t*>(src_of(c, kslot(li + C::NLW * i)));
                     };
                     auto write_g1 = [&](int b, const u32x4_t (&r)[P1]) __attribute__((always_inline)) {
                         char* buf = smem + b * C::BUF;
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < P1; ++i)
                             *reinterpret_cast<u32x4_t*>(buf + kslot(li + C::NLW * i) * 1024 + 16 * lane) = r[i];
                     };
                     auto copy_g2 = [&](int c, int b) __attribute__((always_inline)) {
                         char* buf = smem + b * C::BUF;
-    #pragma unroll
+#pragma unroll
                         for (int j = NG1; j < C::NCOPY; ++j)
                             if (j % C::NLW == li) lds_dma16(src_of(c, kslot(j)), buf + kslot(j) * 1024);
                     };
                     u32x4_t ra[P1], rb[P1];
-                    // chunk c: rc is free (chunk c's group 1 is in LDS), rn holds the
-                    // loads of chunk c+1's group 1
-                    auto step = [&](int c, u32x4_t (&rc)[P1], u32x4_t (&rn)[P1]) __attribute__((always_inline)) {
-                        barrier_keep_loads();       // chunk c's group 1 is in LDS; the compute waves are done with chunk c-1
-                        if (c + 2 < nch) {
-                            load_g1(c + 2, rc);
-                            wait_vmcnt<P1MIN>();    // group 2 of chunk c, and group 1 of chunk c+1, have landed
-                        } else {
-                            wait_vmcnt<0>();
-                        }
+                    // chunk c; rw holds the loads of group 1 of chunk c+1, and
+                    // takes those of chunk c+3 once they are in LDS.  A load of
+                    // group 1 goes out after the copies of the chunk before's
+                    // group 2, so the wait for those does not wait for it.
+                    auto step = [&](int c, u32x4_t (&rw)[P1]) __attribute__((always_inline)) {
+                        barrier_keep_loads();       // group 1 of chunk c is in LDS; the compute waves are done with chunk c-1
+                        if (c + 2 < nch) wait_vmcnt<P1MIN>();   // group 2 of chunk c and group 1 of chunk c+1 have landed
+                        else wait_vmcnt<0>();
                         barrier_keep_loads();       // group 2 of chunk c is in LDS
                         if (c + 1 < nch) {
-                            write_g1((c + 1) % 2, rn);
+                            write_g1((c + 1) % 2, rw);
                             copy_g2(c + 1, (c + 1) % 2);
+                            if (c + 3 < nch) load_g1(c + 3, rw);
                         }
                     };
                     if (nch > 0) {
                         load_g1(0, ra);
-                        copy_g2(0, 0);
                         if (nch > 1) load_g1(1, rb);
-                        // group 1 of chunk 0 (group 2 of chunk 0 and group 1 of chunk 1 may be in flight)
+                        copy_g2(0, 0);
+                        // group 1 of chunk 0 (group 1 of chunk 1 and group 2 of chunk 0 may be in flight)
                         if (nch > 1) wait_vmcnt<P1MIN + NG2 / C::NLW>();
                         else wait_vmcnt<NG2 / C::NLW>();
                         write_g1(0, ra);
+                        if (nch > 2) load_g1(2, ra);
                     }
                     for (int c = 0; c < nch; c += 2) {
-                        step(c, ra, rb);
-                        if (c + 1 < nch) step(c + 1, rb, ra);
+                        step(c, rb);
+                        if (c + 1 < nch) step(c + 1, ra);
                     }
                 };
                 static_assert(C::NLW == 4, "loader count");
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
                     const char* at = tt + wsb * (int64_t)(C::NPM * FB);
                     const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
                     constexpr int NJ = decltype(G)::value == 1 ? NG1 : NG2;
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < NJ; ++j) {
                         if (j % C::NLW != li) continue;
                         int k;
