@@ -678,6 +678,9 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
         // every wave's part of chunk c has landed, and every wave is done with
         // the buffer the next chunk goes to
         barrier_keep_loads();
+        // the KCP pairs have no output phase to hide their copies behind: all
+        // of the next chunk's fragments go out now, a whole chunk ahead
+        if constexpr (C::AUG && C::NBUF == 2 && !C::LW) stage(cn, nb, J_0{}, J_E{});
         // the wave's v fragments from the v rows of the chunk
         if (!ident) {
             const char* vt_rows = C::MIX ? smem + C::O_TV + C::N_T * 1024 : buf + C::NFB * 1024;
@@ -774,7 +777,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             barrier_keep_loads();                  // every wave is done with T and v of chunk c
             if (c + 1 < nch) stage_tv(c + 1);
         }
-        if constexpr (C::NBUF == 2 && !C::LW) stage(cn, nb, J_0{}, J_H{});
+        if constexpr (C::NBUF == 2 && !C::LW && !C::AUG) stage(cn, nb, J_0{}, J_H{});
         Frag df[NKT][NVT];
 #pragma unroll
         for (int u = 0; u < NKT; ++u)
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             }
         }
         if constexpr (C::NBUF == 2) {
-            if constexpr (!C::LW) stage(cn, nb, J_H{}, J_E{});
+            if constexpr (!C::LW && !C::AUG) stage(cn, nb, J_H{}, J_E{});
             if constexpr (!C::LW) load_uz(cn);
         }
         if constexpr (!C::AUG) {
