@@ -1,19 +1,20 @@
 // State scan: carries the state of every (sequence, head) through its chunks
 // with the per-chunk products the preparation kernel stored (twopass.h):
 //     Delta = U + Wn S,   O = Qt S + Pm Delta,   S <- gam * S + Kh^T Delta,
-//     y = O * sigmoid(z).
+//     y = O * sigmoid(z),
+// where U = T V is formed here, from T = L^{-1} diag(beta) and the chunk's v.
 //
 // State columns evolve independently.  A workgroup of NW waves owns
 // 16 NVT NW consecutive columns of one (sequence, head); each wave owns
 // 16 NVT of them and keeps its part of S and Delta in MFMA accumulator tiles,
 // fed back as operands straight from the lanes that hold them (the k-block
 // order of twopass.h).  The chunk operands every wave needs (Wn, Qt, Kh^T,
-// Pm, gam) are copied once per workgroup into LDS by direct global-to-LDS
-// loads, double-buffered so chunk c+1 streams in while chunk c is computed.
-// In LDS each operand fragment (16 rows x one k-block) is stored in lane
-// order, 16 bytes per lane, so that every wave reads a fragment with one
-// conflict-free 16-byte access per lane.  Without loader waves (below), U^T
-// and z, private to a wave, go straight to registers one chunk ahead.
+// Pm, T, gam) and the workgroup's rows of v are copied once per workgroup
+// into LDS, double-buffered so chunk c+1 streams in while chunk c is
+// computed.  In LDS each operand fragment (16 rows x one k-block) is stored
+// in lane order, 16 bytes per lane, so that every wave reads a fragment with
+// one conflict-free 16-byte access per lane.  Without loader waves (below),
+// z, private to a wave, goes straight to registers one chunk ahead.
 // Products (lane layout: rows 4*(l/16)+i, column l%16 of a 16x16 tile):
 //     Delta [t][v]  += Wn[t][c] . S[c][v]            A = Wn rows,   B = S
 //     O^T  [v][t]   += S^T[v][c] . Qt^T[c][t]        A = S,         B = Qt rows
@@ -26,11 +27,10 @@
 // them on one XCD, so they share the chunk operands through its L2.
 //
 // Loader waves.  When two buffers of the chunk operands plus the workgroup's
-// U^T tiles fit in LDS (one value tile per wave), four extra waves do all the
-// staging: they issue the global-to-LDS copies of chunk c+1 while chunk c is
-// computed and meet the compute waves at its barriers (two per chunk: one
-// once U^T and Wn, the operands of Delta, are in; one before the state
-// update, once the rest is).  A wave that issues a 1 KiB copy stalls until
+// v rows fit in LDS (one value tile per wave), four extra waves do all the
+// staging of chunk c+1 while chunk c is computed and meet the compute waves
+// at its barriers (two per chunk: one once v, T and Wn, the operands of
+// Delta, are in; one before the state update, once the rest is).  A wave that issues a 1 KiB copy stalls until
 // the memory pipeline takes it, so the compute waves, which now issue only
 // their z loads and y stores, no longer lose those cycles.  Those move as whole
 // 128-byte rows: right after the first barrier of chunk c each compute wave
