@@ -149,8 +149,9 @@ kda_status kda_chunk_fwd_fused(kda_dtype dt, int H, int dk, int dv, int chunk, f
  * kda_chunk_fwd_workspace_size -- bytes of device workspace with which
  * kda_chunk_fwd (and its _fused and _checkpointed forms) runs every chunk in
  * one pass of each kernel, the fastest way: per (chunk, head) about
- * 3 dk C + dv C + C^2 / 2 elements of dtype dt plus dk fp32 (70.5 KiB at bf16,
- * dk = dv = 128, C = 64), for up to T_total / chunk + num_seqs chunks.
+ * 3 dk C elements of dtype dt, the lower triangles of two C x C products in
+ * dtype dt, and dk fp32 (60.5 KiB at bf16, dk = dv = 128, C = 64), for up to
+ * T_total / chunk + num_seqs chunks.
  * Returns 0 for invalid or unsupported sizes.
  *
  * kda_chunk_fwd_workspace_min -- the smallest workspace those calls accept:
