@@ -6,8 +6,8 @@ the worst (token, head) row (tests/parity.py).
   heads (plus the chunk-scale long-memory variant).
 - The same layer through the fused-input entry point (raw q, k, gate
   pre-activations): every output and final state of all 96 heads.
-- Varlen prefill (16 sequences, lengths in [512, 8192], H=96): 48 (sequence,
-  head) chains, three heads of every sequence.
+- Varlen prefill (16 sequences, lengths in [512, 8192], H=96): 128 (sequence,
+  head) chains, eight heads of every sequence.
 - KCP scan (T=2^20, H=4, 256 segments, segment-scale long-memory draw so the
   carried state matters): every output and final state of all 4 heads, against
   the oracle's KCP form (segment pairs composed in order, pinned against the
@@ -81,17 +81,19 @@ def test_varlen_prefill_full_size(kda):
                           cu_seqlens=inp.cu_seqlens.to(dev), z=inp.z, initial_state=inp.S0,
                           chunk=64)
     torch.cuda.synchronize()
-    ys, yos, ss, sos = [], [], [], []
-    for n in range(len(lens)):
-        for h in (0, 47 + n % 2, 95):
-            q, k, v, z, g, b, s0, sl = _chain(inp, n, h)
-            yo, so = oracle.recurrence(q, k, v, g, b, [0, lens[n]], z=z, S_init=s0)
-            ys.append(y[sl, h].cpu())
-            yos.append(yo[:, 0])
-            ss.append(fs[n, h].cpu())
-            sos.append(so[0])
-    parity.check(f"[fullsize] varlen {len(lens)} sequences x 3 heads", "bf16",
-                 y=(torch.cat(ys), np.concatenate(yos)), state=(torch.stack(ss), np.stack(sos)))
+    # eight heads of every sequence (a different set for odd and even
+    # sequences), packed as one-head sequences for a single oracle call
+    chains = [(n, h) for n in range(len(lens)) for h in (0, 13 + n % 2, 27, 40 + n % 3, 54, 67, 81 + n % 2, 95)]
+    parts = [_chain(inp, n, h) for n, h in chains]
+    cat = lambda i: None if parts[0][i] is None else torch.cat([p[i] for p in parts])
+    q, k, v, z, g, b = (cat(i) for i in range(6))
+    s0 = torch.cat([p[6] for p in parts])
+    cu = np.concatenate([[0], np.cumsum([lens[n] for n, _ in chains])]).tolist()
+    yo, so = oracle.recurrence(q, k, v, g, b, cu, z=z, S_init=s0)
+    ys = torch.cat([y[p[7], h].cpu() for p, (n, h) in zip(parts, chains)])
+    ss = torch.stack([fs[n, h].cpu() for n, h in chains])
+    parity.check(f"[fullsize] varlen {len(lens)} sequences x 8 heads ({len(chains)} chains)", "bf16",
+                 y=(ys, yo[:, 0]), state=(ss, so))
 
 
 def test_kcp_full_size(kda):
