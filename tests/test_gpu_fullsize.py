@@ -6,8 +6,8 @@ the worst (token, head) row (tests/parity.py).
   heads (plus the chunk-scale long-memory variant).
 - The same layer through the fused-input entry point (raw q, k, gate
   pre-activations): every output and final state of all 96 heads.
-- Varlen prefill (16 sequences, lengths in [512, 8192], H=96): 128 (sequence,
-  head) chains, eight heads of every sequence.
+- Varlen prefill (16 sequences, lengths in [512, 8192], H=96): every output
+  and final state of all 1,536 (sequence, head) chains.
 - KCP scan (T=2^20, H=4, 256 segments, segment-scale long-memory draw so the
   carried state matters): every output and final state of all 4 heads, against
   the oracle's KCP form (segment pairs composed in order, pinned against the
@@ -64,16 +64,8 @@ def test_k3_layer_prefill_fused_full_size(kda):
                  state=(fs, so.reshape(fs.shape)))
 
 
-def _chain(inp, n, h):
-    """Host copy of one (sequence, head) chain of device inputs."""
-    cu = inp.cu_seqlens.tolist()
-    sl = slice(cu[n], cu[n + 1])
-    pick = lambda t: None if t is None else t[sl, h:h + 1].contiguous().cpu()
-    s0 = None if inp.S0 is None else inp.S0[n:n + 1, h:h + 1].cpu()
-    return pick(inp.q), pick(inp.k), pick(inp.v), pick(inp.z), pick(inp.g), pick(inp.beta), s0, sl
-
-
 def test_varlen_prefill_full_size(kda):
+    """Every output and final state of all 1,536 (sequence, head) chains."""
     lens = kda_inputs.varlen_lengths()
     dev = torch.device("cuda")
     inp = kda_inputs.draw_on_device(lens, 96, 128, 128, True, 0.02, kda_inputs.workload_seed(2), dev)
@@ -81,19 +73,12 @@ def test_varlen_prefill_full_size(kda):
                           cu_seqlens=inp.cu_seqlens.to(dev), z=inp.z, initial_state=inp.S0,
                           chunk=64)
     torch.cuda.synchronize()
-    # eight heads of every sequence (a different set for odd and even
-    # sequences), packed as one-head sequences for a single oracle call
-    chains = [(n, h) for n in range(len(lens)) for h in (0, 13 + n % 2, 27, 40 + n % 3, 54, 67, 81 + n % 2, 95)]
-    parts = [_chain(inp, n, h) for n, h in chains]
-    cat = lambda i: None if parts[0][i] is None else torch.cat([p[i] for p in parts])
-    q, k, v, z, g, b = (cat(i) for i in range(6))
-    s0 = torch.cat([p[6] for p in parts])
-    cu = np.concatenate([[0], np.cumsum([lens[n] for n, _ in chains])]).tolist()
-    yo, so = oracle.recurrence(q, k, v, g, b, cu, z=z, S_init=s0)
-    ys = torch.cat([y[p[7], h].cpu() for p, (n, h) in zip(parts, chains)])
-    ss = torch.stack([fs[n, h].cpu() for n, h in chains])
-    parity.check(f"[fullsize] varlen {len(lens)} sequences x 8 heads ({len(chains)} chains)", "bf16",
-                 y=(ys, yo[:, 0]), state=(ss, so))
+    host = lambda t: t.cpu()
+    y, fs = host(y), host(fs)
+    yo, so = oracle.recurrence(host(inp.q), host(inp.k), host(inp.v), host(inp.g), host(inp.beta),
+                               inp.cu_seqlens.tolist(), z=host(inp.z), S_init=host(inp.S0))
+    parity.check(f"[fullsize] varlen {len(lens)} sequences x 96 heads", "bf16",
+                 y=(y, yo), state=(fs, so.reshape(fs.shape)))
 
 
 def test_kcp_full_size(kda):
