@@ -456,10 +456,43 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.final_seq_lo = 0;
     a.carry = pairs;
     a.y = nullptr;
-    for (int64_t lo = 0; lo < nchunks; lo += slab) {
-        a.slab_lo = lo;
-        a.slab_hi = lo + slab < nchunks ? lo + slab : nchunks;
-        if (kda::launch_chunk_prep(a, nullptr, a.slab_hi - lo) != hipSuccess) return KDA_ERR_HIP;
+    // a bounded workspace holds a rectangle of segments x chunks at a time:
+    // as many segments as make about one round of scan workgroups, and as
+    // many of their chunks as then fit (slabs of consecutive global chunks
+    // would hold a few whole segments, too few workgroups to fill the GPU)
+    int cus = 0;
+    if (bounded && kda::device_cu_count(&cus) != hipSuccess) return KDA_ERR_HIP;
+    const int64_t cps = (seg_len + chunk - 1) / chunk;
+    auto rects = [&](int wg_per_chain, int wg_per_cu, bool prep) -> kda_status {
+        int64_t gs = (int64_t)cus * wg_per_cu / ((int64_t)wg_per_chain * H);
+        gs = gs < 1 ? 1 : gs > num_segments ? num_segments : gs;
+        if (gs > slab) gs = slab;
+        int64_t pw = slab / gs;
+        if (pw > cps) pw = cps;
+        for (int64_t s0 = 0; s0 < num_segments; s0 += gs) {
+            for (int64_t c0 = 0; c0 < cps; c0 += pw) {
+                a.rect_w = (int)(c0 + pw < cps ? pw : cps - c0);
+                a.rect_c0 = (int)c0;
+                a.rect_s0 = (int)s0;
+                a.rect_s1 = (int)(s0 + gs < num_segments ? s0 + gs : num_segments);
+                if (prep && kda::launch_chunk_prep(a, nullptr, (int64_t)(a.rect_s1 - a.rect_s0) * a.rect_w) !=
+                                hipSuccess)
+                    return KDA_ERR_HIP;
+                if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
+            }
+        }
+        a.rect_w = 0;
+        return KDA_OK;
+    };
+    if (bounded) {
+        // pairs with two value tiles a wave: two workgroups a CU at bf16
+        const int nvg = (dk + dv) / (64 * a.nvt);
+        const kda_status st = rects(nvg, a.nvt == 2 && dt == KDA_BF16 ? 2 : 1, true);
+        if (st != KDA_OK) return st;
+    } else {
+        a.slab_lo = 0;
+        a.slab_hi = nchunks;
+        if (kda::launch_chunk_prep(a, nullptr, nchunks) != hipSuccess) return KDA_ERR_HIP;
         if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
     }
     // phase 2: entering state of every segment
@@ -476,13 +509,9 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.final_seq_lo = num_segments - 1;
     a.carry = starts;
     a.y = y;
-    for (int64_t lo = 0; lo < nchunks; lo += slab) {
-        a.slab_lo = lo;
-        a.slab_hi = lo + slab < nchunks ? lo + slab : nchunks;
-        // with one slab the products of phase 1 are still in place
-        if (bounded && kda::launch_chunk_prep(a, nullptr, a.slab_hi - lo) != hipSuccess) return KDA_ERR_HIP;
-        if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
-    }
+    if (bounded) return rects(dv / (64 * a.nvt), 1, true);
+    // one slab: the products of phase 1 are still in place
+    if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }
 

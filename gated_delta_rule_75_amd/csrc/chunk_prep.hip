@@ -50,6 +50,7 @@ namespace kda {
 struct PrepParams {
     int H, num_seqs, cps;   // cps: chunks per segment when cu_seqlens is NULL
     int gc0;                // global chunk of workspace block 0 (the first chunk of the slab)
+    int rect_w, rect_c0, rect_s0;   // rectangular slab (rect_w > 0): chunks [c0, c0 + w) of segments s0..
     float scale;
     int64_t T_total, seg_len;
     const int32_t* cu_seqlens;
@@ -167,7 +168,10 @@ void chunk_prep_kernel(PrepParams p) {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t wsb = blockIdx.x;  // (chunk, head) block of the workspace
     const int h = (int)(wsb % H);
-    const int gc = p.gc0 + (int)(wsb / H);   // global chunk index
+    // global chunk index: the slab's chunks in order, or those of a rectangle
+    // of segments x chunks, segment by segment
+    const int rb = (int)(wsb / H);
+    const int gc = p.rect_w > 0 ? (p.rect_s0 + rb / p.rect_w) * p.cps + p.rect_c0 + rb % p.rect_w : p.gc0 + rb;
 
     // ---- locate the chunk ----------------------------------------------------
     int64_t ts;
@@ -623,6 +627,9 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
     p.num_seqs = a.num_seqs;
     p.cps = (int)((a.seg_len + a.chunk - 1) / a.chunk);
     p.gc0 = (int)a.slab_lo;
+    p.rect_w = a.rect_w;
+    p.rect_c0 = a.rect_c0;
+    p.rect_s0 = a.rect_s0;
     p.scale = a.scale;
     p.T_total = a.T_total;
     p.seg_len = a.seg_len;

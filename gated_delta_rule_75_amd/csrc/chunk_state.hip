@@ -51,6 +51,7 @@ struct StateParams {
     int H, num_seqs, nchains, nvg, dvt, final_seq_lo, cps;
     int chunk_cap;          // bound on the global chunk count
     int slab_lo, slab_hi;   // global chunks whose products the workspace holds
+    int rect_w, rect_c0, rect_s0, rect_s1;   // or a rectangle of segments x chunks (rect_w > 0)
     int first_slab;         // chains without chunks run here
     float* carry;           // state between slabs, [num_seqs, H, dk, dvt]
     int64_t T_total, seg_len;
@@ -220,17 +221,25 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
     // that its window starts at chunk 0 (tokens t0.., workspace block cws + c)
     const int64_t len_chain = len;
     int cb = 0, ce = nch;
-    if (p.slab_lo > cbase) cb = p.slab_lo - cbase < nch ? p.slab_lo - cbase : nch;
-    if (p.slab_hi < cbase + nch) ce = p.slab_hi > cbase ? p.slab_hi - cbase : 0;
+    const bool rect = p.rect_w > 0;
+    const bool mine = !rect || (n >= p.rect_s0 && n < p.rect_s1);
+    if (rect) {
+        cb = mine ? (p.rect_c0 < nch ? p.rect_c0 : nch) : nch;
+        ce = mine ? (p.rect_c0 + p.rect_w < nch ? p.rect_c0 + p.rect_w : nch) : 0;
+    } else {
+        if (p.slab_lo > cbase) cb = p.slab_lo - cbase < nch ? p.slab_lo - cbase : nch;
+        if (p.slab_hi < cbase + nch) ce = p.slab_hi > cbase ? p.slab_hi - cbase : 0;
+    }
     if (ce <= cb) {
-        if (nch > 0 || !p.first_slab) return;   // nothing of this chain in the slab
+        if (nch > 0 || !p.first_slab || !mine) return;   // nothing of this chain in the slab
         cb = ce = 0;
     }
     const bool from_start = cb == 0, to_end = ce == nch;
     t0 += (int64_t)cb * CH;
     len = len - (int64_t)cb * CH < (int64_t)(ce - cb) * CH ? len - (int64_t)cb * CH : (int64_t)(ce - cb) * CH;
     const int ck0 = cb;                      // chunks of the chain before the window
-    const int cws = cbase + cb - p.slab_lo;  // workspace block of the window's first chunk
+    // workspace block of the window's first chunk
+    const int cws = rect ? (n - p.rect_s0) * p.rect_w + cb - p.rect_c0 : cbase + cb - p.slab_lo;
     nch = ce - cb;
     // first value tile (16 columns of v / U) of the workgroup; negative for
     // the transition columns of mode 2, whose waves take no values
@@ -1012,7 +1021,11 @@ static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_of
     p.chunk_cap = (int)a.chunk_cap;
     p.slab_lo = (int)a.slab_lo;
     p.slab_hi = (int)a.slab_hi;
-    p.first_slab = a.slab_lo == 0;
+    p.rect_w = a.rect_w;
+    p.rect_c0 = a.rect_c0;
+    p.rect_s0 = a.rect_s0;
+    p.rect_s1 = a.rect_s1;
+    p.first_slab = a.rect_w > 0 ? a.rect_c0 == 0 : a.slab_lo == 0;
     p.carry = a.carry;
     p.H = a.H;
     p.num_seqs = a.num_seqs;

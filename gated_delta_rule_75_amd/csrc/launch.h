@@ -58,6 +58,11 @@ struct TwoPassArgs {
     // else into carry[n].  Chains with no chunks at all run in the first slab.
     // One slab [0, chunk_cap) with no carry covers the whole call.
     int64_t slab_lo, slab_hi;
+    // Rectangular slab (equal segments only, cu_seqlens NULL; rect_w > 0):
+    // chunks [rect_c0, rect_c0 + rect_w) of segments [rect_s0, rect_s1), in
+    // workspace block ((n - rect_s0) rect_w + c - rect_c0) H + h; slab_lo and
+    // slab_hi are then unused.  Empty segments run in the part with rect_c0 = 0.
+    int rect_w, rect_c0, rect_s0, rect_s1;
     float* carry;                // [num_seqs, H, dk, dv] (mode 2: dk + dv columns), or NULL
     // prefix-cache checkpoints (modes 0 and 1): the state after every
     // ckpt_every chunks of a sequence, at row ckpt_off[n] + j of ckpt
