@@ -485,9 +485,13 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
         return KDA_OK;
     };
     if (bounded) {
-        // pairs with two value tiles a wave: two workgroups a CU at bf16
+        // pairs with two value tiles a wave: two workgroups a CU at bf16.
+        // The pairs read no Qt and no P, which pass 1 then skips; the
+        // outputs below prepare their rectangles again in full
         const int nvg = (dk + dv) / (64 * a.nvt);
+        a.pairs_only = true;
         const kda_status st = rects(nvg, a.nvt == 2 && dt == KDA_BF16 ? 2 : 1, true);
+        a.pairs_only = false;
         if (st != KDA_OK) return st;
     } else {
         a.slab_lo = 0;

@@ -60,9 +60,13 @@ struct PrepParams {
     TwoPassBufs ws;
 };
 
-template <typename E_, int DK_, int CH_, bool FUSED_>
+template <typename E_, int DK_, int CH_, bool FUSED_, bool NOQP_ = false>
 struct PrepCfg {
     static constexpr bool FUSED = FUSED_;
+    // NOQP: only what the KCP pairs read (W, T, Kh^T, gam): q is not loaded
+    // and neither Qt nor P is formed
+    static constexpr bool NOQP = NOQP_;
+    static_assert(!(FUSED && NOQP), "no fused pairs pass");
     using E = E_;
     using K = KBlk<E_>;
     using T = typename E::T;
@@ -227,8 +231,13 @@ void chunk_prep_kernel(PrepParams p) {
     }
 #pragma unroll
     for (int i = 0; i < TPT; ++i) rk[i] = *reinterpret_cast<const T4*>(gk + rows[i] * DK + c0);
+    if constexpr (!C::NOQP) {
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) rq[i] = *reinterpret_cast<const T4*>(gq + rows[i] * DK + c0);
+        for (int i = 0; i < TPT; ++i) rq[i] = *reinterpret_cast<const T4*>(gq + rows[i] * DK + c0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) rq[i] = T4{};
+    }
     if (tid < CH) {
         if constexpr (C::FUSED) sBeta[tid] = tid < nvalid ? sigmoid(to_f32(braw)) : 0.f;
         else sBeta[tid] = braw;
@@ -388,9 +397,11 @@ void chunk_prep_kernel(PrepParams p) {
         kw[i] = pack4<T>(kg[0], kg[1], kg[2], kg[3]);
         kh[i] = pack4<T>(kx2[0], kx2[1], kx2[2], kx2[3]);
         st4(sKr + t * LK + c0, kr[0], kr[1], kr[2], kr[3]);
-        st4(sQr + t * LK + c0, qr[0], qr[1], qr[2], qr[3]);
         st4(sKc + t * LK + c0, kc[0], kc[1], kc[2], kc[3]);
-        st4(Qt + frag_elem<K>((c0 / K::KB) * NT + t / 16, t, c0), qt[0], qt[1], qt[2], qt[3]);
+        if constexpr (!C::NOQP) {
+            st4(sQr + t * LK + c0, qr[0], qr[1], qr[2], qr[3]);
+            st4(Qt + frag_elem<K>((c0 / K::KB) * NT + t / 16, t, c0), qt[0], qt[1], qt[2], qt[3]);
+        }
     }
     barrier_keep_loads();
 
@@ -412,12 +423,12 @@ void chunk_prep_kernel(PrepParams p) {
                 fc[u] = a > b ? lds_frag_scaled<E>(sKc, LK, 16 * b, kk, lane, dsc)
                               : lds_frag<E>(sKc, LK, 16 * b, kk, lane);
                 fr[u] = lds_frag<E>(sKr, LK, 16 * a, kk, lane);
-                fq[u] = lds_frag<E>(sQr, LK, 16 * a, kk, lane);
+                if constexpr (!C::NOQP) fq[u] = lds_frag<E>(sQr, LK, 16 * a, kk, lane);
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 accA = E::mma(fr[u], fc[u], accA);  // A[t][j]
-                accP = E::mma(fc[u], fq[u], accP);  // P^T[j][t]
+                if constexpr (!C::NOQP) accP = E::mma(fc[u], fq[u], accP);  // P^T[j][t]
             }
         }
         // beta_t A[t][j] (strictly lower): lane holds rows 16a+4g4+i, column 16b+l16
@@ -427,17 +438,19 @@ void chunk_prep_kernel(PrepParams p) {
             const int r = 4 * g4 + i;
             Lb[r * 17 + l16] = (a > b || l16 < r) ? sBeta[16 * a + r] * accA[i] : 0.f;
         }
-        // scale P[t][j] (j <= t): lane holds token 16a+l16, columns 16b+4g4+i
-        float pv[4];
+        if constexpr (!C::NOQP) {
+            // scale P[t][j] (j <= t): lane holds token 16a+l16, columns 16b+4g4+i
+            float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = (a > b || 4 * g4 + i <= l16) ? scale * accP[i] : 0.f;
-        const int j0 = 16 * b + 4 * g4;
-        st4(Pm + frag_elem<K>(pm_frag_index(a, j0 / K::KB, C::NKT, K::KB), l16, j0), pv[0], pv[1], pv[2], pv[3]);
-        // a two-tile k-block holds tile a + 1 beside an even diagonal tile a
-        // (past C when a + 1 = NT): zeros there
-        if (K::TPB == 2 && a == b && a % 2 == 0) {
-            const int jz = j0 + 16;
-            st4(Pm + frag_elem<K>(pm_frag_index(a, jz / K::KB, C::NKT, K::KB), l16, jz), 0.f, 0.f, 0.f, 0.f);
+            for (int i = 0; i < 4; ++i) pv[i] = (a > b || 4 * g4 + i <= l16) ? scale * accP[i] : 0.f;
+            const int j0 = 16 * b + 4 * g4;
+            st4(Pm + frag_elem<K>(pm_frag_index(a, j0 / K::KB, C::NKT, K::KB), l16, j0), pv[0], pv[1], pv[2], pv[3]);
+            // a two-tile k-block holds tile a + 1 beside an even diagonal tile a
+            // (past C when a + 1 = NT): zeros there
+            if (K::TPB == 2 && a == b && a % 2 == 0) {
+                const int jz = j0 + 16;
+                st4(Pm + frag_elem<K>(pm_frag_index(a, jz / K::KB, C::NKT, K::KB), l16, jz), 0.f, 0.f, 0.f, 0.f);
+            }
         }
     }
     barrier_keep_loads();
@@ -649,17 +662,18 @@ static hipError_t launch_prep_cfg(const TwoPassArgs& a, const int32_t* chunk_off
     return hipGetLastError();
 }
 
-template <class E, int DK, bool FUSED>
+template <class E, int DK, bool FUSED, bool NOQP>
 static hipError_t launch_prep_chunk(const TwoPassArgs& a, const int32_t* co, int64_t nb) {
-    if (a.chunk == 64) return launch_prep_cfg<PrepCfg<E, DK, 64, FUSED>>(a, co, nb);
-    if (a.chunk == 32) return launch_prep_cfg<PrepCfg<E, DK, 32, FUSED>>(a, co, nb);
-    return launch_prep_cfg<PrepCfg<E, DK, 16, FUSED>>(a, co, nb);
+    if (a.chunk == 64) return launch_prep_cfg<PrepCfg<E, DK, 64, FUSED, NOQP>>(a, co, nb);
+    if (a.chunk == 32) return launch_prep_cfg<PrepCfg<E, DK, 32, FUSED, NOQP>>(a, co, nb);
+    return launch_prep_cfg<PrepCfg<E, DK, 16, FUSED, NOQP>>(a, co, nb);
 }
 
 template <class E, int DK>
 static hipError_t launch_prep_dk(const TwoPassArgs& a, const int32_t* co, int64_t nb) {
-    if (a.fused) return launch_prep_chunk<E, DK, true>(a, co, nb);
-    return launch_prep_chunk<E, DK, false>(a, co, nb);
+    if (a.fused) return launch_prep_chunk<E, DK, true, false>(a, co, nb);
+    if (a.pairs_only) return launch_prep_chunk<E, DK, false, true>(a, co, nb);
+    return launch_prep_chunk<E, DK, false, false>(a, co, nb);
 }
 
 hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks) {

@@ -42,6 +42,7 @@ struct TwoPassArgs {
     const void *q, *k, *v;
     const void *g, *beta;        // fp32 g, beta; fused: pre-activations a, b in the storage dtype
     bool fused;                  // raw q, k (normalised in the kernel) and gate pre-activations
+    bool pairs_only;             // preparation: only the products the KCP pairs read (no Qt, P)
     const void* z;
     const float* initial_state;  // [num_seqs, H, dk, dv] or NULL
     float* final_state;          // see final_seq_lo; mode 2: [num_seqs, H, dk, dk + dv]
