@@ -420,8 +420,9 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     // segments hold seg_len tokens each; with T not a multiple, trailing ones may be empty
     const int64_t seg_len = (T + num_segments - 1) / num_segments;
     const int64_t nchunks = seg_chunks(seg_len, chunk, num_segments);
-    // the chunk products of all segments at once, or slabs of consecutive
-    // chunks (formed twice then: for the pairs and for the outputs)
+    // the chunk products of all segments at once, or, in a bounded workspace,
+    // of rectangles of segments x chunks (formed twice then: for the pairs
+    // and for the outputs)
     int64_t slab = slab_chunks(dt, H, dk, dv, chunk, num_segments, nchunks, 0, workspace_bytes - fixed);
     if (slab <= 0) return KDA_ERR_WORKSPACE_TOO_SMALL;
     const bool bounded = slab < nchunks;
