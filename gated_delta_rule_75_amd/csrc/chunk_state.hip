@@ -143,9 +143,8 @@ struct StCfg {
     static constexpr int BYTES = NBUF * BUF + (LW ? 2 * ZT : 0) + (MIX ? N_T * 1024 + VTB : 0);
     static_assert(BYTES <= 160 * 1024, "LDS");
     static_assert(!MIX || sizeof(T) == 4 || BYTES <= 80 * 1024, "two pairs workgroups a CU");
-    // loader waves: four (a wave issues a 1 KiB copy about every 170 cycles
-    // on its own; with the copies dealt round-robin, two, three and four
-    // loaders reach 324, 317 and 314 us on the 96-head layer)
+    // loader waves: four (with the copies dealt round-robin, two, three and
+    // four loaders reach 324, 317 and 314 us on the 96-head layer)
     static constexpr int NLW = LW ? 4 : 0;
     // group 1 of the loaders' copies staged through registers two chunks
     // ahead: the single-sequence and varlen scans, whose few workgroups wait
