@@ -11,7 +11,8 @@ the worst (token, head) row (tests/parity.py).
 - KCP scan (T=2^20, H=4, 256 segments, segment-scale long-memory draw so the
   carried state matters): every output and final state of all 4 heads, against
   the oracle's KCP form (segment pairs composed in order, pinned against the
-  sequential recurrence on the CPU).
+  sequential recurrence on the CPU).  The same call in a 512 MiB workspace,
+  and a second one-pass call, equal it bit for bit.
 - Decode (128 requests x 96 heads, 1000 steps): every state and output after
   step 1, 32 sampled chains after step 10, 8 after step 1000.
 - Speculative replay (128 requests x 96 heads, 4 draft tokens, acceptance
@@ -99,6 +100,24 @@ def test_kcp_full_size(kda):
                      y=(y[:, h], out["y"][:, h]))
     # the long-memory draw really carries state across segments
     assert np.abs(out["starts"][S - 1]).max() > 1e-3
+
+
+def test_kcp_full_size_bounded_and_repeated(kda):
+    """The 2^20-token KCP call in a 512 MiB workspace (rectangles of segments x
+    chunks, the chunk products formed twice) and a second one-pass call both
+    equal the first one-pass call bit for bit."""
+    w = kda_inputs.WORKLOADS[3]
+    T, H, S = w["lens"][0], w["H"], w["segments"]
+    inp = kda_inputs.draw_on_device([T], H, 128, 128, False, 0.0,
+                                    kda_inputs.workload_seed(3), torch.device("cuda"))
+    x = (inp.q, inp.k, inp.v, inp.g, inp.beta)
+    y1, s1 = kda.kcp_scan(*x, S, chunk=64)
+    y2, s2 = kda.kcp_scan(*x, S, chunk=64)
+    y3, s3 = kda.kcp_scan(*x, S, chunk=64, max_workspace_bytes=512 << 20)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1).all() and torch.isfinite(s1).all()
+    assert torch.equal(y1, y2) and torch.equal(s1, s2), "two one-pass calls differ"
+    assert torch.equal(y1, y3) and torch.equal(s1, s3), "the bounded call differs from the one-pass call"
 
 
 def test_decode_full_size(kda):

@@ -76,6 +76,27 @@ def test_decode_matches_oracle(kda, dtype, d):
     parity.check(f"decode {dtype} d={d}", dtype, y=(y, yo), state=(state, so))
 
 
+def test_decode_and_replay_are_deterministic(kda):
+    """The same step from two copies of one state gives the same bits, as do
+    two replay calls (no atomics or order-dependent reductions)."""
+    dec = kda_inputs.make_decode(N=16, H=8, dk=128, dv=128, dtype="bf16", gated=True, s0_std=0.02,
+                                 pool=1, seed=12)
+    x = [getattr(dec, n)[0].cuda() for n in ("q", "k", "v", "g", "beta", "z")]
+    sa, sb = dec.S0.clone().cuda(), dec.S0.clone().cuda()
+    ya = kda.decode_step(*x[:5], sa, z=x[5])
+    yb = kda.decode_step(*x[:5], sb, z=x[5])
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(sa, sb)
+    rep = kda_inputs.make_replay(8, 3, 4, 128, 128, "bf16", True, 0.02, 13)
+    r = [getattr(rep, n).cuda() for n in ("q", "k", "v", "g", "beta", "z")]
+    ra, rb = rep.S0.clone().cuda(), rep.S0.clone().cuda()
+    acc = rep.accepted.cuda()
+    y1 = kda.decode_replay(*r[:5], ra, z=r[5], accepted=acc)
+    y2 = kda.decode_replay(*r[:5], rb, z=r[5], accepted=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(ra, rb)
+
+
 def test_decode_ungated_and_scaled(kda):
     dec = kda_inputs.make_decode(N=2, H=2, dk=128, dv=128, dtype="f32", gated=False,
                                  s0_std=0.5, pool=1, seed=8)
