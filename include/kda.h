@@ -21,6 +21,10 @@
  * synchronisation.  No call allocates device or host memory, keeps state
  * between calls, or throws across the ABI.  Calls on different streams may
  * run concurrently; results are deterministic (no atomics in reductions).
+ * No call issues a memset or a host synchronisation, so a call can be
+ * recorded in a HIP graph (stream capture) once an earlier call on the same
+ * device has run: the first call of each kernel on a device raises its LDS
+ * limit, which is not a stream operation.
  *
  * Layouts (row-major, last index fastest; T_total = packed token count):
  *   q, k        [T_total, H, dk]       dtype dt
