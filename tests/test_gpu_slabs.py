@@ -107,6 +107,7 @@ def test_fused_prefill_with_slabs(kda):
 
 @pytest.mark.parametrize("dtype,d,chunk,T,nseg", [
     ("bf16", 128, 64, 4096, 8), ("f32", 64, 16, 1001, 7), ("bf16", 128, 32, 2000, 16),
+    ("f32", 128, 64, 3000, 5), ("bf16", 64, 64, 2500, 3),
 ])
 def test_kcp_slabs_equal_one_pass(kda, dtype, d, chunk, T, nseg):
     inp = kda_inputs.make_workload(3, "segment", lens=[T], H=2, dk=d, dv=d, dtype=dtype,
