@@ -486,12 +486,12 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
         return KDA_OK;
     };
     if (bounded) {
-        // pairs with two value tiles a wave: two workgroups a CU at bf16.
         // The pairs read no Qt and no P, which pass 1 then skips; the
         // outputs below prepare their rectangles again in full
-        const int nvg = (dk + dv) / (64 * a.nvt);
+        int per_chain = 1, per_cu = 1;
+        kda::state_geometry(a, &per_chain, &per_cu);
         a.pairs_only = true;
-        const kda_status st = rects(nvg, a.nvt == 2 && dt == KDA_BF16 ? 2 : 1, true);
+        const kda_status st = rects(per_chain, per_cu, true);
         a.pairs_only = false;
         if (st != KDA_OK) return st;
     } else {
@@ -514,7 +514,11 @@ kda_status kda_kcp_scan(kda_dtype dt, int H, int dk, int dv, int chunk, float sc
     a.final_seq_lo = num_segments - 1;
     a.carry = starts;
     a.y = y;
-    if (bounded) return rects(dv / (64 * a.nvt), 1, true);
+    if (bounded) {
+        int per_chain = 1, per_cu = 1;
+        kda::state_geometry(a, &per_chain, &per_cu);
+        return rects(per_chain, per_cu, true);
+    }
     // one slab: the products of phase 1 are still in place
     if (kda::launch_chunk_state(a, nullptr, nullptr) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;

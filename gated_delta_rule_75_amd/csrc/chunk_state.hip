@@ -70,14 +70,14 @@ struct StateParams {
     int64_t ckpt_cap;
 };
 
-template <typename E_, int DK_, int DV_, int CH_, int NVT_, int MODE_>
+template <typename E_, int DK_, int DV_, int CH_, int NVT_, int MODE_, int NW_ = 4>
 struct StCfg {
     using E = E_;
     using K = KBlk<E_>;
     using T = typename K::T;
     static constexpr int DK = DK_, DV = DV_, CH = CH_, NVT = NVT_, MODE = MODE_;
     static constexpr bool AUG = MODE_ == kModePairs;
-    static constexpr int NW = 4;                        // compute waves
+    static constexpr int NW = NW_;                      // compute waves
     static constexpr int CW = 16 * NVT * NW;            // state columns per workgroup
     static constexpr int NTT = CH / 16, NCT = DK / 16;
     static constexpr int KB = K::KB, TPB = K::TPB;
@@ -142,7 +142,7 @@ struct StCfg {
     static constexpr int O_TV = NBUF * BUF;                // MIX: T fragments, then the v rows
     static constexpr int BYTES = NBUF * BUF + (LW ? 2 * ZT : 0) + (MIX ? N_T * 1024 + VTB : 0);
     static_assert(BYTES <= 160 * 1024, "LDS");
-    static_assert(!MIX || sizeof(T) == 4 || BYTES <= 80 * 1024, "two pairs workgroups a CU");
+    static_assert(!MIX || sizeof(T) == 4 || NW != 4 || BYTES <= 80 * 1024, "two pairs workgroups a CU");
     // loader waves: four (with the copies dealt round-robin, two, three and
     // four loaders reach 324, 317 and 314 us on the 96-head layer)
     static constexpr int NLW = LW ? 4 : 0;
@@ -1059,41 +1059,60 @@ static hipError_t launch_state_cfg(const TwoPassArgs& a, const int32_t* chunk_of
     return hipGetLastError();
 }
 
-template <class E, int DK, int CH, int MODE>
-static hipError_t launch_state_nvt(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
-    // One value tile per wave wherever loader waves apply, whatever the
-    // number of chains (on the 16-sequence varlen layer 2.84 ms against 3.04
-    // with two tiles); the transition pairs, with dk + dv columns a chain,
-    // keep the choice made from the chain count (two tiles: 0.74 ms against
-    // 1.07 for 1024 chains).
+// The configuration a call runs with, handed to f as a value of its type.
+// One value tile per wave wherever loader waves apply, whatever the number of
+// chains (on the 16-sequence varlen layer 2.84 ms against 3.04 with two
+// tiles); the transition pairs, with dk + dv columns a chain, keep the choice
+// made from the chain count (two tiles: 0.74 ms against 1.07 for 1024
+// chains), at bf16 and dk = 128 with all 256 columns of a chain in one
+// workgroup of eight compute waves.
+template <class E, int DK, int CH, int MODE, class F>
+static auto with_state_nvt(const TwoPassArgs& a, F&& f) {
     using C1 = StCfg<E, DK, DK, CH, 1, MODE>;
-    if (a.nvt == 1 || (C1::LW && MODE != kModePairs)) return launch_state_cfg<C1>(a, co, ord);
-    return launch_state_cfg<StCfg<E, DK, DK, CH, 2, MODE>>(a, co, ord);
+    if (a.nvt == 1 || (C1::LW && MODE != kModePairs)) return f(C1{});
+    if constexpr (MODE == kModePairs && DK == 128 && sizeof(typename E::T) == 2)
+        return f(StCfg<E, DK, DK, CH, 2, MODE, kPairsWaves>{});
+    else
+        return f(StCfg<E, DK, DK, CH, 2, MODE>{});
 }
 
-template <class E, int DK, int CH>
-static hipError_t launch_state_mode(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
+template <class E, int DK, int CH, class F>
+static auto with_state_mode(const TwoPassArgs& a, F&& f) {
     switch (a.mode) {
-        case kModeSeq: return launch_state_nvt<E, DK, CH, kModeSeq>(a, co, ord);
-        case kModeVarlen: return launch_state_nvt<E, DK, CH, kModeVarlen>(a, co, ord);
-        case kModePairs: return launch_state_nvt<E, DK, CH, kModePairs>(a, co, ord);
-        default: return launch_state_nvt<E, DK, CH, kModeFinish>(a, co, ord);
+        case kModeSeq: return with_state_nvt<E, DK, CH, kModeSeq>(a, f);
+        case kModeVarlen: return with_state_nvt<E, DK, CH, kModeVarlen>(a, f);
+        case kModePairs: return with_state_nvt<E, DK, CH, kModePairs>(a, f);
+        default: return with_state_nvt<E, DK, CH, kModeFinish>(a, f);
     }
 }
 
-template <class E, int DK>
-static hipError_t launch_state_dk(const TwoPassArgs& a, const int32_t* co, const int32_t* ord) {
-    if (a.chunk == 64) return launch_state_mode<E, DK, 64>(a, co, ord);
-    if (a.chunk == 32) return launch_state_mode<E, DK, 32>(a, co, ord);
-    return launch_state_mode<E, DK, 16>(a, co, ord);
+template <class E, int DK, class F>
+static auto with_state_dk(const TwoPassArgs& a, F&& f) {
+    if (a.chunk == 64) return with_state_mode<E, DK, 64>(a, f);
+    if (a.chunk == 32) return with_state_mode<E, DK, 32>(a, f);
+    return with_state_mode<E, DK, 16>(a, f);
+}
+
+template <class F>
+static auto with_state_cfg(const TwoPassArgs& a, F&& f) {
+    if (a.dtype == 0) return a.dk == 128 ? with_state_dk<BF16, 128>(a, f) : with_state_dk<BF16, 64>(a, f);
+    return a.dk == 128 ? with_state_dk<F32, 128>(a, f) : with_state_dk<F32, 64>(a, f);
 }
 
 hipError_t launch_chunk_state(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order) {
-    if (a.dtype == 0)
-        return a.dk == 128 ? launch_state_dk<BF16, 128>(a, chunk_off, order)
-                           : launch_state_dk<BF16, 64>(a, chunk_off, order);
-    return a.dk == 128 ? launch_state_dk<F32, 128>(a, chunk_off, order)
-                       : launch_state_dk<F32, 64>(a, chunk_off, order);
+    return with_state_cfg(a, [&](auto c) { return launch_state_cfg<decltype(c)>(a, chunk_off, order); });
+}
+
+void state_geometry(const TwoPassArgs& a, int* wg_per_chain, int* wg_per_cu) {
+    with_state_cfg(a, [&](auto c) {
+        using C = decltype(c);
+        const int cols = C::AUG ? a.dk + a.dv : a.dv;
+        *wg_per_chain = cols / C::CW > 0 ? cols / C::CW : 1;
+        // eight waves a CU at the scan's register count, and the LDS
+        const int by_waves = 8 / (C::NW + C::NLW), by_lds = (int)((160 * 1024) / C::BYTES);
+        *wg_per_cu = by_waves < by_lds ? (by_waves > 0 ? by_waves : 1) : (by_lds > 0 ? by_lds : 1);
+        return 0;
+    });
 }
 
 hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int64_t T_total, int chunk,

@@ -94,6 +94,12 @@ hipError_t launch_varlen_plan(int num_seqs, const int32_t* cu_seqlens, int64_t T
 hipError_t launch_chunk_prep(const TwoPassArgs& a, const int32_t* chunk_off, int64_t nchunks);
 // The sequential pass over the chunks of every (sequence, head).
 hipError_t launch_chunk_state(const TwoPassArgs& a, const int32_t* chunk_off, const int32_t* order);
+// Workgroups a chain of the state scan takes, and how many of them fit on a
+// CU at once, for the configuration launch_chunk_state picks for `a`.
+void state_geometry(const TwoPassArgs& a, int* wg_per_chain, int* wg_per_cu);
+// compute waves of a KCP pairs workgroup at bf16, dk = 128: all dk + dv
+// columns of a chain in one workgroup
+constexpr int kPairsWaves = 8;
 
 hipError_t launch_decode(const DecodeArgs& a);
 // Td draft tokens per request (inputs [N, Td, H, d]) against the resident
