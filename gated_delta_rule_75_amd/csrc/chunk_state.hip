@@ -91,7 +91,8 @@ struct StCfg {
     // 0 .. NW/2-1 take transition columns and the others value columns, so
     // each workgroup needs v for half its columns, and T and the v rows sit
     // in one region of their own (restaged mid-chunk) while the rest is
-    // double-buffered: 80 KB, two workgroups a CU.
+    // double-buffered: with four waves (half of a chain's columns) 80 KB, two
+    // workgroups a CU; with eight (all of them at dk = 128) 88 KB, one.
     static constexpr bool MIX = AUG && NVT == 2;
     static constexpr int F_W = 0, N_W = NKC * NTT;
     static constexpr int N_T = NPM;                     // L^{-1} diag(beta), operand of U = T V
