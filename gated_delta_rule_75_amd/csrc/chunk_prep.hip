@@ -273,10 +273,30 @@ void chunk_prep_kernel(PrepParams p) {
                 rq[i] = T4{};
             }
     }
+    // running sum over the thread's tokens, then over the wave's token groups,
+    // then over the token slices before this wave's (slice sums through LDS)
+#pragma unroll
+    for (int i = 1; i < TPT; ++i) G[i] += G[i - 1];
+    float* sTot = reinterpret_cast<float*>(smem + C::O_TOT);   // [NTS][DK]
+    f32x4_t ex;   // sum over the wave's earlier token groups
+    {
+        f32x4_t inc = G[TPT - 1];
+#pragma unroll
+        for (int d = 1; d < TGW; d <<= 1) {
+            f32x4_t y;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) y[ch] = __shfl_up(inc[ch], d * CGW, 64);
+            if (tg >= d) inc += y;
+        }
+        ex = inc - G[TPT - 1];
+        if (tg == TGW - 1) *reinterpret_cast<f32x4_t*>(sTot + tsl * DK + c0) = inc;
+    }
     float* sNorm = sL;  // FUSED: [2][NWC][CH] partial squared norms (k, then q)
     if constexpr (C::FUSED) {
         // this thread's 4 channels, then the CGW lanes of a token group, then
-        // one partial per (channel set, token) in LDS
+        // one partial per (channel set, token) in LDS; placed after the slice
+        // sums, which wait for g alone, so that their shuffles are not queued
+        // behind the loads of k and q
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             float sk = 0.f, sq = 0.f;
@@ -296,25 +316,24 @@ void chunk_prep_kernel(PrepParams p) {
         }
     }
 
-    // running sum over the thread's tokens, then over the wave's token groups,
-    // then over the token slices before this wave's (slice sums through LDS)
-#pragma unroll
-    for (int i = 1; i < TPT; ++i) G[i] += G[i - 1];
-    float* sTot = reinterpret_cast<float*>(smem + C::O_TOT);   // [NTS][DK]
-    f32x4_t ex;   // sum over the wave's earlier token groups
-    {
-        f32x4_t inc = G[TPT - 1];
-#pragma unroll
-        for (int d = 1; d < TGW; d <<= 1) {
-            f32x4_t y;
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) y[ch] = __shfl_up(inc[ch], d * CGW, 64);
-            if (tg >= d) inc += y;
-        }
-        ex = inc - G[TPT - 1];
-        if (tg == TGW - 1) *reinterpret_cast<f32x4_t*>(sTot + tsl * DK + c0) = inc;
-    }
     barrier_keep_loads();
+    // FUSED: each thread sums the channel-set partials of its own tokens (the
+    // barrier above has made them visible), with no further exchange; read
+    // before the slice sums so that the two LDS round trips overlap
+    float ik[TPT], iq[TPT];
+    if constexpr (C::FUSED) {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < C::NWC; ++w) {
+                sk += sNorm[w * CH + tl0 + i];
+                sq += sNorm[(C::NWC + w) * CH + tl0 + i];
+            }
+            ik[i] = rsqrtf(sk + kNormEps);
+            iq[i] = rsqrtf(sq + kNormEps);
+        }
+    }
     // sub-tile references R_b = G at token 16 b - 1 (R_0 = 0), the sum over
     // the slices before this one, and G_C
     f32x4_t Rb[NT], Ro, RoL, GC;
@@ -343,22 +362,6 @@ void chunk_prep_kernel(PrepParams p) {
                 for (int ch = 0; ch < 4; ++ch) d[ch] = exp2_fast(Rb[a][ch] - Rb[b][ch]);
             }
         st4(gam + c0, exp2_fast(GC[0]), exp2_fast(GC[1]), exp2_fast(GC[2]), exp2_fast(GC[3]));
-    }
-    // FUSED: each thread sums the channel-set partials of its own tokens (the
-    // barrier above has made them visible), with no further exchange
-    float ik[TPT], iq[TPT];
-    if constexpr (C::FUSED) {
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int w = 0; w < C::NWC; ++w) {
-                sk += sNorm[w * CH + tl0 + i];
-                sq += sNorm[(C::NWC + w) * CH + tl0 + i];
-            }
-            ik[i] = rsqrtf(sk + kNormEps);
-            iq[i] = rsqrtf(sq + kNormEps);
-        }
     }
     // two exponentials per element, e^{G - R} <= 1 and e^{R - G} <= e^80 (R the
     // sub-tile reference); e^G and e^{G_C - G} follow by per-channel factors
