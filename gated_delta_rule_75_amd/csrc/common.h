@@ -160,10 +160,13 @@ __device__ __forceinline__ void barrier_keep_loads() {
 // row: DPP quad permutations [1,0,3,2] and [2,3,0,1] for lane distances 1
 // and 2, then the half-row and row mirrors for 4 and 8.  Four VALU adds and
 // no LDS traffic (a __shfl_xor is an LDS permute); every lane adds the same
-// pairs in the same order, so all of them hold the same bits.
+// pairs in the same order, so all of them hold the same bits.  Each pattern
+// reads a lane of the same row, so the zero fill for out-of-range lanes never
+// applies; requesting it lets the compiler fold the move into the add
+// (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
