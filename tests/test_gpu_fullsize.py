@@ -18,6 +18,10 @@ the worst (token, head) row (tests/parity.py).
 - Speculative replay (128 requests x 96 heads, 4 draft tokens, acceptance
   uniform in [0, 4]): every draft output of the verify call and every state
   after the commit call.
+- Prefix-cache checkpoints of the K3 layer every 512 tokens: all 16 states of
+  all 96 heads, the outputs and the final states.
+- Fused-input decode (128 requests x 96 heads, raw q, k and gate
+  pre-activations): every output and state after each of 4 steps.
 """
 import numpy as np
 import pytest
@@ -167,3 +171,45 @@ def test_replay_full_size(kda):
     parity.check("[fullsize] replay 128x96, 4 drafts", "bf16", y=(y, yo), committed=(state, so))
     untouched = (rep.accepted == 0).nonzero().flatten()
     assert torch.equal(state[untouched].cpu(), rep.S0[untouched])
+
+
+def test_k3_layer_checkpoints_full_size(kda):
+    """kda_chunk_fwd_checkpointed at the K3 layer shape, a state every 512
+    tokens (the pages' prefix-hash granularity): 16 checkpoints per head."""
+    inp = kda_inputs.make_workload(1)
+    dev = torch.device("cuda")
+    interval = 512
+    y, fs, ck, offs = kda.chunk_fwd_checkpointed(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev),
+                                                 inp.g.to(dev), inp.beta.to(dev), interval,
+                                                 z=inp.z.to(dev), chunk=64)
+    torch.cuda.synchronize()
+    co, oo = oracle.checkpoints(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, interval)
+    assert offs.cpu().tolist() == oo.tolist() == [0, 16]   # integer offsets: exact
+    parity.check("[fullsize] k3 layer checkpoints every 512 (16 x 96 states)", "bf16",
+                 checkpoints=(ck.cpu(), co))
+    yo, so = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, z=inp.z)
+    parity.check("[fullsize] k3 layer checkpointed prefill (96 heads)", "bf16", y=(y, yo),
+                 state=(fs, so.reshape(fs.shape)))
+    # the last checkpoint is the state after all 8192 tokens
+    assert torch.equal(ck[15].cpu(), fs[0].cpu())
+
+
+def test_decode_fused_full_size(kda):
+    """kda_decode_step_fused at the decode workload's shape, four steps from a
+    resident state; each step is checked on every chain."""
+    w = kda_inputs.WORKLOADS[4]
+    N, H, d, steps = w["N"], w["H"], w["dk"], 4
+    raw = kda_inputs.make_raw_decode(N, H, d, d, "bf16", True, w["s0_std"], steps,
+                                     kda_inputs.workload_seed(4) + 100)
+    dev = torch.device("cuda")
+    state = raw.S0.clone().to(dev)
+    cu = np.arange(N + 1, dtype=np.int32)
+    st = raw.S0.double().numpy().reshape(N * H, d, d)
+    for s in range(steps):
+        y = kda.decode_step_fused(raw.q[s].to(dev), raw.k[s].to(dev), raw.v[s].to(dev),
+                                  raw.a[s].to(dev), raw.b[s].to(dev), state, z=raw.z[s].to(dev))
+        torch.cuda.synchronize()
+        yo, st = oracle.recurrence_fused(raw.q[s], raw.k[s], raw.v[s], raw.a[s], raw.b[s], cu,
+                                         z=raw.z[s], chain_states=st)
+        parity.check(f"[fullsize] fused decode step {s + 1} (all {N * H} chains)", "bf16",
+                     y=(y.cpu(), yo), state=(state.cpu(), st))
