@@ -28,9 +28,11 @@
 //
 // Loader waves.  When two buffers of the chunk operands plus the workgroup's
 // v rows fit in LDS (one value tile per wave), four extra waves do all the
-// staging of chunk c+1 while chunk c is computed and meet the compute waves
-// at its barriers (two per chunk: one once v, T and Wn, the operands of
-// Delta, are in; one before the state update, once the rest is).  A wave that issues a 1 KiB copy stalls until
+// staging of later chunks while chunk c is computed and meet the compute
+// waves at its barriers (two per chunk: one once v, T and Wn, the operands of
+// Delta, are in; one before the state update, once the rest is).  v, T and Wn
+// go out one and a half chunks ahead, into the slots of the buffer whose
+// chunk has just passed its middle barrier; the rest one chunk ahead.  A wave that issues a 1 KiB copy stalls until
 // the memory pipeline takes it, so the compute waves, which now issue only
 // their z loads and y stores, no longer lose those cycles.  Those move as whole
 // 128-byte rows: right after the first barrier of chunk c each compute wave
@@ -147,12 +149,6 @@ struct StCfg {
     // loader waves: four (with the copies dealt round-robin, two, three and
     // four loaders reach 324, 317 and 314 us on the 96-head layer)
     static constexpr int NLW = LW ? 4 : 0;
-    // group 1 of the loaders' copies staged through registers two chunks
-    // ahead: the single-sequence and varlen scans, whose few workgroups wait
-    // on memory latency (K3 layer: pass 2 372 -> 327 us); the KCP outputs,
-    // eight rounds of workgroups that keep HBM busy, keep the direct copies
-    // (4.00 against 3.86 ms a call with registers)
-    static constexpr bool LWREG = LW && (MODE == kModeSeq || MODE == kModeVarlen);
     static constexpr int NCOPY = NF + NVC;                   // 1 KiB copies per chunk (LW)
     static constexpr int NTHR = 64 * (NW + NLW);
 };
@@ -248,7 +244,7 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
 
     if constexpr (C::LW) {
         if (wave >= NW) {
-            // ---- loader waves: the operands of chunk c+1 into buffer (c+1) % 2 during chunk c ----
+            // ---- loader waves: the operands of later chunks into LDS while chunk c is computed ----
             constexpr int FB = 64 * KPL * (int)sizeof(T);   // bytes of one fragment (1 KiB)
             static_assert(FB == 1024, "fragment size");
             const char* wn = static_cast<const char*>(p.ws.wn) + 16 * lane;
@@ -263,172 +259,94 @@ __global__ __launch_bounds__(C::NTHR) void chunk_state_kernel(StateParams p) {
             constexpr int VU = C::VRB / 16;                    // units per row
             const int vrow_l = lane / VU, vx = lane % VU;
             const int vcol_wg = vt_wg > 0 ? 16 * vt_wg : 0;
-            if constexpr (C::LWREG) {
-                // copy j of a chunk (1 KiB): the v rows first (private to the
-                // workgroup, so never in L2 already), then Wn, T, gam, Kh^T, Qt, Pm;
-                // LDS slot k of copy j: fragment k, or v-row copy k - NF.  The copies
-                // are dealt to the loaders in turn.  Group 1 (v, Wn, T: the operands
-                // of Delta, needed at the top of a chunk) goes through registers:
-                // its loads for chunk c+3 go out after the middle barrier of chunk
-                // c and are written into LDS buffer (c+3) % 2 after the middle
-                // barrier of chunk c+2, two chunks later.  Group 2 (gam, Kh^T, Qt,
-                // Pm, needed after the middle barrier) is copied straight into LDS
-                // after the middle barrier of the chunk before.
-                constexpr int NU = C::NCOPY - C::NF;
-                constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
-                constexpr int P1MIN = NG1 / C::NLW;
-                static_assert(P1MIN + NG2 / C::NLW <= 63, "vmcnt range");
-                auto src_of = [&](int c, int k) __attribute__((always_inline)) -> const char* {
-                    const int64_t wsb = (int64_t)(cws + c) * H + h;
-                    if (k < C::F_T0) return wn + wsb * (int64_t)(CH * DK * sizeof(T)) + (k - C::F_W) * FB;
-                    if (k < C::F_Q) return tt + wsb * (int64_t)(C::NPM * FB) + (k - C::F_T0) * FB;
-                    if (k < C::F_K) return qt + wsb * (int64_t)(CH * DK * sizeof(T)) + (k - C::F_Q) * FB;
-                    if (k < C::F_P) return kh + wsb * (int64_t)(DK * CP * sizeof(T)) + (k - C::F_K) * FB;
-                    if (k < C::F_G) return pm + wsb * (int64_t)(C::NPM * FB) + (k - C::F_P) * FB;
-                    if (k == C::F_G) return gm + wsb * (int64_t)(DK * sizeof(float));
-                    // v row of this lane (rows past the chunk's end repeat its last one)
-                    const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
-                    int row = (k - C::NF) * C::VRPC + vrow_l;
-                    row = row < nv ? row : nv - 1;
-                    return reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
-                           16 * (vx ^ vswz<C>(row));
+            // copy j of a chunk (1 KiB): the v rows first (private to the
+            // workgroup, so never in L2 already), then Wn, T, gam, Kh^T, Qt, Pm;
+            // LDS slot k of copy j: fragment k, or v-row copy k - NF.  The copies
+            // are dealt to the loaders in turn.  Group 1 (v, Wn, T: the operands
+            // of Delta, read before the middle barrier) and group 2 (gam, Kh^T,
+            // Qt, Pm, read after it) go straight into LDS:
+            //   after the middle barrier of chunk c, group 2 of chunk c+1 into
+            //   buffer (c+1) % 2, then group 1 of chunk c+2 into the group-1
+            //   slots of buffer c % 2, which every compute wave has finished
+            //   reading by that barrier.
+            // Group 1 then has one and a half chunks to land, group 2 one.  The
+            // waits count copies, which relies on vector memory operations
+            // completing in issue order.
+            constexpr int NU = C::NCOPY - C::NF;
+            constexpr int NG1 = NU + C::N_W + C::N_T;
+            auto src_of = [&](int c, int k) __attribute__((always_inline)) -> const char* {
+                const int64_t wsb = (int64_t)(cws + c) * H + h;
+                if (k < C::F_T0) return wn + wsb * (int64_t)(CH * DK * sizeof(T)) + (k - C::F_W) * FB;
+                if (k < C::F_Q) return tt + wsb * (int64_t)(C::NPM * FB) + (k - C::F_T0) * FB;
+                if (k < C::F_K) return qt + wsb * (int64_t)(CH * DK * sizeof(T)) + (k - C::F_Q) * FB;
+                if (k < C::F_P) return kh + wsb * (int64_t)(DK * CP * sizeof(T)) + (k - C::F_K) * FB;
+                if (k < C::F_G) return pm + wsb * (int64_t)(C::NPM * FB) + (k - C::F_P) * FB;
+                if (k == C::F_G) return gm + wsb * (int64_t)(DK * sizeof(float));
+                // v row of this lane (rows past the chunk's end repeat its last one)
+                const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
+                int row = (k - C::NF) * C::VRPC + vrow_l;
+                row = row < nv ? row : nv - 1;
+                return reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
+                       16 * (vx ^ vswz<C>(row));
+            };
+            // the loader's program, with its index LI a constant, so that each
+            // copy's slot and source array fold at compile time
+            auto loader = [&](auto LI) __attribute__((always_inline)) {
+                constexpr int li = decltype(LI)::value;
+                constexpr auto kslot = [](int j) -> int {
+                    if (j < NU) return C::NF + j;                     // v rows
+                    j -= NU;
+                    if (j < C::N_W + C::N_T) return C::F_W + j;       // Wn, then T
+                    j -= C::N_W + C::N_T;
+                    if (j == 0) return C::F_G;
+                    if (j <= C::N_K) return C::F_K + j - 1;
+                    if (j <= C::N_K + C::N_Q) return C::F_Q + j - 1 - C::N_K;
+                    return C::F_P + j - 1 - C::N_K - C::N_Q;
                 };
-                // the loader's program, with its index LI a constant, so that each
-                // copy's slot, source array and register fold at compile time
-                auto loader = [&](auto LI) __attribute__((always_inline)) {
-                    constexpr int li = decltype(LI)::value;
-                    constexpr int P1 = (NG1 - li + C::NLW - 1) / C::NLW;   // group-1 copies of this loader
-                    constexpr auto kslot = [](int j) -> int {
-                        if (j < NU) return C::NF + j;                     // v rows
-                        j -= NU;
-                        if (j < C::N_W + C::N_T) return C::F_W + j;       // Wn, then T
-                        j -= C::N_W + C::N_T;
-                        if (j == 0) return C::F_G;
-                        if (j <= C::N_K) return C::F_K + j - 1;
-                        if (j <= C::N_K + C::N_Q) return C::F_Q + j - 1 - C::N_K;
-                        return C::F_P + j - 1 - C::N_K - C::N_Q;
-                    };
-                    auto load_g1 = [&](int c, u32x4_t (&r)[P1]) __attribute__((always_inline)) {
-#pragma unroll
-                        for (int i = 0; i < P1; ++i)
-                            r[i] = *reinterpret_cast<const u32x4_t*>(src_of(c, kslot(li + C::NLW * i)));
-                    };
-                    auto write_g1 = [&](int b, const u32x4_t (&r)[P1]) __attribute__((always_inline)) {
-                        char* buf = smem + b * C::BUF;
-#pragma unroll
-                        for (int i = 0; i < P1; ++i)
-                            *reinterpret_cast<u32x4_t*>(buf + kslot(li + C::NLW * i) * 1024 + 16 * lane) = r[i];
-                    };
-                    auto copy_g2 = [&](int c, int b) __attribute__((always_inline)) {
-                        char* buf = smem + b * C::BUF;
-#pragma unroll
-                        for (int j = NG1; j < C::NCOPY; ++j)
-                            if (j % C::NLW == li) lds_dma16(src_of(c, kslot(j)), buf + kslot(j) * 1024);
-                    };
-                    u32x4_t ra[P1], rb[P1];
-                    // chunk c; rw holds the loads of group 1 of chunk c+1, and
-                    // takes those of chunk c+3 once they are in LDS.  A load of
-                    // group 1 goes out after the copies of the chunk before's
-                    // group 2, so the wait for those does not wait for it.
-                    auto step = [&](int c, u32x4_t (&rw)[P1]) __attribute__((always_inline)) {
-                        barrier_keep_loads();       // group 1 of chunk c is in LDS; the compute waves are done with chunk c-1
-                        if (c + 2 < nch) wait_vmcnt<P1MIN>();   // group 2 of chunk c and group 1 of chunk c+1 have landed
-                        else wait_vmcnt<0>();
-                        barrier_keep_loads();       // group 2 of chunk c is in LDS
-                        if (c + 1 < nch) {
-                            write_g1((c + 1) % 2, rw);
-                            copy_g2(c + 1, (c + 1) % 2);
-                            if (c + 3 < nch) load_g1(c + 3, rw);
-                        }
-                    };
-                    if (nch > 0) {
-                        load_g1(0, ra);
-                        if (nch > 1) load_g1(1, rb);
-                        copy_g2(0, 0);
-                        // group 1 of chunk 0 (group 1 of chunk 1 and group 2 of chunk 0 may be in flight)
-                        if (nch > 1) wait_vmcnt<P1MIN + NG2 / C::NLW>();
-                        else wait_vmcnt<NG2 / C::NLW>();
-                        write_g1(0, ra);
-                        if (nch > 2) load_g1(2, ra);
-                    }
-                    for (int c = 0; c < nch; c += 2) {
-                        step(c, rb);
-                        if (c + 1 < nch) step(c + 1, ra);
-                    }
-                };
-                static_assert(C::NLW == 4, "loader count");
-                switch (wave - NW) {
-                    case 0: loader(std::integral_constant<int, 0>{}); break;
-                    case 1: loader(std::integral_constant<int, 1>{}); break;
-                    case 2: loader(std::integral_constant<int, 2>{}); break;
-                    default: loader(std::integral_constant<int, 3>{}); break;
-                }
-            } else {
-                // copy k of a chunk: fragment k (k < NF) or v-row copy k - NF.  Two
-                // groups, each with a barrier of its own: group 1 (v rows, T and Wn,
-                // the operands of Delta) and group 2 (gam, Kh^T, Qt, Pm), whose last
-                // copies land while Delta is formed.  The v rows, private to the
-                // workgroup and so never in L2 already, go out first; the copies
-                // of a group are dealt to the loaders in turn.
-                const int li = wave - NW;
-                constexpr int NU = C::NCOPY - C::NF;
-                constexpr int NG1 = NU + C::N_W + C::N_T, NG2 = C::NCOPY - NG1;
-                auto stage_group = [&](int c, int b, auto G) {
-                    const int64_t wsb = (int64_t)(cws + c) * H + h;
+                // copies of this loader in group 1 and in group 2
+                constexpr int N1 = (NG1 - li + C::NLW - 1) / C::NLW;
+                constexpr int N2 = (C::NCOPY - li + C::NLW - 1) / C::NLW - N1;
+                static_assert(N1 + N2 <= 63, "vmcnt range");
+                auto copy_g1 = [&](int c, int b) __attribute__((always_inline)) {
                     char* buf = smem + b * C::BUF;
-                    const char* aw = wn + wsb * (int64_t)(CH * DK * sizeof(T));
-                    const char* aq = qt + wsb * (int64_t)(CH * DK * sizeof(T));
-                    const char* ak = kh + wsb * (int64_t)(DK * CP * sizeof(T));
-                    const char* ap = pm + wsb * (int64_t)(C::NPM * FB);
-                    const char* ag = gm + wsb * (int64_t)(DK * sizeof(float));
-                    const char* at = tt + wsb * (int64_t)(C::NPM * FB);
-                    const int nv = len - (int64_t)c * CH < CH ? (int)(len - (int64_t)c * CH) : CH;
-                    constexpr int NJ = decltype(G)::value == 1 ? NG1 : NG2;
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        if (j % C::NLW != li) continue;
-                        int k;
-                        if constexpr (decltype(G)::value == 1) k = j < NU ? C::NF + j : C::F_W + j - NU;  // v, Wn, T
-                        else k = j == 0 ? C::F_G : j <= C::N_K ? C::F_K + j - 1 : j <= C::N_K + C::N_Q ? C::F_Q + j - 1 - C::N_K
-                                                                                                : C::F_P + j - 1 - C::N_K - C::N_Q;
-                        const char* src;
-                        if (k < C::F_T0) src = aw + (k - C::F_W) * FB;
-                        else if (k < C::F_Q) src = at + (k - C::F_T0) * FB;
-                        else if (k < C::F_K) src = aq + (k - C::F_Q) * FB;
-                        else if (k < C::F_P) src = ak + (k - C::F_K) * FB;
-                        else if (k < C::F_G) src = ap + (k - C::F_P) * FB;
-                        else if (k == C::F_G) src = ag;
-                        else {
-                            // v row of this lane (rows past the chunk's end repeat its last one)
-                            int row = (k - C::NF) * C::VRPC + vrow_l;
-                            row = row < nv ? row : nv - 1;
-                            src = reinterpret_cast<const char*>(gv + ((t0 + (int64_t)c * CH + row) * H + h) * DV + vcol_wg) +
-                                  16 * (vx ^ vswz<C>(row));
-                        }
-                        lds_dma16(src, buf + k * 1024);
-                    }
+                    for (int j = 0; j < NG1; ++j)
+                        if (j % C::NLW == li) lds_dma16(src_of(c, kslot(j)), buf + kslot(j) * 1024);
                 };
-                using G1 = std::integral_constant<int, 1>;
-                using G2 = std::integral_constant<int, 2>;
-                // copies of a group that every loader issues at least
-                constexpr int M1 = NG1 / C::NLW, M2 = NG2 / C::NLW;
-                static_assert(M1 <= 63 && M2 <= 63, "vmcnt range");
+                auto copy_g2 = [&](int c, int b) __attribute__((always_inline)) {
+                    char* buf = smem + b * C::BUF;
+#pragma unroll
+                    for (int j = NG1; j < C::NCOPY; ++j)
+                        if (j % C::NLW == li) lds_dma16(src_of(c, kslot(j)), buf + kslot(j) * 1024);
+                };
+                // the waits below count on this issue order, which the
+                // scheduling barriers keep
                 if (nch > 0) {
-                    stage_group(0, 0, G1{});
-                    stage_group(0, 0, G2{});
+                    copy_g1(0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    copy_g2(0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (nch > 1) copy_g1(1, 1);
                 }
                 for (int c = 0; c < nch; ++c) {
-                    wait_vmcnt<M2>();           // group 1 of chunk c has landed (group 2 may be in flight)
-                    barrier_keep_loads();       // ... and the compute waves are done with chunk c-1
-                    if (c + 1 < nch) {
-                        stage_group(c + 1, (c + 1) % 2, G1{});
-                        wait_vmcnt<M1>();       // group 2 of chunk c (group 1 of c+1 may be in flight)
-                    } else {
-                        wait_vmcnt<0>();
-                    }
+                    // group 1 of chunk c has landed (group 2 of c and group 1 of c+1 may be in flight)
+                    if (c + 1 < nch) wait_vmcnt<N1 + N2>();
+                    else wait_vmcnt<N2>();
+                    barrier_keep_loads();       // group 1 of chunk c is in LDS; the compute waves are done with chunk c-1
+                    if (c + 1 < nch) wait_vmcnt<N1>();   // group 2 of chunk c (group 1 of c+1 may be in flight)
+                    else wait_vmcnt<0>();
                     barrier_keep_loads();       // group 2 of chunk c is in LDS
-                    if (c + 1 < nch) stage_group(c + 1, (c + 1) % 2, G2{});
+                    if (c + 1 < nch) copy_g2(c + 1, (c + 1) % 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (c + 2 < nch) copy_g1(c + 2, c % 2);
                 }
+            };
+            static_assert(C::NLW == 4, "loader count");
+            switch (wave - NW) {
+                case 0: loader(std::integral_constant<int, 0>{}); break;
+                case 1: loader(std::integral_constant<int, 1>{}); break;
+                case 2: loader(std::integral_constant<int, 2>{}); break;
+                default: loader(std::integral_constant<int, 3>{}); break;
             }
             if constexpr (!C::AUG) {
                 if (nch > 0) barrier_keep_loads();   // matches the compute waves' last y hand-off
